@@ -1,0 +1,274 @@
+"""Benchmark of the fused CE + TVD loss on one MI355X.
+
+One step = the whole hot path over one batch already resident in HBM:
+forward (lse, ce, tvd, sigma per row) -> mean reduction (and 1/n_valid on the
+device) -> backward (gradient of mean ce + mean tvd w.r.t. the student logits).
+The default workload is the training batch: 8192 rows x 151936 classes, bf16
+logits, LM-like synthetic logits (N(0, 1.5^2) plus 32 N(8, 2^2) spikes per row,
+independent teacher).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
+                    [--mode ce_tvd|ce] [--no-cpu-baseline] [--no-ce-only]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
+KERNEL_SOURCES = ["common.hpp", "forward.hip", "backward.hip", "reduce.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "cross_entropy_tv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(BT, V, es, n_valid, teacher):
+    """Unique bytes each kernel must move (see the design notes, 'algorithmic bytes')."""
+    n_ign = BT - n_valid
+    streams = 2 if teacher else 1
+    fwd = n_valid * streams * V * es + BT * 8 + BT * 4 * (5 if teacher else 2)
+    bwd = n_valid * (streams + 1) * V * es + n_ign * V * es + BT * 8 + BT * 4 * (3 if teacher else 1) + 4
+    red = BT * (4 * (2 if teacher else 1) + 8) + 16
+    return {"forward": fwd, "reduce": red, "backward": bwd}
+
+
+def run_mode(w, zs, us, tg, n_valid, steps, warmup, teacher):
+    import torch
+    import cross_entropy_tv_amd as lx
+
+    BT, V = w.BT, w.V
+    dev = zs.device
+    f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
+    ce, lse_s = f(), f()
+    tvd, lse_t, sigma = (f(), f(), f()) if teacher else (None, None, None)
+    mean = torch.empty(2, dtype=torch.float32, device=dev)
+    inv = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty_like(zs)
+    dt = lx.LX_BF16 if w.dtype == "bf16" else lx.LX_F32
+    nws = lx.lx_ce_tvd_workspace_bytes(BT, V, dt, teacher)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    u = us if teacher else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        lx.lx_ce_tvd_forward(zs, u, tg, -100, ce, tvd, lse_s, lse_t, sigma, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        lx.lx_ce_tvd_reduce_mean(ce, tvd, tg, -100, mean, None, inv, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        lx.lx_ce_tvd_backward(grad, zs, u, tg, -100, lse_s, lse_t, sigma, 1.0, 1.0, inv, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    ab = algorithmic_bytes(BT, V, w.esize, n_valid, teacher)
+    res = {
+        "ms_per_step": wall * 1e3 / steps,
+        "tokens_per_s": BT * steps / wall,
+        "forward_ms": fwd_ms, "reduce_ms": red_ms, "backward_ms": bwd_ms,
+        "forward_GBs": ab["forward"] / fwd_ms / 1e6, "backward_GBs": ab["backward"] / bwd_ms / 1e6,
+        "alg_bytes": ab,
+        "mean": mean.cpu().tolist(),
+    }
+    res["forward_pct_peak"] = 100.0 * res["forward_GBs"] / HBM_PEAK_GBS
+    res["backward_pct_peak"] = 100.0 * res["backward_GBs"] / HBM_PEAK_GBS
+    return res
+
+
+def copy_ceiling(dev, nbytes=2 << 30, reps=10):
+    """Achieved GB/s of a plain device copy (read + write), the practical streaming ceiling."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2 * nbytes / ms / 1e6
+
+
+def traffic_from_profiles(kernel_key, launches_bytes):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel_key)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds_per_worker=1.5, batch=4, workers=None):
+    """The float64 oracle, as it stands, timed on the host cores over a bounded sample of
+    the same workload's rows (forward + backward per row).  Each worker process takes
+    its own rows in batches and stops once its timed oracle work passes
+    ``seconds_per_worker``; the rate is the sum of the workers' rates (they run
+    concurrently)."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    workers = workers or min(cores, 16)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_cpu_worker, [(w.name, i, workers, batch, seconds_per_worker) for i in range(workers)])
+    rate = sum(r[0] / r[1] for r in res)
+    nrows = sum(r[0] for r in res)
+    cpu_s = sum(r[1] for r in res)
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{nrows} rows of the {w.name} workload ({w.BT}x{w.V} {w.dtype}), float64 numpy oracle "
+                      f"forward+backward per row, {workers} single-threaded processes, {cpu_s:.1f} s of timed "
+                      f"CPU work in total"}
+
+
+def _cpu_worker(arg):
+    name, wid, nworkers, batch, budget = arg
+    os.environ["OMP_NUM_THREADS"] = "1"
+    import oracle
+    import workloads as W
+    w = W.get(name)
+    tg = W.targets(w)
+    done, spent, k = 0, 0.0, 0
+    while spent < budget and done < 256:
+        rows = [(wid + nworkers * (k * batch + j)) % w.BT for j in range(batch)]
+        k += 1
+        z, u = W.rows(w, rows)
+        t = tg[rows]
+        t0 = time.perf_counter()
+        oracle.forward(z, u, t, W.IGNORE_INDEX)
+        oracle.backward(z, u, t, W.IGNORE_INDEX, 1.0 / w.BT, 1.0 / w.BT)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+    return done, spent
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train")
+    ap.add_argument("--mode", default="ce_tvd", choices=["ce_tvd", "ce"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ce-only", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
+              "with no exchange except a 3-scalar loss reduction, which this single-GPU build does not run)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import cross_entropy_tv_amd as lx  # noqa: F401  (fails loudly if the HIP library is missing)
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.get(args.workload)
+    t_gen = time.perf_counter()
+    z, u, t = W.full(w)
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] generated {w.name} {w.BT}x{w.V} {w.dtype} in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    def dev_copy(raw):
+        if raw.dtype == np.uint16:
+            return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(raw).to(dev)
+
+    zs, us, tg = dev_copy(z), dev_copy(u), dev_copy(t)
+    del z, u
+    n_valid = int((t != W.IGNORE_INDEX).sum())
+    teacher = args.mode == "ce_tvd"
+    main_res = run_mode(w, zs, us, tg, n_valid, args.steps, args.warmup, teacher)
+    print(f"[bench] {args.mode}: {main_res['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    extra = {}
+    if teacher and not args.no_ce_only:
+        ce_res = run_mode(w, zs, us, tg, n_valid, args.steps, args.warmup, False)
+        extra["ce_only"] = {k: ce_res[k] for k in ("tokens_per_s", "ms_per_step", "forward_ms", "backward_ms",
+                                                    "forward_GBs", "backward_GBs", "forward_pct_peak",
+                                                    "backward_pct_peak")}
+    if not args.no_ceiling:
+        extra["copy_ceiling_GBs"] = copy_ceiling(dev)
+
+    # dominant kernel: the pass with the larger share of the step
+    dom = "backward" if main_res["backward_ms"] >= main_res["forward_ms"] else "forward"
+    achieved = main_res[f"{dom}_GBs"]
+    kkey = f"{dom}_{args.mode}_{w.name}"
+    traffic = traffic_from_profiles(kkey, main_res["alg_bytes"][dom])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                "alg_bytes_per_launch": main_res["alg_bytes"][dom],
+                "avg_launch_ms": round(main_res[f"{dom}_ms"], 4)}
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "BT": w.BT, "V": w.V, "logits": w.dtype, "mode": args.mode,
+                   "global_batch": w.BT, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "passes": {"forward_ms": round(main_res["forward_ms"], 4), "reduce_ms": round(main_res["reduce_ms"], 4),
+                   "backward_ms": round(main_res["backward_ms"], 4),
+                   "forward_GBs": round(main_res["forward_GBs"], 1),
+                   "backward_GBs": round(main_res["backward_GBs"], 1),
+                   "forward_pct_peak": round(main_res["forward_pct_peak"], 2),
+                   "backward_pct_peak": round(main_res["backward_pct_peak"], 2)},
+        "mean_loss": main_res["mean"],
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

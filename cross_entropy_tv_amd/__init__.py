@@ -1,0 +1,163 @@
+"""Fused cross-entropy + total-variation-distance loss for MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in ``include/lx_ce_tvd.h``: every
+function here has the name of the C entry point it calls and only marshals
+arguments (PyTorch tensors supply device memory and the HIP stream).  All of
+the loss is computed by the HIP kernels in ``liblx_ce_tvd.so``; there is no
+other code path.  Importing this package fails if the library is not built
+(``python cross_entropy_tv_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblx_ce_tvd.so")
+
+LX_OK = 0
+LX_ERR_INVALID_ARG = 1
+LX_ERR_UNSUPPORTED_DTYPE = 2
+LX_ERR_ALIAS = 3
+LX_ERR_WORKSPACE = 4
+LX_ERR_HIP = 5
+LX_F32 = 0
+LX_BF16 = 1
+
+
+class LxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = lib.lx_status_string(status).decode()
+        extra = f" (hipError {lib.lx_last_hip_error()})" if status == LX_ERR_HIP else ""
+        super().__init__(f"{where}: {name}{extra}")
+
+
+def _load() -> ctypes.CDLL:
+    # PyTorch-ROCm ships its own HIP runtime and links it as "libamdhip64.so";
+    # the library links "libamdhip64.so.7".  Importing torch first puts torch's
+    # runtime in the process under that soname, so the library binds to it.
+    # Loading the library first would start a second HIP runtime, whose
+    # launches then fail with hipErrorNoDevice.
+    import torch  # noqa: F401
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python cross_entropy_tv_amd/build.py` "
+                          "(the HIP library is the only implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.lx_status_string.argtypes = [i32]
+    L.lx_status_string.restype = ctypes.c_char_p
+    L.lx_abi_version.argtypes = []
+    L.lx_abi_version.restype = i32
+    L.lx_last_hip_error.argtypes = []
+    L.lx_last_hip_error.restype = i32
+    L.lx_ce_tvd_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    L.lx_ce_tvd_workspace_bytes.restype = sz
+    L.lx_ce_tvd_forward.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p, i32, p, sz, p]
+    L.lx_ce_tvd_forward.restype = i32
+    L.lx_ce_tvd_backward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, f32, f32, p, i32, p]
+    L.lx_ce_tvd_backward.restype = i32
+    L.lx_ce_tvd_reduce_mean.argtypes = [p, p, p, i64, i64, p, p, p, p]
+    L.lx_ce_tvd_reduce_mean.restype = i32
+    return L
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LX_BF16
+    if t.dtype == torch.float32:
+        return LX_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _logits2d(t, name):
+    if t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous 2-D (BT, V) device tensor")
+    return t.shape
+
+
+def _check(status: int, where: str) -> None:
+    if status != LX_OK:
+        raise LxError(status, where)
+
+
+# ------------------------------------------------------------------ entry points
+
+def lx_status_string(status: int) -> str:
+    return lib.lx_status_string(status).decode()
+
+
+def lx_abi_version() -> int:
+    return lib.lx_abi_version()
+
+
+def lx_ce_tvd_workspace_bytes(BT: int, V: int, dt: int, has_teacher: bool) -> int:
+    return lib.lx_ce_tvd_workspace_bytes(BT, V, dt, int(bool(has_teacher)))
+
+
+def lx_ce_tvd_forward(student, teacher, target, ignore_index, ce, tvd, lse_s, lse_t, sigma,
+                      workspace=None, stream=None) -> None:
+    """Forward pass into the caller's float32 [BT] output tensors (tvd, lse_t, sigma
+    may be None in CE-only mode, i.e. teacher=None).  ``workspace`` is a uint8
+    device tensor of at least lx_ce_tvd_workspace_bytes bytes; when None and the
+    shape needs one, it is allocated here with torch."""
+    BT, V = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if teacher is not None and (teacher.shape != student.shape or teacher.dtype != student.dtype):
+        raise ValueError("teacher must match student in shape and dtype")
+    need = lx_ce_tvd_workspace_bytes(BT, V, dt, teacher is not None)
+    if workspace is None and need:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=student.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lx_ce_tvd_forward(_ptr(student), _ptr(teacher), _ptr(target), BT, V, int(ignore_index),
+                                 _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t), _ptr(sigma), dt,
+                                 _ptr(workspace), wbytes, _stream(stream)), "lx_ce_tvd_forward")
+
+
+def lx_ce_tvd_backward(grad, student, teacher, target, ignore_index, lse_s, lse_t, sigma,
+                       g_ce: float, g_tvd: float, g_scale=None, stream=None) -> None:
+    """Backward pass into ``grad`` (may be ``student`` itself).  ``g_scale`` is an
+    optional float32 device tensor of one element multiplying g_ce and g_tvd."""
+    BT, V = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if grad.shape != student.shape or grad.dtype != student.dtype or not grad.is_contiguous():
+        raise ValueError("grad must match student in shape and dtype and be contiguous")
+    _check(lib.lx_ce_tvd_backward(_ptr(grad), _ptr(student), _ptr(teacher), _ptr(target), BT, V,
+                                  int(ignore_index), _ptr(lse_s), _ptr(lse_t), _ptr(sigma),
+                                  float(g_ce), float(g_tvd), _ptr(g_scale), dt, _stream(stream)),
+           "lx_ce_tvd_backward")
+
+
+def lx_ce_tvd_reduce_mean(ce, tvd, target, ignore_index, mean_out, n_valid=None, inv_n_valid=None,
+                          stream=None) -> None:
+    """Mean of ce (and tvd) over non-ignored rows into mean_out (float32 [2])."""
+    BT = target.shape[0]
+    _check(lib.lx_ce_tvd_reduce_mean(_ptr(ce), _ptr(tvd), _ptr(target), BT, int(ignore_index),
+                                     _ptr(mean_out), _ptr(n_valid), _ptr(inv_n_valid), _stream(stream)),
+           "lx_ce_tvd_reduce_mean")
+
+
+__all__ = [
+    "LxError", "lib", "LIB_PATH", "LX_OK", "LX_ERR_INVALID_ARG", "LX_ERR_UNSUPPORTED_DTYPE", "LX_ERR_ALIAS",
+    "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "lx_status_string", "lx_abi_version",
+    "lx_ce_tvd_workspace_bytes", "lx_ce_tvd_forward", "lx_ce_tvd_backward", "lx_ce_tvd_reduce_mean",
+]

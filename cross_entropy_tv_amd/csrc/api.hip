@@ -1,0 +1,186 @@
+// C ABI entry points (include/lx_ce_tvd.h): host-side validation, path
+// selection and kernel launches.  Validation runs entirely on the host and
+// before any HIP call, so a rejected call enqueues nothing.
+#include <limits.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "lx_ce_tvd.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+lx_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return LX_OK;
+  g_last_hip_error = (int)e;
+  return LX_ERR_HIP;
+}
+
+int esize_of(lx_dtype dt) {
+  switch (dt) {
+    case LX_F32: return 4;
+    case LX_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// byte range [lo, hi) of an array; empty when p is NULL
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t bytes) {
+  const uintptr_t a = (uintptr_t)p;
+  return p ? Span{a, a + (uintptr_t)bytes} : Span{0, 0};
+}
+bool overlaps(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+bool any_overlap(const Span* s, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlaps(s[i], s[j])) return true;
+  return false;
+}
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+lx_status check_shape(int64_t BT, int64_t V, int es) {
+  if (BT < 0 || V < 1 || V > (int64_t)INT_MAX) return LX_ERR_INVALID_ARG;
+  if (BT > 0 && BT > INT64_MAX / V / es) return LX_ERR_INVALID_ARG;
+  return LX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lx_status_string(lx_status s) {
+  switch (s) {
+    case LX_OK: return "LX_OK";
+    case LX_ERR_INVALID_ARG: return "LX_ERR_INVALID_ARG";
+    case LX_ERR_UNSUPPORTED_DTYPE: return "LX_ERR_UNSUPPORTED_DTYPE";
+    case LX_ERR_ALIAS: return "LX_ERR_ALIAS";
+    case LX_ERR_WORKSPACE: return "LX_ERR_WORKSPACE";
+    case LX_ERR_HIP: return "LX_ERR_HIP";
+  }
+  return "LX_ERR_UNKNOWN";
+}
+
+int lx_abi_version(void) { return LX_CE_TVD_ABI_VERSION; }
+
+int lx_last_hip_error(void) { return g_last_hip_error; }
+
+size_t lx_ce_tvd_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher) {
+  const int es = esize_of(dt);
+  if (!es || check_shape(BT, V, es) != LX_OK) return 0;
+  return lx::plan_forward(BT, V, es, has_teacher != 0).workspace_bytes;
+}
+
+lx_status lx_ce_tvd_forward(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                            int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s, float* lse_t,
+                            float* sigma, lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = teacher != nullptr;
+  if (!student || !target || !ce || !lse_s) return LX_ERR_INVALID_ARG;
+  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) || !aligned(ce, 4) ||
+      !aligned(lse_s, 4))
+    return LX_ERR_INVALID_ARG;
+  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
+
+  const int64_t lb = BT * V * es, fb = BT * 4;
+  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
+  Span sp[9] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(ce, fb), span(lse_s, fb),
+                span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
+                span(has_t ? sigma : nullptr, fb), span(plan.workspace_bytes ? workspace : nullptr,
+                                                         (int64_t)plan.workspace_bytes)};
+  // inputs may overlap each other (e.g. teacher == student); outputs and the
+  // workspace may overlap nothing
+  for (int o = 3; o < 9; ++o)
+    for (int i = 0; i < 9; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  if (plan.workspace_bytes) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
+  }
+
+  lx::FwdArgs a;
+  a.student = student;
+  a.teacher = teacher;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.ce = ce;
+  a.tvd = tvd;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.vec = (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0;
+  a.workspace = workspace;
+  return from_hip(lx::launch_forward(a, plan, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teacher, const int64_t* target,
+                             int64_t BT, int64_t V, int64_t ignore_index, const float* lse_s, const float* lse_t,
+                             const float* sigma, float g_ce, float g_tvd, const float* g_scale, lx_dtype dt,
+                             void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = teacher != nullptr;
+  if (!grad || !student || !target || !lse_s) return LX_ERR_INVALID_ARG;
+  if (has_t && (!lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(grad, es) || !aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) ||
+      !aligned(lse_s, 4) || (has_t && (!aligned(lse_t, 4) || !aligned(sigma, 4))) ||
+      (g_scale && !aligned(g_scale, 4)))
+    return LX_ERR_INVALID_ARG;
+
+  const int64_t lb = BT * V * es, fb = BT * 4;
+  const Span g = span(grad, lb);
+  const Span ins[7] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(lse_s, fb),
+                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb), span(g_scale, 4)};
+  // in place (grad == student) is allowed; any other overlap is not
+  if (grad != student && overlaps(g, ins[0])) return LX_ERR_ALIAS;
+  for (int i = 1; i < 7; ++i)
+    if (overlaps(g, ins[i])) return LX_ERR_ALIAS;
+
+  lx::BwdArgs a;
+  a.grad = grad;
+  a.student = student;
+  a.teacher = teacher;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.g_ce = g_ce;
+  a.g_tvd = g_tvd;
+  a.g_scale = g_scale;
+  const uintptr_t m = (uintptr_t)student & 15u;
+  a.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
+  return from_hip(lx::launch_backward(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
+                                int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,
+                                void* stream) {
+  if (BT < 0) return LX_ERR_INVALID_ARG;
+  if (!mean_out || (BT > 0 && (!ce || !target))) return LX_ERR_INVALID_ARG;
+  if (!aligned(ce, 4) || !aligned(tvd, 4) || !aligned(target, 8) || !aligned(mean_out, 4) ||
+      !aligned(n_valid, 8) || !aligned(inv_n_valid, 4))
+    return LX_ERR_INVALID_ARG;
+  const int64_t fb = BT * 4;
+  const Span sp[6] = {span(ce, fb), span(tvd, fb), span(target, BT * 8), span(mean_out, tvd ? 8 : 4),
+                      span(n_valid, 8), span(inv_n_valid, 4)};
+  for (int o = 3; o < 6; ++o)
+    for (int i = 0; i < 6; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_reduce_mean(ce, tvd, target, BT, ignore_index, mean_out, n_valid, inv_n_valid,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

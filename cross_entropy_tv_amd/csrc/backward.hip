@@ -1,0 +1,138 @@
+// Backward kernel of the fused CE + TVD loss.
+//
+// The "Backward Pass" section of the Liger-Kernel PR #1384 analysis page: the
+// logits are streamed again, p and q are recomputed from the forward's stored
+// log-sum-exps, and the student gradient
+//
+//   g_v = k * ( g_ce * (p_v - [v == t]) + g_tvd * 0.5 * p_v * (s_v - sigma) ),
+//   s_v = sign(p_v - q_v), sign(0) = 0,
+//
+// is written, with the target element's -g_ce added by the lane that owns it.
+// Per row this is p_v * (alpha + beta * s_v) with alpha = k * (g_ce - 0.5 *
+// g_tvd * sigma) and beta = 0.5 * k * g_tvd, so each element costs two
+// exponentials, a sign and two FMAs.
+//
+// Work is tiled over (row, chunk) with a grid-stride loop; each lane reads an
+// element group before it writes the same group, so the gradient may be the
+// student buffer itself (in place).  Ignored rows are only written (+0.0),
+// never read.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lx {
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdUnroll = 4;  // groups of 8 elements per lane per chunk
+constexpr int kBwdGroupsPerChunk = kBwdThreads * kBwdUnroll;
+constexpr int kMaxGrid = 1 << 20;
+
+template <typename T, bool TEACHER, int NT, int UNR>
+__global__ __launch_bounds__(NT) void bwd_kernel(
+    T* grad, const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
+    int64_t BT, int V, int64_t ignore_index, int vec, int chunks_per_row,
+    const float* __restrict__ lse_s, const float* __restrict__ lse_t, const float* __restrict__ sigma,
+    float g_ce, float g_tvd, const float* __restrict__ g_scale) {
+  const int tid = threadIdx.x;
+  const float k = g_scale ? *g_scale : 1.0f;
+  const int64_t tiles = BT * (int64_t)chunks_per_row;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t r = tile / chunks_per_row;
+    const int c = (int)(tile - r * chunks_per_row);
+    const int64_t t = target[r];
+    T* gr = grad + r * (int64_t)V;
+    const T* z = student + r * (int64_t)V;
+    const T* u = TEACHER ? teacher + r * (int64_t)V : nullptr;
+    const RowLayout L = row_layout(z, V, vec);
+    const int nsc = L.head + L.tail;
+    // this chunk's groups and scalar elements
+    const int g0 = c * (NT * UNR);
+    const int g1 = min(L.groups, g0 + NT * UNR);
+    const int s0 = c * (NT * UNR * 8);
+    const int s1 = min(nsc, s0 + NT * UNR * 8);
+    T* gb = gr + L.head;
+    const T* zb = z + L.head;
+    const T* ub = TEACHER ? u + L.head : nullptr;
+
+    if (t == ignore_index || t < 0 || t >= V) {
+      // ignored row: +0.0; invalid target: NaN (the loud failure of the ABI contract)
+      const uint32_t fill = (t == ignore_index) ? 0u : kQNaN32;
+      for (int i = s0 + tid; i < s1; i += NT) store_bits1(gr + scalar_elem(L, i), fill);
+      for (int g = g0 + tid; g < g1; g += NT) store_bits8(gb + 8 * g, fill);
+      continue;
+    }
+
+    const float nbs = neg_scaled(lse_s[r]);
+    const float nbt = TEACHER ? neg_scaled(lse_t[r]) : 0.0f;
+    const float kce = k * g_ce;
+    const float beta = TEACHER ? 0.5f * k * g_tvd : 0.0f;
+    const float alpha = TEACHER ? kce - beta * sigma[r] : kce;
+
+    for (int i = s0 + tid; i < s1; i += NT) {
+      const int e = scalar_elem(L, i);
+      const float p = prob(load1(z + e), nbs);
+      float gv;
+      if (TEACHER) {
+        const float q = prob(load1(u + e), nbt);
+        gv = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+      } else {
+        gv = p * alpha;
+      }
+      if (e == t) gv -= kce;
+      store1(gr + e, gv);
+    }
+
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int g = g0 + j * NT + tid;
+      if (g < g1) {
+        float x[8], y[8], o[8];
+        load8(zb + 8 * g, x);
+        if (TEACHER) load8(ub + 8 * g, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = prob(x[e], nbs);
+          if (TEACHER) {
+            const float q = prob(y[e], nbt);
+            o[e] = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+          } else {
+            o[e] = p * alpha;
+          }
+        }
+        const int rel = (int)(t - (int64_t)(L.head + 8 * g));
+        if ((unsigned)rel < 8u) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+        }
+        store8(gb + 8 * g, o);
+      }
+    }
+  }
+}
+
+template <typename T, bool TEACHER>
+static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated call
+  const int V = (int)a.V;
+  // chunks needed by the longest layout: groups (vector path) or scalar elements
+  const int64_t per_chunk_groups = kBwdGroupsPerChunk;
+  const int64_t cpr = a.vec ? (a.V / 8 + per_chunk_groups - 1) / per_chunk_groups
+                            : (a.V + per_chunk_groups * 8 - 1) / (per_chunk_groups * 8);
+  const int chunks = (int)(cpr < 1 ? 1 : cpr);
+  const int64_t tiles = a.BT * (int64_t)chunks;
+  const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
+  hipLaunchKernelGGL((bwd_kernel<T, TEACHER, kBwdThreads, kBwdUnroll>), dim3(grid), dim3(kBwdThreads), 0, st,
+                     static_cast<T*>(a.grad), static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
+                     a.target, a.BT, V, a.ignore_index, a.vec, chunks, a.lse_s, a.lse_t, a.sigma, a.g_ce,
+                     a.g_tvd, a.g_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  const bool teacher = a.teacher != nullptr;
+  if (bf16) {
+    return teacher ? launch_backward_t<uint16_t, true>(a, stream) : launch_backward_t<uint16_t, false>(a, stream);
+  }
+  return teacher ? launch_backward_t<float, true>(a, stream) : launch_backward_t<float, false>(a, stream);
+}
+
+}  // namespace lx

@@ -1,0 +1,185 @@
+// Device helpers shared by the CE + TVD kernels (gfx950, wave64).
+//
+// Numerics (the same helpers serve the forward and the backward, so both
+// passes form p, q and sign(p - q) with the same instruction sequence):
+//   * logits are widened to f32 (bf16 -> f32 is exact), all arithmetic is f32;
+//   * exp(x - lse) is evaluated as exp2(fma(x, log2 e, -lse * log2 e)), one
+//     rounding before the hardware v_exp_f32;
+//   * running maxima start at kMFloor, a finite floor, so every rescale factor
+//     exp2((m_old - m_new) * log2 e) is finite (no inf - inf) even for rows
+//     holding -inf entries;
+//   * sign(p - q) with sign(0) = 0 is med3(d * 2^126, -1, 1): exact for every
+//     d that is 0 or at least 2^-126 in magnitude; p - q is never a nonzero
+//     number below that unless both p and q are below 2^-103.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lx {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kMFloor = -1.0e30f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ loads
+
+// 8 consecutive logits at a 16-byte-aligned address, widened to f32.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+  x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+  x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
+  x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+// ------------------------------------------------------------------ stores
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&g)[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(g[0], g[1]); w.y = pack_bf16x2(g[2], g[3]);
+  w.z = pack_bf16x2(g[4], g[5]); w.w = pack_bf16x2(g[6], g[7]);
+  *reinterpret_cast<uint4*>(p) = w;
+}
+__device__ __forceinline__ void store8(float* p, const float (&g)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(g[0], g[1], g[2], g[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(g[4], g[5], g[6], g[7]);
+}
+__device__ __forceinline__ void store1(uint16_t* p, float g) {
+  *p = (uint16_t)(pack_bf16x2(g, 0.0f) & 0xffffu);
+}
+__device__ __forceinline__ void store1(float* p, float g) { *p = g; }
+
+// Quiet-NaN bit patterns.  The kernels are compiled with NaNs assumed absent
+// from floating-point arithmetic, so a NaN the ABI promises as an output is
+// written as an integer bit pattern and never produced by an FP operation.
+constexpr uint32_t kQNaN32 = 0x7fc00000u;
+constexpr uint16_t kQNaN16 = 0x7fc0u;
+
+__device__ __forceinline__ void store_bits1(uint16_t* p, uint32_t f32bits) { *p = (uint16_t)(f32bits >> 16); }
+__device__ __forceinline__ void store_bits1(float* p, uint32_t f32bits) { *reinterpret_cast<uint32_t*>(p) = f32bits; }
+// 8 copies of one f32 bit pattern (bf16: its upper half), stored as integers
+__device__ __forceinline__ void store_bits8(uint16_t* p, uint32_t f32bits) {
+  const uint32_t h = f32bits >> 16, w = h | (h << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w, w, w, w);
+}
+__device__ __forceinline__ void store_bits8(float* p, uint32_t f32bits) {
+  reinterpret_cast<uint4*>(p)[0] = make_uint4(f32bits, f32bits, f32bits, f32bits);
+  reinterpret_cast<uint4*>(p)[1] = make_uint4(f32bits, f32bits, f32bits, f32bits);
+}
+__device__ __forceinline__ void store_nan(float* p) { *reinterpret_cast<uint32_t*>(p) = kQNaN32; }
+
+// ------------------------------------------------------------------ math
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// -lse * log2(e): the bias every probability of the row is formed with.
+__device__ __forceinline__ float neg_scaled(float lse) { return -(lse * kLog2e); }
+
+// exp(x - lse) given nb = neg_scaled(lse).
+__device__ __forceinline__ float prob(float x, float nb) { return exp2_hw(__builtin_fmaf(x, kLog2e, nb)); }
+
+// sign(d) with sign(0) = 0 (see header comment).
+__device__ __forceinline__ float sign0(float d) { return __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.0f, 1.0f); }
+
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  return fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+}
+
+// Online log-sum-exp state: sum_i exp(x_i - m) = s.
+struct Lse {
+  float m, s;
+};
+
+__device__ __forceinline__ Lse lse_init() { return Lse{kMFloor, 0.0f}; }
+
+__device__ __forceinline__ void lse_add8(Lse& a, const float (&x)[8]) {
+  const float mn = fmaxf(a.m, max8(x));
+  const float nb = -(mn * kLog2e);
+  float s0 = a.s * exp2_hw((a.m - mn) * kLog2e);
+  float s1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    s0 += exp2_hw(__builtin_fmaf(x[k], kLog2e, nb));
+    s1 += exp2_hw(__builtin_fmaf(x[k + 1], kLog2e, nb));
+  }
+  a.m = mn;
+  a.s = s0 + s1;
+}
+
+__device__ __forceinline__ void lse_add1(Lse& a, float x) {
+  const float mn = fmaxf(a.m, x);
+  a.s = a.s * exp2_hw((a.m - mn) * kLog2e) + exp2_hw((x - mn) * kLog2e);
+  a.m = mn;
+}
+
+// Merge b into a.  Both maxima are >= kMFloor, so no NaN can arise.
+__device__ __forceinline__ void lse_merge(Lse& a, const Lse& b) {
+  const float mn = fmaxf(a.m, b.m);
+  a.s = a.s * exp2_hw((a.m - mn) * kLog2e) + b.s * exp2_hw((b.m - mn) * kLog2e);
+  a.m = mn;
+}
+
+__device__ __forceinline__ float lse_value(const Lse& a) { return a.m + logf(a.s); }
+
+// ------------------------------------------------------------------ wave / block reductions
+
+__device__ __forceinline__ Lse wave_lse(Lse a) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Lse b{__shfl_xor(a.m, off, 64), __shfl_xor(a.s, off, 64)};
+    lse_merge(a, b);
+  }
+  return a;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ row layout
+
+// A row of V elements starting at `row` is cut into a scalar head [0, head),
+// body groups of 8 elements [head, head + 8 * groups) that start on a
+// 16-byte boundary, and a scalar tail.  With vec == 0 every element is
+// scalar (head = V, groups = 0).
+struct RowLayout {
+  int head, groups, tail;
+};
+
+template <typename T>
+__device__ __forceinline__ RowLayout row_layout(const T* row, int V, int vec) {
+  RowLayout L;
+  if (!vec) {
+    L.head = V; L.groups = 0; L.tail = 0;
+    return L;
+  }
+  const int mis = (int)((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / (int)sizeof(T);
+  L.head = mis < V ? mis : V;
+  L.groups = (V - L.head) / 8;
+  L.tail = V - L.head - 8 * L.groups;
+  return L;
+}
+
+// i-th scalar element (0 <= i < head + tail) of the row.
+__device__ __forceinline__ int scalar_elem(const RowLayout& L, int i) {
+  return i < L.head ? i : L.head + 8 * L.groups + (i - L.head);
+}
+
+}  // namespace lx

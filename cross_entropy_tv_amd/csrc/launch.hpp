@@ -1,0 +1,50 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lx {
+
+// How the forward is run for a shape.
+//   split == 1: one workgroup per row ("row path").
+//   split  > 1: each row is cut into `split` chunks handled by separate
+//               workgroups; per-chunk partials go through the workspace and
+//               are merged in chunk order ("split-V path").
+struct FwdPlan {
+  int split;
+  size_t workspace_bytes;
+};
+
+FwdPlan plan_forward(int64_t BT, int64_t V, int esize, bool teacher);
+
+struct FwdArgs {
+  const void* student;
+  const void* teacher;  // nullptr: CE-only
+  const int64_t* target;
+  int64_t BT, V, ignore_index;
+  float *ce, *tvd, *lse_s, *lse_t, *sigma;
+  int vec;  // 16-byte vector path usable
+  void* workspace;
+};
+
+struct BwdArgs {
+  void* grad;
+  const void* student;
+  const void* teacher;  // nullptr: CE-only
+  const int64_t* target;
+  int64_t BT, V, ignore_index;
+  const float *lse_s, *lse_t, *sigma;
+  float g_ce, g_tvd;
+  const float* g_scale;
+  int vec;
+};
+
+hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
+                              int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,
+                              hipStream_t stream);
+
+}  // namespace lx

@@ -1,0 +1,165 @@
+/*
+ * lx_ce_tvd.h -- C ABI of the fused cross-entropy + total-variation-distance
+ * (CE + TVD) distillation loss for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the "Liger-Kernel PR #1384 analysis" page
+ * (blog.secrett2633.cloud; the analysis of the merged Liger-Kernel pull
+ * request "add fused CE + TV distance kernel") describes.  Per token row r of
+ * student logits z (length V), teacher logits u and target t = target[r]:
+ *
+ *   lse_s = log sum_v exp(z_v),  lse_t = log sum_v exp(u_v)
+ *                                          (page section "Forward Pass", step 1)
+ *   p_v = exp(z_v - lse_s),  q_v = exp(u_v - lse_t)
+ *   tvd   = 0.5 * sum_v |p_v - q_v|
+ *   sigma = sum_v p_v * sign(p_v - q_v),  sign(0) = 0
+ *                                          (page section "Forward Pass", step 2)
+ *   ce    = lse_s - z_t                    (same section, the stored outputs)
+ *   d(g_ce*ce + g_tvd*tvd)/dz_v =
+ *       g_ce * (p_v - [v == t]) + g_tvd * 0.5 * p_v * (sign(p_v - q_v) - sigma)
+ *                                          (page section "Backward Pass")
+ *
+ * Only the O(BT) per-row state (ce, tvd, lse_s, lse_t, sigma) passes from the
+ * forward to the backward (page section "Core idea"); no (BT, V) temporary is
+ * ever allocated.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Logits are row-major, contiguous, shape (BT, V), element type `dt`;
+ *   student and teacher share the type.  Row r starts at element r * V.
+ * - All array pointers are DEVICE pointers owned by the caller.  The library
+ *   allocates nothing, keeps no state between calls and is safe to call from
+ *   several host threads (on different or on the same stream).
+ * - `stream` is a hipStream_t passed as an opaque pointer; NULL selects the
+ *   null stream.  Every call is asynchronous on that stream: the call returns
+ *   after enqueueing its kernels.
+ * - Arguments are validated on the host before anything is enqueued; a failed
+ *   validation returns a status other than LX_OK and enqueues nothing.
+ *   LX_ERR_HIP means a kernel launch was rejected by the HIP runtime; call
+ *   lx_last_hip_error() for the hipError_t code.
+ * - BT == 0 is a no-op returning LX_OK (pointers are not inspected).
+ * - Requirements: BT >= 0, 1 <= V <= 2^31 - 1, BT * V * element size fits in
+ *   int64; logits pointers aligned to the element size, float arrays to 4
+ *   bytes, target to 8 bytes.  Fast 16-byte vector paths are taken when the
+ *   logits (and gradient) pointers share their address modulo 16; any other
+ *   element-aligned layout runs a slower element-wise path of the same kernels.
+ * - Target handling: a row whose target equals ignore_index is IGNORED (tested
+ *   first, so an ignore_index inside [0, V) ignores that class): its logits
+ *   are never read, its five forward outputs are +0.0 and its gradient row is
+ *   +0.0.  A target outside [0, V) that is not ignore_index is a caller error
+ *   the device cannot report synchronously: that row's ce and its whole
+ *   gradient row are written as NaN.
+ * - Logits must be finite.  -inf entries are allowed in a row that has at
+ *   least one finite entry (they get probability 0); NaN or +inf entries give
+ *   unspecified (NaN) results for their row.
+ * - Results are deterministic: the same inputs give bit-identical outputs on
+ *   every call.  Identical student and teacher rows give tvd == sigma == 0
+ *   exactly and a total-variation gradient of exactly 0.
+ */
+#ifndef LX_CE_TVD_H
+#define LX_CE_TVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LX_CE_TVD_ABI_VERSION 1
+
+typedef enum lx_status {
+  LX_OK = 0,
+  LX_ERR_INVALID_ARG = 1,       /* NULL / misaligned pointer, bad size */
+  LX_ERR_UNSUPPORTED_DTYPE = 2, /* dt is not LX_F32 or LX_BF16 */
+  LX_ERR_ALIAS = 3,             /* an output overlaps an input or another output */
+  LX_ERR_WORKSPACE = 4,         /* workspace NULL or smaller than required */
+  LX_ERR_HIP = 5                /* the HIP runtime rejected a launch */
+} lx_status;
+
+typedef enum lx_dtype {
+  LX_F32 = 0,  /* IEEE binary32 logits (and gradient) */
+  LX_BF16 = 1  /* bfloat16 logits (and gradient); gradients rounded to nearest-even */
+} lx_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* lx_status_string(lx_status s);
+
+/* LX_CE_TVD_ABI_VERSION of the built library. */
+int lx_abi_version(void);
+
+/* hipError_t code (as int) of the last LX_ERR_HIP returned on this host thread; 0 if none. */
+int lx_last_hip_error(void);
+
+/*
+ * Bytes of device workspace lx_ce_tvd_forward needs for this shape
+ * (0 when the shape runs without workspace).  has_teacher: 0 = CE-only mode.
+ * Returns 0 for shapes that the forward would reject.
+ */
+size_t lx_ce_tvd_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher);
+
+/*
+ * Forward pass ("Forward Pass" section of the PR #1384 analysis page).
+ *
+ * Inputs : student (BT, V) dt; teacher (BT, V) dt or NULL for CE-only mode;
+ *          target (BT) int64; ignore_index.
+ * Outputs: ce, lse_s: float[BT], required.
+ *          tvd, lse_t, sigma: float[BT], required with a teacher; in CE-only
+ *          mode they may be NULL and are never written.
+ *          All outputs hold fp32 values computed with fp32 accumulation.
+ * Workspace: device buffer of at least lx_ce_tvd_workspace_bytes(BT, V, dt,
+ *          teacher != NULL) bytes, 256-byte aligned, contents ignored and
+ *          clobbered; may be NULL when that size is 0.  It must not be used by
+ *          another call that overlaps this one on the device.
+ * Errors : LX_ERR_INVALID_ARG, LX_ERR_UNSUPPORTED_DTYPE, LX_ERR_ALIAS (any
+ *          output overlapping an input or another output), LX_ERR_WORKSPACE,
+ *          LX_ERR_HIP.
+ */
+lx_status lx_ce_tvd_forward(const void* student, const void* teacher, const int64_t* target,
+                            int64_t BT, int64_t V, int64_t ignore_index,
+                            float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                            lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass ("Backward Pass" section of the PR #1384 analysis page):
+ *
+ *   grad[r, v] = k * ( g_ce * (p_v - [v == t]) + g_tvd * 0.5 * p_v * (s_v - sigma[r]) )
+ *
+ * with p, q recomputed from the logits and the forward's lse_s / lse_t,
+ * s_v = sign(p_v - q_v) (0 at ties), and k = *g_scale when g_scale is not
+ * NULL (a device float, e.g. the inv_n_valid written by
+ * lx_ce_tvd_reduce_mean), else 1.  Ignored rows are written +0.0.
+ *
+ * Inputs : student, teacher (NULL = CE-only: the g_tvd term is absent and
+ *          lse_t / sigma may be NULL), target, lse_s, lse_t, sigma as written
+ *          by lx_ce_tvd_forward on the same logits; g_ce, g_tvd host scalars.
+ * Output : grad (BT, V) dt.  grad may EQUAL student (in place: each element is
+ *          read before it is overwritten); any other overlap with an input is
+ *          LX_ERR_ALIAS.  bf16 gradients are rounded to nearest-even.
+ */
+lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teacher,
+                             const int64_t* target, int64_t BT, int64_t V, int64_t ignore_index,
+                             const float* lse_s, const float* lse_t, const float* sigma,
+                             float g_ce, float g_tvd, const float* g_scale,
+                             lx_dtype dt, void* stream);
+
+/*
+ * Mean reduction over the rows whose target is not ignore_index.
+ *
+ * Inputs : ce float[BT]; tvd float[BT] or NULL (CE-only); target int64[BT].
+ * Outputs: mean_out float[2] = { sum ce / n_valid, sum tvd / n_valid }
+ *          (mean_out[1] is written only when tvd is not NULL; 0/0 = NaN when
+ *          every row is ignored); n_valid int64[1] or NULL; inv_n_valid
+ *          float[1] or NULL, = 1 / n_valid (0 when n_valid == 0), the factor
+ *          a mean-reduced loss passes to lx_ce_tvd_backward as g_scale.
+ *          Sums are accumulated in float64 in a fixed order (deterministic).
+ */
+lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t* target,
+                                int64_t BT, int64_t ignore_index,
+                                float* mean_out, int64_t* n_valid, float* inv_n_valid,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LX_CE_TVD_H */

@@ -216,3 +216,42 @@ def full(w: Workload, threads: int | None = None, rows_limit: int | None = None)
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill, chunks))
     return zs, us, targets(w)[:n]
+
+
+def custom(BT: int, V: int, dtype: str, seed: int, scale: float = 2.0, teacher_noise: float | None = None,
+           ignore_rows=(), identical_rows=(), uniform_rows=(), offset_range: float = 0.0):
+    """Seeded inputs of any shape for parity cases that are not one of the named workloads.
+
+    Student ~ N(0, scale^2) (+ a per-row offset ~ U(-offset_range, offset_range));
+    teacher independent with the same law, or student + N(0, teacher_noise^2)
+    when ``teacher_noise`` is given.  Rows listed in ``identical_rows`` get a
+    bit-identical teacher, rows in ``uniform_rows`` a constant student row, rows
+    in ``ignore_rows`` the ignore index.  Returns (student_raw, teacher_raw,
+    target) with bf16 as uint16 bit patterns.
+    """
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ENTROPY, spawn_key=(1000 + seed,))))
+    z = g.standard_normal((BT, V), dtype=np.float32) * np.float32(scale)
+    if offset_range:
+        z += g.uniform(-offset_range, offset_range, size=(BT, 1)).astype(np.float32)
+    for r in uniform_rows:
+        z[r] = z[r, 0]
+    if teacher_noise is None:
+        u = g.standard_normal((BT, V), dtype=np.float32) * np.float32(scale)
+        if offset_range:
+            u += g.uniform(-offset_range, offset_range, size=(BT, 1)).astype(np.float32)
+    if dtype == "bf16":
+        zr = bf16_bits_rne(z)
+        if teacher_noise is not None:
+            u = bf16_bits_to_f32(zr) + g.standard_normal((BT, V), dtype=np.float32) * np.float32(teacher_noise)
+        ur = bf16_bits_rne(u)
+    else:
+        zr = z
+        if teacher_noise is not None:
+            u = z + g.standard_normal((BT, V), dtype=np.float32) * np.float32(teacher_noise)
+        ur = u.astype(np.float32)
+    for r in identical_rows:
+        ur[r] = zr[r]
+    t = g.integers(0, V, size=BT, dtype=np.int64)
+    for r in ignore_rows:
+        t[r] = IGNORE_INDEX
+    return np.ascontiguousarray(zr), np.ascontiguousarray(ur), t
