@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
-KERNEL_SOURCES = ["common.hpp", "forward.hip", "backward.hip", "reduce.hip"]
+KERNEL_SOURCES = ["common.hpp", "forward.hip", "forward_cluster.hip", "backward.hip", "reduce.hip"]
 
 
 def kernel_source_hash() -> str:

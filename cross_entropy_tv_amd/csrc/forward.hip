@@ -32,17 +32,19 @@ constexpr int kSplitMinChunk = 4096;  // elements
 constexpr int kMaxGrid = 1 << 20;
 
 FwdPlan plan_forward(int64_t BT, int64_t V, int esize, bool teacher) {
-  (void)esize;
-  FwdPlan p{1, 0};
-  if (BT <= 0 || BT >= kRowPathMinRows) return p;
-  int64_t s = (kSplitTargetBlocks + BT - 1) / BT;
-  const int64_t cap = (V + kSplitMinChunk - 1) / kSplitMinChunk;
-  if (s > cap) s = cap;
-  if (s > 1024) s = 1024;
-  if (s <= 1) return p;
-  p.split = (int)s;
-  const size_t per = teacher ? 6 : 2;
-  p.workspace_bytes = ((size_t)BT * (size_t)s * per * sizeof(float) + 255) & ~(size_t)255;
+  FwdPlan p{1, plan_cluster(BT, V, esize, teacher), 0};
+  if (BT > 0 && BT < kRowPathMinRows) {
+    int64_t s = (kSplitTargetBlocks + BT - 1) / BT;
+    const int64_t cap = (V + kSplitMinChunk - 1) / kSplitMinChunk;
+    if (s > cap) s = cap;
+    if (s > 1024) s = 1024;
+    if (s > 1) {
+      p.split = (int)s;
+      const size_t per = teacher ? 6 : 2;
+      p.workspace_bytes = ((size_t)BT * (size_t)s * per * sizeof(float) + 255) & ~(size_t)255;
+    }
+  }
+  if (p.cluster.workspace_bytes > p.workspace_bytes) p.workspace_bytes = p.cluster.workspace_bytes;
   return p;
 }
 
@@ -402,6 +404,9 @@ static hipError_t launch_forward_t(const FwdArgs& a, const FwdPlan& plan, hipStr
 
 hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream) {
   const bool teacher = a.teacher != nullptr;
+  // the read-once path needs both rows on 16-byte boundaries (V % 8 == 0 keeps every row there)
+  if (plan.cluster.K > 0 && ((((uintptr_t)a.student) | ((uintptr_t)a.teacher)) & 15u) == 0)
+    return launch_forward_cluster(a, plan.cluster, stream);
   if (bf16) {
     return teacher ? launch_forward_t<uint16_t, true>(a, plan, stream)
                    : launch_forward_t<uint16_t, false>(a, plan, stream);

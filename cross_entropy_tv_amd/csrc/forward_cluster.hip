@@ -1,0 +1,384 @@
+// Read-once forward of the fused CE + TVD loss for long bf16 rows.
+//
+// The "Forward Pass" section of the Liger-Kernel PR #1384 analysis page
+// streams a row twice: step 1 builds both log-sum-exps, step 2 forms p and q
+// from them and accumulates sum |p - q| and sum p * sign(p - q).  A 151936-
+// class bf16 row pair is ~600 KB, more than one compute unit holds, and an
+// L2 miss on MI355X crosses the same fabric whether the Infinity Cache has the
+// line or not, so the page's second stream doubles the traffic.  Here the row
+// is cut into K member chunks, each owned by one workgroup that keeps its
+// chunk in registers between the two steps, so every logit is read from HBM
+// exactly once:
+//
+//   1. a workgroup takes a ticket (a device-wide counter), which names its
+//      tile: row = ticket / K, member = ticket % K;
+//   2. it loads its chunk (up to G groups of 8 elements per thread and tensor)
+//      into registers with streaming loads;
+//   3. step 1: sum of exp(x - m) against one reference m per thread (the
+//      maximum of the thread's first group), so no running rescale is needed;
+//      a logit ~88 above that reference would overflow, which the thread
+//      detects and then redoes its sums against its true maxima (exact either
+//      way, and from registers);
+//   4. the workgroup publishes its (max, sum-exp) pairs for both tensors and
+//      waits for the K pairs of its row, merges them in member order (every
+//      member gets bit-identical log-sum-exps), and runs step 2 over its
+//      registers with the same p / q / sign helpers as the backward;
+//   5. it publishes its (sum |p - q|, sum p * sign) pair; the member that
+//      arrives last adds the K pairs in member order and writes ce, tvd,
+//      lse_s, lse_t and sigma.
+//
+// Exchange.  Every published value is one 64-bit word written with a
+// device-coherent atomic store into a slot that a fill kernel preset to the
+// all-ones pattern (a pair of NaNs, which no partial can be); readers poll
+// with device-coherent atomic loads until no slot of the row is empty, so a
+// slot is its own ready flag and no fence is needed.  Tickets are handed out
+// in the order workgroups start, so a workgroup only ever waits for members
+// of its own row that have started or will start once any running workgroup
+// exits: with at least K workgroups resident the exchange cannot deadlock.
+// Every wait is bounded; a wait that gives up leaves NaN in the row's outputs
+// instead of hanging.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lx {
+
+namespace {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint64_t kEmpty = ~0ull;          // unpublished slot
+constexpr unsigned kSpinLimit = 1u << 18;   // polls (each one a device-coherent load) before giving up
+
+constexpr int kRsrcFlags = 0x00020000;      // buffer resource word 3 for gfx9-family raw buffers
+constexpr int kStreamPolicy = 2;            // cache policy of the loads: non-temporal (streamed once)
+
+// Buffer resource covering `bytes` bytes from p: loads past the end return 0
+// without touching memory, so a thread's loads need no branch around them
+// (which would also keep the compiler from waiting on them one at a time).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint16_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, bytes, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4_t ld_stream(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kStreamPolicy));
+}
+
+__device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
+  x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+  x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+  x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
+  x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+
+__device__ __forceinline__ void publish(uint64_t* slot, uint64_t v) {
+  __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t peek(const uint64_t* slot) {
+  return __hip_atomic_load(const_cast<uint64_t*>(slot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Hides a packed group from common-subexpression elimination: without it the
+// compiler keeps step 1's unpacked floats (16 registers per group pair) alive
+// until step 2 instead of the 8 packed ones, and the chunk no longer fits.
+__device__ __forceinline__ void launder(u32x4_t& w) {
+  unsigned a = w.x, b = w.y, c = w.z, d = w.w;
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  w = (u32x4_t){a, b, c, d};
+}
+
+// sum of exp(x - m) over one group, m given as nb = -m * log2(e)
+__device__ __forceinline__ void expsum8(const u32x4_t& w, float nb, float& s0, float& s1) {
+  float x[8];
+  unpack8(w, x);
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    s0 += exp2_hw(__builtin_fmaf(x[e], kLog2e, nb));
+    s1 += exp2_hw(__builtin_fmaf(x[e + 1], kLog2e, nb));
+  }
+}
+
+// step-2 accumulation of one group pair: |p - q| and p * sign(p - q)
+__device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float nbs, float nbt, float& A0,
+                                    float& A1, float& S0, float& S1) {
+  float x[8], y[8];
+  unpack8(wz, x);
+  unpack8(wu, y);
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float p0 = prob(x[e], nbs), q0 = prob(y[e], nbt);
+    const float p1 = prob(x[e + 1], nbs), q1 = prob(y[e + 1], nbt);
+    const float d0 = p0 - q0, d1 = p1 - q1;
+    A0 += fabsf(d0);
+    A1 += fabsf(d1);
+    S0 = __builtin_fmaf(p0, sign0(d0), S0);
+    S1 = __builtin_fmaf(p1, sign0(d1), S1);
+  }
+}
+
+// Lanes [0, n) of wave 0 poll slots sl[0..n) until none is empty (or the
+// bounded wait gives up) and store what they read in got[]; n <= 64.
+// Returns true, in wave 0, when the wait gave up.
+__device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* got) {
+  const int lane = threadIdx.x;
+  const bool mine = lane < n;
+  uint64_t v = kEmpty;
+  unsigned spins = 0;
+  bool gave_up = false;
+  for (;;) {
+    if (mine && v == kEmpty) v = peek(sl + lane);
+    if (__all(!mine || v != kEmpty)) break;
+    if (++spins > kSpinLimit) {
+      gave_up = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (mine) got[lane] = v;
+  return gave_up;
+}
+
+}  // namespace
+
+template <int NT, int G>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2 * NT / 256, 2 * NT / 256)))
+void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __restrict__ teacher,
+                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
+                        float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
+                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
+                        uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
+                        unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
+  constexpr int W = NT / 64;
+  __shared__ Lse red_z[W], red_u[W];
+  __shared__ float red_a[W], red_s[W];
+  __shared__ uint64_t got[2 * kClusterMaxK];
+  __shared__ unsigned s_tile;
+  __shared__ float s_lse[2];
+
+  const int tid = threadIdx.x;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned tile = s_tile;
+  const int64_t r = tile / (unsigned)K;
+  const int j = (int)(tile - (unsigned)r * (unsigned)K);
+  const int64_t t = target[r];
+  if (t == ignore_index) {
+    if (j == 0 && tid == 0) {
+      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
+    }
+    return;
+  }
+
+  // ---- this member's chunk: groups [gb, ge) of the row; thread tid owns gb + tid + i * NT
+  const int NG = V >> 3;
+  const int gb = j * gpm;
+  const int ge = min(NG, gb + gpm);
+  const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
+  const int64_t row = r * (int64_t)V;
+  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  u32x4_t rz[G], ru[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+    ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+  }
+  const bool t_ok = t >= 0 && t < V;
+
+  // ---- step 1: sums of exponentials against this thread's reference maxima
+  float mz = kMFloor, mu = kMFloor;
+  if (n > 0) {
+    float x[8], y[8];
+    unpack8(rz[0], x);
+    unpack8(ru[0], y);
+    mz = fmaxf(mz, max8(x));
+    mu = fmaxf(mu, max8(y));
+  }
+  float sz0 = 0.f, sz1 = 0.f, su0 = 0.f, su1 = 0.f;
+  {
+    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        expsum8(rz[i], nbz, sz0, sz1);
+        expsum8(ru[i], nbu, su0, su1);
+      }
+    }
+  }
+  if (!(sz0 + sz1 < 3.0e38f) || !(su0 + su1 < 3.0e38f)) {
+    // a logit far above the first group's maximum: redo against the true maxima
+#pragma unroll
+    for (int i = 1; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        float x[8], y[8];
+        unpack8(rz[i], x);
+        unpack8(ru[i], y);
+        mz = fmaxf(mz, max8(x));
+        mu = fmaxf(mu, max8(y));
+      }
+    }
+    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+    sz0 = sz1 = su0 = su1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        expsum8(rz[i], nbz, sz0, sz1);
+        expsum8(ru[i], nbu, su0, su1);
+      }
+    }
+  }
+  {
+    Lse pz = wave_lse(Lse{mz, sz0 + sz1});
+    Lse pu = wave_lse(Lse{mu, su0 + su1});
+    if ((tid & 63) == 0) {
+      red_z[tid >> 6] = pz;
+      red_u[tid >> 6] = pu;
+    }
+  }
+  __syncthreads();
+  uint64_t* s1 = slot1 + r * (int64_t)K * 2;
+  if (tid == 0) {
+    Lse fz = red_z[0], fu = red_u[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      lse_merge(fz, red_z[w]);
+      lse_merge(fu, red_u[w]);
+    }
+    publish(s1 + 2 * j, pack2(fz.m, fz.s));
+    publish(s1 + 2 * j + 1, pack2(fu.m, fu.s));
+  }
+
+  // ---- exchange 1: the row's K (max, sum-exp) pairs, merged in member order
+  if (tid < 64) wait_slots(s1, 2 * K, got);
+  __syncthreads();
+  if (tid == 0) {
+    Lse fz{lo_f(got[0]), hi_f(got[0])}, fu{lo_f(got[1]), hi_f(got[1])};
+    for (int k = 1; k < K; ++k) {
+      lse_merge(fz, Lse{lo_f(got[2 * k]), hi_f(got[2 * k])});
+      lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
+    }
+    s_lse[0] = lse_value(fz);
+    s_lse[1] = lse_value(fu);
+  }
+  __syncthreads();
+  const float lse_s = s_lse[0], lse_t = s_lse[1];
+
+  // ---- step 2 over the kept chunk
+  const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
+  float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (i < n) {
+      launder(rz[i]);
+      launder(ru[i]);
+      tv8(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
+    }
+  }
+  {
+    const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
+    if ((tid & 63) == 0) {
+      red_a[tid >> 6] = A;
+      red_s[tid >> 6] = S;
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+
+  // ---- exchange 2: the last member to arrive adds the K pairs in member order
+  uint64_t* s2 = slot2 + r * (int64_t)K;
+  unsigned old = 0;
+  if (tid == 0) {
+    float A = red_a[0], S = red_s[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      A += red_a[w];
+      S += red_s[w];
+    }
+    publish(s2 + j, pack2(A, S));
+    old = __hip_atomic_fetch_add(arrived + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  old = __shfl(old, 0, 64);
+  if (old != (unsigned)(K - 1)) return;
+  float zt = 0.f;
+  if (tid == 0 && t_ok) zt = load1(student + row + t);
+  wait_slots(s2, K, got);
+  if (tid == 0) {
+    float A = lo_f(got[0]), S = hi_f(got[0]);
+    for (int k = 1; k < K; ++k) {
+      A += lo_f(got[k]);
+      S += hi_f(got[k]);
+    }
+    if (t_ok) ce[r] = lse_s - zt; else store_nan(ce + r);
+    tvd[r] = 0.5f * A;
+    lse_s_out[r] = lse_s;
+    lse_t_out[r] = lse_t;
+    sigma_out[r] = S;
+  }
+}
+
+// Presets the exchange slots to kEmpty and the arrival counters and the ticket to 0.
+__global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restrict__ slots, int64_t nslots,
+                                                              unsigned* __restrict__ zeros, int64_t nzeros) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < nslots; i += stride) slots[i] = kEmpty;
+  for (int64_t i = i0; i < nzeros; i += stride) zeros[i] = 0u;
+}
+
+// ---------------------------------------------------------------- planning and launch
+
+constexpr int kClThreads = 512;
+constexpr int kClGroups = 10;            // G: groups of 8 per thread and tensor kept in registers
+constexpr int64_t kClTargetTiles = 2048;  // enough workgroups to fill 256 compute units several times
+
+ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
+  ClusterPlan c{0, 0, 0};
+  if (!teacher || esize != 2 || V % 8 != 0 || BT <= 0) return c;
+  const int64_t NG = V / 8;
+  if (NG < kClThreads) return c;  // short rows: the one-workgroup-per-row path is as good
+  const int64_t cap = (int64_t)kClThreads * kClGroups;
+  const int64_t k_fit = (NG + cap - 1) / cap;        // fewest members whose chunks fit in registers
+  int64_t k_fill = (kClTargetTiles + BT - 1) / BT;  // members that give enough workgroups
+  if (k_fill > NG / kClThreads) k_fill = NG / kClThreads;  // every thread keeps at least one group
+  int64_t K = k_fit > k_fill ? k_fit : k_fill;
+  if (K > kClusterMaxK) K = kClusterMaxK;
+  const int64_t gpm = (NG + K - 1) / K;
+  if (gpm > cap) return c;  // a row too long for kClusterMaxK members
+  K = (NG + gpm - 1) / gpm;  // no empty member
+  if (BT * K >= ((int64_t)1 << 31)) return c;  // tickets are 32-bit
+  c.K = (int)K;
+  c.gpm = (int)gpm;
+  const size_t slots = (size_t)BT * (size_t)K * 3 * sizeof(uint64_t);
+  const size_t counters = ((size_t)BT + 1) * sizeof(unsigned);
+  c.workspace_bytes = (slots + counters + 255) & ~(size_t)255;
+  return c;
+}
+
+hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
+  (void)hipGetLastError();
+  uint64_t* slot1 = static_cast<uint64_t*>(a.workspace);
+  uint64_t* slot2 = slot1 + a.BT * (int64_t)c.K * 2;
+  unsigned* arrived = reinterpret_cast<unsigned*>(slot2 + a.BT * (int64_t)c.K);
+  unsigned* ticket = arrived + a.BT;
+  const int64_t nslots = a.BT * (int64_t)c.K * 3;
+  const int64_t nzeros = a.BT + 1;
+  const int64_t blocks = (nslots + 255) / 256;
+  hipLaunchKernelGGL(cluster_ws_init_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
+                     slot1, nslots, arrived, nzeros);
+  const int64_t tiles = a.BT * (int64_t)c.K;
+  hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups>), dim3((unsigned)tiles), dim3(kClThreads), 0, st,
+                     static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher), a.target,
+                     (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, slot1, slot2,
+                     arrived, ticket);
+  return hipGetLastError();
+}
+
+}  // namespace lx

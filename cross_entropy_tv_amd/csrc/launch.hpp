@@ -12,9 +12,25 @@ namespace lx {
 //   split  > 1: each row is cut into `split` chunks handled by separate
 //               workgroups; per-chunk partials go through the workspace and
 //               are merged in chunk order ("split-V path").
+//   cluster.K > 0: long bf16 rows with a teacher; each row is cut into K
+//               member chunks kept in registers by K cooperating workgroups,
+//               so the logits are read once ("read-once path").  Taken when
+//               the student and teacher rows are 16-byte aligned; otherwise
+//               the forward falls back to the row or split-V path.
+constexpr int kClusterMaxK = 32;
+
+struct ClusterPlan {
+  int K;    // member workgroups per row (0: not applicable)
+  int gpm;  // groups of 8 elements per member
+  size_t workspace_bytes;
+};
+
+ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher);
+
 struct FwdPlan {
   int split;
-  size_t workspace_bytes;
+  ClusterPlan cluster;
+  size_t workspace_bytes;  // enough for whichever path the call takes
 };
 
 FwdPlan plan_forward(int64_t BT, int64_t V, int esize, bool teacher);
@@ -42,6 +58,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream);
+hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
                               int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,

@@ -69,7 +69,12 @@ def test_forward_validation():
     # split-V shape (few rows, long rows) needs a workspace
     need = lx.lx_ce_tvd_workspace_bytes(4, 100000, 1, 1)
     assert need > 0 and lx.lx_ce_tvd_workspace_bytes(4, 100000, 1, 0) < need
-    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1) == 0
+    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 0) == 0   # CE-only: one stream, no exchange
+    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 0, 1) == 0   # f32 rows: one workgroup per row
+    # bf16 with a teacher: the read-once path exchanges per-row partials of its K = 4
+    # member workgroups (3 64-bit slots per member) and keeps a counter per row + a ticket
+    slots, counters = 8192 * 4 * 3 * 8, (8192 + 1) * 4
+    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1) == (slots + counters + 255) // 256 * 256
     assert fwd(V=100000, teacher=A * 2) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6, wsb=need - 4) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6 + 16, wsb=need) == lx.LX_ERR_WORKSPACE  # 256-B alignment

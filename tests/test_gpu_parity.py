@@ -115,6 +115,39 @@ def test_ragged_shapes(BT, V, dtype, teacher):
         assert abs(host(out)["ce"][3] - math.log(V)) <= 1e-4
 
 
+@pytest.mark.parametrize("BT,V", [(520, 8200), (600, 20000), (512, 24576)],
+                         ids=["cluster_520x8200", "cluster_600x20000", "cluster_512x24576"])
+def test_cluster_path_shapes(BT, V):
+    """Read-once forward (rows split across cooperating workgroups): ragged last member,
+    ignored / identical / uniform rows, and rows whose logits span more than the
+    per-thread exponent range (the overflow fallback)."""
+    z, u, t = W.custom(BT, V, "bf16", seed=BT + V, scale=3.0, teacher_noise=0.5,
+                       ignore_rows=[0, 7, BT - 1], identical_rows=[2, 9], uniform_rows=[3])
+    hi = W.bf16_bits_rne(np.array([150.0, 120.0], dtype=np.float32))
+    z[5, V // 3] = hi[0]          # far above every thread's first-group reference
+    u[6, V - 5] = hi[1]
+    z[8, 1], u[8, 2] = hi[0], hi[1]
+    out, g = full_case(f"cluster {BT}x{V}", z, u, t, g_ce=0.5, g_tvd=1.5)
+    o = host(out)
+    assert o["tvd"][2] == 0.0 and o["sigma"][2] == 0.0 and o["tvd"][9] == 0.0
+    assert abs(o["ce"][3] - math.log(V)) <= 1e-4
+
+
+def test_cluster_path_deterministic_and_matches_row_path():
+    z, u, t = W.custom(530, 16384, "bf16", seed=77, scale=2.0, offset_range=10.0, ignore_rows=[4])
+    announce("cluster path: 3 repeats bitwise, and vs the two-stream row path on unaligned copies")
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    runs = [host(run_fwd(zs, us, tg)) for _ in range(3)]
+    for o in runs[1:]:
+        for k in o:
+            assert np.array_equal(bits32(o[k]), bits32(runs[0][k])), k
+    # an unaligned copy takes the two-stream row path: same results within the tolerances
+    zo, uo = _offset_view(z, 1), _offset_view(u, 1)
+    o2 = host(run_fwd(zo, uo, tg))
+    for k, tol in (("ce", 1e-4), ("lse_s", 1e-4), ("lse_t", 1e-4), ("tvd", 2e-5), ("sigma", 2e-5)):
+        assert np.max(np.abs(o2[k] - runs[0][k])) <= tol, k
+
+
 def test_independent_teacher_and_offsets():
     z, u, t = W.custom(40, 70001, "bf16", seed=5, scale=2.0, offset_range=20.0)
     full_case("split 40x70001 bf16 offsets", z, u, t, g_ce=1.0, g_tvd=-0.75)
