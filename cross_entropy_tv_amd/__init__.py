@@ -60,6 +60,12 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_backward.restype = i32
     L.lx_ce_tvd_reduce_mean.argtypes = [p, p, p, i64, i64, p, p, p, p]
     L.lx_ce_tvd_reduce_mean.restype = i32
+    L.lx_ce_tvd_forward_backward_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    L.lx_ce_tvd_forward_backward_workspace_bytes.restype = sz
+    L.lx_ce_tvd_forward_backward.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p, p, f32, f32, p, i32, p, sz, p]
+    L.lx_ce_tvd_forward_backward.restype = i32
+    L.lx_ce_tvd_count_valid.argtypes = [p, i64, i64, p, p, p]
+    L.lx_ce_tvd_count_valid.restype = i32
     return L
 
 
@@ -147,6 +153,39 @@ def lx_ce_tvd_backward(grad, student, teacher, target, ignore_index, lse_s, lse_
            "lx_ce_tvd_backward")
 
 
+def lx_ce_tvd_forward_backward_workspace_bytes(BT: int, V: int, dt: int, has_teacher: bool) -> int:
+    return lib.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, int(bool(has_teacher)))
+
+
+def lx_ce_tvd_forward_backward(student, teacher, target, ignore_index, ce, tvd, lse_s, lse_t, sigma, grad,
+                               g_ce: float, g_tvd: float, g_scale=None, workspace=None, stream=None) -> None:
+    """Forward outputs and the student gradient in one call (``grad`` may be
+    ``student``).  ``workspace`` as in lx_ce_tvd_forward, sized by
+    lx_ce_tvd_forward_backward_workspace_bytes."""
+    BT, V = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if teacher is not None and (teacher.shape != student.shape or teacher.dtype != student.dtype):
+        raise ValueError("teacher must match student in shape and dtype")
+    if grad.shape != student.shape or grad.dtype != student.dtype or not grad.is_contiguous():
+        raise ValueError("grad must match student in shape and dtype and be contiguous")
+    need = lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher is not None)
+    if workspace is None and need:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=student.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lx_ce_tvd_forward_backward(_ptr(student), _ptr(teacher), _ptr(target), BT, V, int(ignore_index),
+                                          _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t), _ptr(sigma), _ptr(grad),
+                                          float(g_ce), float(g_tvd), _ptr(g_scale), dt, _ptr(workspace), wbytes,
+                                          _stream(stream)), "lx_ce_tvd_forward_backward")
+
+
+def lx_ce_tvd_count_valid(target, ignore_index, n_valid=None, inv_n_valid=None, stream=None) -> None:
+    """Number of non-ignored rows (int64 [1]) and its reciprocal (float32 [1])."""
+    BT = target.shape[0]
+    _check(lib.lx_ce_tvd_count_valid(_ptr(target), BT, int(ignore_index), _ptr(n_valid), _ptr(inv_n_valid),
+                                     _stream(stream)), "lx_ce_tvd_count_valid")
+
+
 def lx_ce_tvd_reduce_mean(ce, tvd, target, ignore_index, mean_out, n_valid=None, inv_n_valid=None,
                           stream=None) -> None:
     """Mean of ce (and tvd) over non-ignored rows into mean_out (float32 [2])."""
@@ -160,4 +199,5 @@ __all__ = [
     "LxError", "lib", "LIB_PATH", "LX_OK", "LX_ERR_INVALID_ARG", "LX_ERR_UNSUPPORTED_DTYPE", "LX_ERR_ALIAS",
     "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "lx_status_string", "lx_abi_version",
     "lx_ce_tvd_workspace_bytes", "lx_ce_tvd_forward", "lx_ce_tvd_backward", "lx_ce_tvd_reduce_mean",
+    "lx_ce_tvd_forward_backward_workspace_bytes", "lx_ce_tvd_forward_backward", "lx_ce_tvd_count_valid",
 ]

@@ -165,6 +165,102 @@ lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teache
   return from_hip(lx::launch_backward(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
 }
 
+size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher) {
+  const int es = esize_of(dt);
+  if (!es || check_shape(BT, V, es) != LX_OK) return 0;
+  const size_t f = lx::plan_forward(BT, V, es, has_teacher != 0).workspace_bytes;
+  const size_t u = lx::plan_fused(BT, V, es, has_teacher != 0).workspace_bytes;
+  return f > u ? f : u;
+}
+
+lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                                     int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s,
+                                     float* lse_t, float* sigma, void* grad, float g_ce, float g_tvd,
+                                     const float* g_scale, lx_dtype dt, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = teacher != nullptr;
+  if (!student || !target || !ce || !lse_s || !grad) return LX_ERR_INVALID_ARG;
+  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(grad, es) || !aligned(target, 8) ||
+      !aligned(ce, 4) || !aligned(lse_s, 4) || (g_scale && !aligned(g_scale, 4)))
+    return LX_ERR_INVALID_ARG;
+  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
+
+  const int64_t lb = BT * V * es, fb = BT * 4;
+  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
+  const lx::ClusterPlan fused = lx::plan_fused(BT, V, es, has_t);
+  const size_t need = plan.workspace_bytes > fused.workspace_bytes ? plan.workspace_bytes : fused.workspace_bytes;
+  // 0..2 inputs (may overlap each other), 3..8 outputs and workspace, 9 g_scale (input)
+  Span sp[10] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(ce, fb), span(lse_s, fb),
+                 span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
+                 span(has_t ? sigma : nullptr, fb), span(need ? workspace : nullptr, (int64_t)need),
+                 span(g_scale, 4)};
+  for (int o = 3; o < 9; ++o)
+    for (int i = 0; i < 10; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  // the gradient may be the student logits themselves (in place); any other overlap is an error
+  const Span g = span(grad, lb);
+  if (grad != student && overlaps(g, sp[0])) return LX_ERR_ALIAS;
+  for (int i = 1; i < 10; ++i)
+    if (overlaps(g, sp[i])) return LX_ERR_ALIAS;
+  if (need) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
+  }
+
+  lx::FwdArgs a;
+  a.student = student;
+  a.teacher = teacher;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.ce = ce;
+  a.tvd = tvd;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.vec = (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0;
+  a.workspace = workspace;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused.K > 0 && ((((uintptr_t)student) | ((uintptr_t)teacher) | ((uintptr_t)grad)) & 15u) == 0) {
+    const lx::FusedGrad fg{grad, g_ce, g_tvd, g_scale};
+    return from_hip(lx::launch_fused_cluster(a, fg, fused, st));
+  }
+  // no fused kernel for this shape or layout: the forward, then the backward, on the same stream
+  if (lx_status s = from_hip(lx::launch_forward(a, plan, dt == LX_BF16, st))) return s;
+  lx::BwdArgs b;
+  b.grad = grad;
+  b.student = student;
+  b.teacher = teacher;
+  b.target = target;
+  b.BT = BT;
+  b.V = V;
+  b.ignore_index = ignore_index;
+  b.lse_s = lse_s;
+  b.lse_t = lse_t;
+  b.sigma = sigma;
+  b.g_ce = g_ce;
+  b.g_tvd = g_tvd;
+  b.g_scale = g_scale;
+  const uintptr_t m = (uintptr_t)student & 15u;
+  b.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
+  return from_hip(lx::launch_backward(b, dt == LX_BF16, st));
+}
+
+lx_status lx_ce_tvd_count_valid(const int64_t* target, int64_t BT, int64_t ignore_index, int64_t* n_valid,
+                                float* inv_n_valid, void* stream) {
+  if (BT < 0 || (BT > 0 && !target) || (!n_valid && !inv_n_valid)) return LX_ERR_INVALID_ARG;
+  if (!aligned(target, 8) || !aligned(n_valid, 8) || !aligned(inv_n_valid, 4)) return LX_ERR_INVALID_ARG;
+  const Span sp[3] = {span(target, BT * 8), span(n_valid, 8), span(inv_n_valid, 4)};
+  if (any_overlap(sp, 3)) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_reduce_mean(nullptr, nullptr, target, BT, ignore_index, nullptr, n_valid, inv_n_valid,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
                                 int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,
                                 void* stream) {

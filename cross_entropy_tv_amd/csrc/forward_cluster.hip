@@ -61,6 +61,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint16_t* p, 
 __device__ __forceinline__ u32x4_t ld_stream(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kStreamPolicy));
 }
+__device__ __forceinline__ void st_stream(__amdgpu_buffer_rsrc_t rs, int byte_off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, byte_off, 0, kStreamPolicy);
+}
 
 __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
   x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
@@ -144,8 +147,10 @@ __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* 
 
 }  // namespace
 
-template <int NT, int G>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2 * NT / 256, 2 * NT / 256)))
+// NT threads per workgroup, G groups of 8 elements per thread and tensor, WPE
+// waves per SIMD (occupancy the register budget is sized for).
+template <int NT, int G, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
 void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __restrict__ teacher,
                         const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
                         float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
@@ -324,6 +329,279 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
   }
 }
 
+// ---------------------------------------------------------------- kept-exponential variant
+//
+// Keeps E = exp(x - m) (fp32, twice the registers of the bf16 logits) instead
+// of the logits, m being the thread's exact maximum over its groups (taken
+// while the chunk is unpacked, so no exponential can overflow), so that step 2
+// forms P = p * 2^126 as E * (exp(m - lse) *
+// 2^126), one multiply per element instead of an exponential.  The 2^126
+// scale makes sign(p - q) a plain med3(P - Q, -1, 1): a nonzero difference of
+// two scaled probabilities is at least 1 in magnitude unless both p and q are
+// below 2^-103.  Products are never contracted into the differences, so
+// bit-identical student and teacher rows give P == Q exactly.
+//
+// FUSED additionally writes the student gradient of the "Backward Pass"
+// section, g = p * (alpha + beta * s) - k * g_ce * [v == t], from the kept
+// exponentials: every member waits for the K step-2 pairs (so all members hold
+// the same sigma), then stores its chunk of the gradient.  Each member has
+// read its whole chunk, and member 0 the target logit, before any member
+// stores, so the gradient may overwrite the student logits.
+template <int NT, int G, int WPE, bool FUSED>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
+void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
+                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
+                        float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
+                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
+                        uint16_t* grad, float g_ce, float g_tvd, const float* __restrict__ g_scale,
+                        uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
+                        unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
+  constexpr int W = NT / 64;
+  __shared__ Lse red_z[W], red_u[W];
+  __shared__ float red_a[W], red_s[W];
+  __shared__ uint64_t got[2 * kClusterMaxK];
+  __shared__ unsigned s_tile;
+  __shared__ float s_bc[4];
+  __shared__ float s_zt;
+
+  const int tid = threadIdx.x;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned tile = s_tile;
+  const int64_t r = tile / (unsigned)K;
+  const int j = (int)(tile - (unsigned)r * (unsigned)K);
+  const int64_t t = target[r];
+  const int NG = V >> 3;
+  const int gb = j * gpm;
+  const int ge = min(NG, gb + gpm);
+  const int64_t row = r * (int64_t)V;
+  const bool t_ok = t >= 0 && t < V;
+  if (t == ignore_index) {
+    if (j == 0 && tid == 0) {
+      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
+    }
+    if (FUSED) {
+      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+#pragma unroll
+      for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
+    }
+    return;
+  }
+  const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
+  float zt = 0.f;
+  if (j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
+
+  // ---- load the chunk; unpack it into the E registers and take this thread's exact maxima
+  float ez[G][8], eu[G][8];
+  float mz = kMFloor, mu = kMFloor;
+  {
+    const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
+    const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
+    u32x4_t rz[G], ru[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+      ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      unpack8(rz[i], ez[i]);
+      unpack8(ru[i], eu[i]);
+      if (i < n) {
+        mz = fmaxf(mz, max8(ez[i]));
+        mu = fmaxf(mu, max8(eu[i]));
+      }
+    }
+  }
+  // ---- step 1: E = exp(x - m) in place (every E <= 1: no overflow), and its sums
+  float sz0 = 0.f, sz1 = 0.f, su0 = 0.f, su1 = 0.f;
+  {
+    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ez[i][e] = exp2_hw(__builtin_fmaf(ez[i][e], kLog2e, nbz));
+        eu[i][e] = exp2_hw(__builtin_fmaf(eu[i][e], kLog2e, nbu));
+      }
+      if (i < n) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          sz0 += ez[i][e];
+          sz1 += ez[i][e + 1];
+          su0 += eu[i][e];
+          su1 += eu[i][e + 1];
+        }
+      }
+    }
+  }
+  {
+    Lse pz = wave_lse(Lse{mz, sz0 + sz1});
+    Lse pu = wave_lse(Lse{mu, su0 + su1});
+    if ((tid & 63) == 0) {
+      red_z[tid >> 6] = pz;
+      red_u[tid >> 6] = pu;
+    }
+    // the target logit has been read (not merely requested) before this member
+    // publishes anything, hence before any member can store a gradient over it
+    if (tid == 0) s_zt = zt;
+  }
+  __syncthreads();
+  uint64_t* s1 = slot1 + r * (int64_t)K * 2;
+  if (tid == 0) {
+    Lse fz = red_z[0], fu = red_u[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      lse_merge(fz, red_z[w]);
+      lse_merge(fu, red_u[w]);
+    }
+    publish(s1 + 2 * j, pack2(fz.m, fz.s));
+    publish(s1 + 2 * j + 1, pack2(fu.m, fu.s));
+  }
+
+  // ---- exchange 1: the row's K (max, sum-exp) pairs, merged in member order
+  if (tid < 64) wait_slots(s1, 2 * K, got);
+  __syncthreads();
+  if (tid == 0) {
+    Lse fz{lo_f(got[0]), hi_f(got[0])}, fu{lo_f(got[1]), hi_f(got[1])};
+    for (int k = 1; k < K; ++k) {
+      lse_merge(fz, Lse{lo_f(got[2 * k]), hi_f(got[2 * k])});
+      lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
+    }
+    s_bc[0] = lse_value(fz);
+    s_bc[1] = lse_value(fu);
+  }
+  __syncthreads();
+  const float lse_s = s_bc[0], lse_t = s_bc[1];
+
+  // ---- step 2: P = E * (exp(m - lse) * 2^126), sum |P - Q| and P * sign(P - Q)
+  const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(lse_s)));
+  const float cu = exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t)));
+  {
+    const float czs = cz * 0x1p126f, cus = cu * 0x1p126f;
+    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float P0 = ez[i][e] * czs, Q0 = eu[i][e] * cus;
+          const float P1 = ez[i][e + 1] * czs, Q1 = eu[i][e + 1] * cus;
+          const float D0 = P0 - Q0, D1 = P1 - Q1;
+          A0 += fabsf(D0);
+          A1 += fabsf(D1);
+          S0 = __builtin_fmaf(P0, __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f), S0);
+          S1 = __builtin_fmaf(P1, __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f), S1);
+        }
+      }
+    }
+    const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
+    if ((tid & 63) == 0) {
+      red_a[tid >> 6] = A;
+      red_s[tid >> 6] = S;
+    }
+  }
+  __syncthreads();
+  uint64_t* s2 = slot2 + r * (int64_t)K;
+  if (!FUSED) {
+    // ---- exchange 2: the last member to arrive adds the K pairs in member order
+    if (tid >= 64) return;
+    unsigned old = 0;
+    if (tid == 0) {
+      float A = red_a[0], S = red_s[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        A += red_a[w];
+        S += red_s[w];
+      }
+      publish(s2 + j, pack2(A, S));
+      old = __hip_atomic_fetch_add(arrived + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = __shfl(old, 0, 64);
+    if (old != (unsigned)(K - 1)) return;
+    if (tid == 0 && t_ok) zt = load1(student + row + t);
+    wait_slots(s2, K, got);
+    if (tid == 0) {
+      float A = lo_f(got[0]), S = hi_f(got[0]);
+      for (int k = 1; k < K; ++k) {
+        A += lo_f(got[k]);
+        S += hi_f(got[k]);
+      }
+      if (t_ok) ce[r] = lse_s - zt; else store_nan(ce + r);
+      tvd[r] = 0.5f * A * 0x1p-126f;
+      lse_s_out[r] = lse_s;
+      lse_t_out[r] = lse_t;
+      sigma_out[r] = S * 0x1p-126f;
+    }
+    return;
+  } else {
+    // ---- exchange 2: every member sums the K pairs in member order (identical sigma)
+    if (tid == 0) {
+      float A = red_a[0], S = red_s[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        A += red_a[w];
+        S += red_s[w];
+      }
+      publish(s2 + j, pack2(A, S));
+    }
+    if (tid < 64) wait_slots(s2, K, got);
+    __syncthreads();
+    if (tid == 0) {
+      float A = lo_f(got[0]), S = hi_f(got[0]);
+      for (int k = 1; k < K; ++k) {
+        A += lo_f(got[k]);
+        S += hi_f(got[k]);
+      }
+      s_bc[2] = 0.5f * A * 0x1p-126f;
+      s_bc[3] = S * 0x1p-126f;
+      if (j == 0) {
+        if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
+        tvd[r] = s_bc[2];
+        lse_s_out[r] = lse_s;
+        lse_t_out[r] = lse_t;
+        sigma_out[r] = s_bc[3];
+      }
+    }
+    __syncthreads();
+    // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
+    const float k = g_scale ? *g_scale : 1.0f;
+    const float kce = k * g_ce;
+    const float beta = 0.5f * k * g_tvd;
+    const float alpha = kce - beta * s_bc[3];
+    const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+    const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int g = tid + i * NT;
+      float o[8];
+      {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = ez[i][e] * cz, q = eu[i][e] * cu;
+          o[e] = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+        }
+      }
+      const int rel = trel - 8 * g;
+      if ((unsigned)rel < 8u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+      }
+      u32x4_t w;
+      if (t_ok) {
+        w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
+        w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
+      } else {
+        const unsigned h = kQNaN16 | (kQNaN16 << 16);
+        w = (u32x4_t){h, h, h, h};
+      }
+      st_stream(rsg, g * 16, w);
+    }
+  }
+}
+
 // Presets the exchange slots to kEmpty and the arrival counters and the ticket to 0.
 __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restrict__ slots, int64_t nslots,
                                                               unsigned* __restrict__ zeros, int64_t nzeros) {
@@ -335,19 +613,37 @@ __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restri
 
 // ---------------------------------------------------------------- planning and launch
 
-constexpr int kClThreads = 512;
-constexpr int kClGroups = 10;            // G: groups of 8 per thread and tensor kept in registers
+// Forward kernel: NT threads x G groups of bf16 logits per thread and tensor,
+// WPE waves per SIMD (three 256-thread workgroups per compute unit).  Measured
+// on the 8192 x 151936 training batch: 256 x 16 x 3 (K = 5) 1.03 ms, 256 x 10
+// x 4 (K = 8) 1.06 ms, 512 x 10 x 4 (K = 4) 1.14 ms, 1024 x 10 x 4 1.23 ms.
+constexpr int kClThreads = 256;
+constexpr int kClGroups = 16;
+constexpr int kClWavesPerSimd = 3;
+// The forward keeps logits (false) or exponentials (true, cluster_exp_kernel).
+// Keeping exponentials halves the elements a thread holds, so more members
+// share a row, and measured slower (1.20 ms at 256 x 8 x 3).
+constexpr bool kFwdKeepExp = false;
+constexpr int kFwdExpThreads = 256;
+constexpr int kFwdExpGroups = 8;
+constexpr int kFwdExpWavesPerSimd = 3;
+// Fused forward + backward kernel (keeps exponentials; step 3 then needs no
+// exponential).  Measured: 256 x 8 x 3 (K = 10) 1.72 ms, 256 x 6 x 4 1.79 ms,
+// 256 x 12 x 2 1.82 ms, 512 x 4 x 4 2.04 ms, 128 x 8 x 3 2.02 ms.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedGroups = 8;
+constexpr int kFusedWavesPerSimd = 3;
 constexpr int64_t kClTargetTiles = 2048;  // enough workgroups to fill 256 compute units several times
 
-ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
+static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, bool teacher, int nt, int groups) {
   ClusterPlan c{0, 0, 0};
   if (!teacher || esize != 2 || V % 8 != 0 || BT <= 0) return c;
   const int64_t NG = V / 8;
-  if (NG < kClThreads) return c;  // short rows: the one-workgroup-per-row path is as good
-  const int64_t cap = (int64_t)kClThreads * kClGroups;
+  if (NG < nt) return c;  // short rows: the one-workgroup-per-row path is as good
+  const int64_t cap = (int64_t)nt * groups;
   const int64_t k_fit = (NG + cap - 1) / cap;        // fewest members whose chunks fit in registers
   int64_t k_fill = (kClTargetTiles + BT - 1) / BT;  // members that give enough workgroups
-  if (k_fill > NG / kClThreads) k_fill = NG / kClThreads;  // every thread keeps at least one group
+  if (k_fill > NG / nt) k_fill = NG / nt;            // every thread keeps at least one group
   int64_t K = k_fit > k_fill ? k_fit : k_fill;
   if (K > kClusterMaxK) K = kClusterMaxK;
   const int64_t gpm = (NG + K - 1) / K;
@@ -362,22 +658,62 @@ ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
   return c;
 }
 
-hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
-  (void)hipGetLastError();
-  uint64_t* slot1 = static_cast<uint64_t*>(a.workspace);
-  uint64_t* slot2 = slot1 + a.BT * (int64_t)c.K * 2;
-  unsigned* arrived = reinterpret_cast<unsigned*>(slot2 + a.BT * (int64_t)c.K);
-  unsigned* ticket = arrived + a.BT;
-  const int64_t nslots = a.BT * (int64_t)c.K * 3;
-  const int64_t nzeros = a.BT + 1;
+ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
+  return kFwdKeepExp ? plan_cfg(BT, V, esize, teacher, kFwdExpThreads, kFwdExpGroups)
+                     : plan_cfg(BT, V, esize, teacher, kClThreads, kClGroups);
+}
+
+ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher) {
+  return plan_cfg(BT, V, esize, teacher, kFusedThreads, kFusedGroups);
+}
+
+// Workspace: slot1 [BT][K][2] | slot2 [BT][K] (64-bit) | arrived [BT] | ticket (32-bit)
+struct ClusterWs {
+  uint64_t *slot1, *slot2;
+  unsigned *arrived, *ticket;
+};
+
+static ClusterWs cluster_ws(void* ws, int64_t BT, int K, hipStream_t st) {
+  ClusterWs w;
+  w.slot1 = static_cast<uint64_t*>(ws);
+  w.slot2 = w.slot1 + BT * (int64_t)K * 2;
+  w.arrived = reinterpret_cast<unsigned*>(w.slot2 + BT * (int64_t)K);
+  w.ticket = w.arrived + BT;
+  const int64_t nslots = BT * (int64_t)K * 3;
   const int64_t blocks = (nslots + 255) / 256;
   hipLaunchKernelGGL(cluster_ws_init_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
-                     slot1, nslots, arrived, nzeros);
-  const int64_t tiles = a.BT * (int64_t)c.K;
-  hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups>), dim3((unsigned)tiles), dim3(kClThreads), 0, st,
+                     w.slot1, nslots, w.arrived, BT + 1);
+  return w;
+}
+
+hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
+  (void)hipGetLastError();
+  const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
+  const auto* zs = static_cast<const uint16_t*>(a.student);
+  const auto* us = static_cast<const uint16_t*>(a.teacher);
+  const unsigned tiles = (unsigned)(a.BT * (int64_t)c.K);
+  if (kFwdKeepExp) {
+    hipLaunchKernelGGL((cluster_exp_kernel<kFwdExpThreads, kFwdExpGroups, kFwdExpWavesPerSimd, false>), dim3(tiles),
+                       dim3(kFwdExpThreads), 0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
+                       a.tvd, a.lse_s, a.lse_t, a.sigma, nullptr, 0.f, 0.f, nullptr, w.slot1, w.slot2, w.arrived,
+                       w.ticket);
+  } else {
+    hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd>), dim3(tiles), dim3(kClThreads),
+                       0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t,
+                       a.sigma, w.slot1, w.slot2, w.arrived, w.ticket);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
+  (void)hipGetLastError();
+  const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
+  hipLaunchKernelGGL((cluster_exp_kernel<kFusedThreads, kFusedGroups, kFusedWavesPerSimd, true>),
+                     dim3((unsigned)(a.BT * (int64_t)c.K)), dim3(kFusedThreads), 0, st,
                      static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher), a.target,
-                     (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, slot1, slot2,
-                     arrived, ticket);
+                     (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
+                     static_cast<uint16_t*>(g.grad), g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.arrived,
+                     w.ticket);
   return hipGetLastError();
 }
 

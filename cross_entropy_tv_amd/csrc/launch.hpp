@@ -26,6 +26,8 @@ struct ClusterPlan {
 };
 
 ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher);
+// Plan of the fused forward + backward kernel (same conditions, its own chunk size).
+ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher);
 
 struct FwdPlan {
   int split;
@@ -59,6 +61,14 @@ struct BwdArgs {
 
 hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream);
 hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t stream);
+
+// Gradient arguments of the fused forward + backward.
+struct FusedGrad {
+  void* grad;
+  float g_ce, g_tvd;
+  const float* g_scale;
+};
+hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
                               int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,

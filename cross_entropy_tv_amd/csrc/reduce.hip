@@ -1,6 +1,8 @@
 // Mean of the per-row losses over the rows whose target is not the ignore
 // index (a mean-reduced loss, the usual reduction for token-level CE), plus
-// 1 / n_valid, the factor such a loss hands to the backward.
+// 1 / n_valid, the factor such a loss hands to the backward.  With no losses
+// given (ce == NULL) the kernel only counts the valid rows, which is all a
+// fused forward + backward needs before it runs.
 //
 // One workgroup; each lane sums a strided subset of rows in float64, then a
 // fixed-shape tree in LDS combines the lanes: the result does not depend on
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_mean_kernel(
   long long n = 0;
   for (int64_t i = tid; i < BT; i += kRedThreads) {
     if (target[i] != ignore_index) {
-      a += (double)ce[i];
+      if (ce) a += (double)ce[i];
       if (tvd) b += (double)tvd[i];
       ++n;
     }
@@ -44,7 +46,9 @@ __global__ __launch_bounds__(kRedThreads) void reduce_mean_kernel(
   if (tid == 0) {
     const long long nv = sn[0];
     const double dn = (double)nv;
-    if (nv > 0) {
+    if (!mean_out) {
+      // counting only (no losses given)
+    } else if (nv > 0) {
       mean_out[0] = (float)(sc[0] / dn);
       if (tvd) mean_out[1] = (float)(st[0] / dn);
     } else {  // 0 / 0: NaN, written as bits

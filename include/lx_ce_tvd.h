@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 1
+#define LX_CE_TVD_ABI_VERSION 2
 
 typedef enum lx_status {
   LX_OK = 0,
@@ -141,6 +141,57 @@ lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teache
                              const float* lse_s, const float* lse_t, const float* sigma,
                              float g_ce, float g_tvd, const float* g_scale,
                              lx_dtype dt, void* stream);
+
+/*
+ * Bytes of device workspace lx_ce_tvd_forward_backward needs for this shape
+ * (0 when the shape runs without workspace); otherwise as
+ * lx_ce_tvd_workspace_bytes.
+ */
+size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher);
+
+/*
+ * Forward and backward in one call, for a loss whose upstream gradients are
+ * known before the forward runs (the loss is the last node of the graph, and a
+ * mean over valid rows needs only their count, see lx_ce_tvd_count_valid).
+ * Computes exactly what lx_ce_tvd_forward followed by lx_ce_tvd_backward
+ * computes, combining the "Forward Pass" and "Backward Pass" sections of the
+ * PR #1384 analysis page into one pass over the logits where the shape allows:
+ * for bf16 logits with a teacher, V % 8 == 0 and student, teacher and grad
+ * 16-byte aligned, each row is read from HBM once and its gradient written
+ * once; any other shape runs the two passes back to back on `stream`.
+ *
+ * Inputs : as lx_ce_tvd_forward, plus g_ce, g_tvd and g_scale as
+ *          lx_ce_tvd_backward (g_scale: optional device float, e.g. the
+ *          inv_n_valid written by lx_ce_tvd_count_valid on the same stream).
+ * Outputs: ce, tvd, lse_s, lse_t, sigma as lx_ce_tvd_forward; grad (BT, V) dt
+ *          as lx_ce_tvd_backward.  grad may EQUAL student (in place: every
+ *          logit of a row is read before any gradient of that row is stored);
+ *          any other overlap with an input, an output or the workspace is
+ *          LX_ERR_ALIAS.  The forward outputs are bit-identical to those of
+ *          lx_ce_tvd_forward only when both take the same path; both meet the
+ *          same tolerances against the definition.
+ * Workspace: at least lx_ce_tvd_forward_backward_workspace_bytes(...) bytes,
+ *          256-byte aligned, contents ignored and clobbered.
+ * Errors : as lx_ce_tvd_forward and lx_ce_tvd_backward.
+ */
+lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, const int64_t* target,
+                                     int64_t BT, int64_t V, int64_t ignore_index,
+                                     float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                                     void* grad, float g_ce, float g_tvd, const float* g_scale,
+                                     lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Count of the rows whose target is not ignore_index, the only quantity a
+ * mean-reduced loss needs before its backward.
+ *
+ * Inputs : target int64[BT] (may be NULL when BT == 0).
+ * Outputs: n_valid int64[1] or NULL; inv_n_valid float[1] or NULL, = 1 / n_valid
+ *          (0 when n_valid == 0); at least one of them must be given.
+ * Errors : LX_ERR_INVALID_ARG (BT < 0, no output, misaligned pointer),
+ *          LX_ERR_ALIAS (outputs overlapping target or each other), LX_ERR_HIP.
+ */
+lx_status lx_ce_tvd_count_valid(const int64_t* target, int64_t BT, int64_t ignore_index,
+                                int64_t* n_valid, float* inv_n_valid, void* stream);
 
 /*
  * Mean reduction over the rows whose target is not ignore_index.

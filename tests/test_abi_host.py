@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 1
+    assert lx.lx_abi_version() == 2
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
                        (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP")):
         assert lx.lx_status_string(code) == name
@@ -71,10 +71,14 @@ def test_forward_validation():
     assert need > 0 and lx.lx_ce_tvd_workspace_bytes(4, 100000, 1, 0) < need
     assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 0) == 0   # CE-only: one stream, no exchange
     assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 0, 1) == 0   # f32 rows: one workgroup per row
-    # bf16 with a teacher: the read-once path exchanges per-row partials of its K = 4
+    # bf16 with a teacher: the read-once path exchanges per-row partials of its K >= 2
     # member workgroups (3 64-bit slots per member) and keeps a counter per row + a ticket
-    slots, counters = 8192 * 4 * 3 * 8, (8192 + 1) * 4
-    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1) == (slots + counters + 255) // 256 * 256
+    ws = lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1)
+    counters = (8192 + 1) * 4
+    assert ws % 256 == 0 and any(ws == (8192 * k * 24 + counters + 255) // 256 * 256 for k in range(2, 33))
+    wf = lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 1)
+    assert wf >= ws and any(wf == (8192 * k * 24 + counters + 255) // 256 * 256 for k in range(2, 33))
+    assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 0) == 0
     assert fwd(V=100000, teacher=A * 2) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6, wsb=need - 4) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6 + 16, wsb=need) == lx.LX_ERR_WORKSPACE  # 256-B alignment
@@ -93,6 +97,43 @@ def test_backward_validation():
     assert bwd(grad=A + (1 << 31) - 100) == lx.LX_ERR_ALIAS       # overlaps teacher
     assert bwd(grad=A * 4 + 100) == lx.LX_ERR_ALIAS               # overlaps lse / sigma
     assert bwd(grad=A * 5, g_scale=A * 5 + 12) == lx.LX_ERR_ALIAS
+
+
+def fwdbwd(student=A, teacher=A + (1 << 31), target=A * 3, BT=4, V=100, ce=A * 4, tvd=A * 4 + 64,
+           lse_s=A * 4 + 128, lse_t=A * 4 + 192, sigma=A * 4 + 256, grad=A * 5, g_scale=None, dt=1, ws=None,
+           wsb=0):
+    return L.lx_ce_tvd_forward_backward(student, teacher, target, BT, V, -100, ce, tvd, lse_s, lse_t, sigma, grad,
+                                        1.0, 1.0, g_scale, dt, ws, wsb, None)
+
+
+def test_forward_backward_validation():
+    assert fwdbwd(BT=0) == lx.LX_OK
+    assert fwdbwd(dt=5) == lx.LX_ERR_UNSUPPORTED_DTYPE
+    assert fwdbwd(grad=None) == lx.LX_ERR_INVALID_ARG
+    assert fwdbwd(sigma=None) == lx.LX_ERR_INVALID_ARG
+    assert fwdbwd(grad=A + 1) == lx.LX_ERR_INVALID_ARG                 # not element aligned
+    assert fwdbwd(g_scale=A * 6 + 2) == lx.LX_ERR_INVALID_ARG
+    assert fwdbwd(grad=A + 2) == lx.LX_ERR_ALIAS                       # partial overlap with student
+    assert fwdbwd(grad=A + (1 << 31)) == lx.LX_ERR_ALIAS               # the teacher
+    assert fwdbwd(grad=A * 4 + 100) == lx.LX_ERR_ALIAS                 # the forward outputs
+    assert fwdbwd(ce=A * 5 + 8) == lx.LX_ERR_ALIAS                     # an output inside the gradient
+    assert fwdbwd(g_scale=A * 4 + 64) == lx.LX_ERR_ALIAS               # g_scale inside an output
+    need = lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 1)
+    big = dict(BT=8192, V=151936, teacher=A * 8, target=A * 3, ce=A * 4, tvd=A * 4 + (1 << 16),
+               lse_s=A * 4 + (2 << 16), lse_t=A * 4 + (3 << 16), sigma=A * 4 + (4 << 16), grad=A * 12)
+    assert fwdbwd(**big) == lx.LX_ERR_WORKSPACE
+    assert fwdbwd(**big, ws=A * 16, wsb=need - 256) == lx.LX_ERR_WORKSPACE
+    assert fwdbwd(**big, ws=A * 16 + 64, wsb=need) == lx.LX_ERR_WORKSPACE   # 256-B alignment
+    assert fwdbwd(**big, ws=A * 12, wsb=need) == lx.LX_ERR_ALIAS          # workspace inside the gradient
+
+
+def test_count_valid_validation():
+    c = L.lx_ce_tvd_count_valid
+    assert c(A, -1, -100, A * 2, None, None) == lx.LX_ERR_INVALID_ARG
+    assert c(A, 4, -100, None, None, None) == lx.LX_ERR_INVALID_ARG       # no output
+    assert c(A + 4, 4, -100, A * 2, None, None) == lx.LX_ERR_INVALID_ARG  # target alignment
+    assert c(A, 4, -100, A + 8, None, None) == lx.LX_ERR_ALIAS            # n_valid inside target
+    assert c(A, 4, -100, A * 2, A * 2 + 4, None) == lx.LX_ERR_ALIAS       # outputs overlap
 
 
 def test_reduce_validation():

@@ -1,0 +1,232 @@
+"""Parity of the fused forward + backward entry point (and the valid-row count it
+relies on) with the float64 oracle, on the GPU, through the C ABI.
+
+Shapes that take the one-pass kernel (bf16 with a teacher, V % 8 == 0,
+16-byte aligned) are compared element by element on small cases that span
+several member chunks, ragged last members and the special rows; the other
+shapes run the forward and the backward back to back and are checked the same
+way.  Full-size workloads run in the configuration the benchmark times and
+compare sampled rows with the oracle, plus properties on every row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _parity import DEV, announce, bits32, check_forward, check_grad, grad_bits, grad_to_host, tie_info, to_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import cross_entropy_tv_amd as lx  # noqa: E402
+
+II = W.IGNORE_INDEX
+SENTINEL = 12345.0
+
+
+def outputs(BT, teacher=True):
+    keys = ("ce", "tvd", "lse_s", "lse_t", "sigma") if teacher else ("ce", "lse_s")
+    return {k: torch.full((BT,), SENTINEL, dtype=torch.float32, device=DEV) for k in keys}
+
+
+def run_fused(zs, us, tg, g_ce, g_tvd, grad=None, g_scale=None, ii=II):
+    out = outputs(zs.shape[0], us is not None)
+    if grad is None:
+        grad = torch.full_like(zs, SENTINEL)
+    lx.lx_ce_tvd_forward_backward(zs, us, tg, ii, out["ce"], out.get("tvd"), out["lse_s"], out.get("lse_t"),
+                                  out.get("sigma"), grad, g_ce, g_tvd, g_scale)
+    return out, grad
+
+
+def host(out):
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def one_pass(BT, V, dtype="bf16", teacher=True):
+    """True when the shape takes the one-pass kernel (it needs a workspace)."""
+    dt = lx.LX_BF16 if dtype == "bf16" else lx.LX_F32
+    return teacher and dtype == "bf16" and V % 8 == 0 and \
+        lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, True) > 0 and V // 8 >= 256
+
+
+def fused_case(label, z, u, t, g_ce=0.5, g_tvd=1.5, in_place=False):
+    announce(f"fused {label}: shape {z.shape} dtype {z.dtype} teacher {u is not None} in_place {in_place}")
+    zs, tg = to_dev(z), to_dev(t)
+    us = None if u is None else to_dev(u)
+    out, g = run_fused(zs, us, tg, g_ce, g_tvd, grad=zs if in_place else None)
+    o = host(out)
+    check_forward(o, z, u, t, II, label)
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, g_ce, g_tvd, label)
+    return o, g
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
+@pytest.mark.parametrize("BT,V", [(520, 8200), (600, 20000), (3, 65536), (40, 151936)],
+                         ids=["520x8200", "600x20000", "3x65536", "40x151936"])
+def test_one_pass_shapes(BT, V, in_place):
+    """One-pass kernel: ragged last member, ignored / identical / uniform rows and rows
+    whose logits span more than a thread's exponent range (the overflow reload)."""
+    assert one_pass(BT, V)
+    ign = [0, BT - 1] if BT > 4 else [1]
+    ident = [2] if BT > 4 else []
+    unif = [3] if BT > 4 else []
+    z, u, t = W.custom(BT, V, "bf16", seed=BT * 3 + V, scale=3.0, teacher_noise=0.5, ignore_rows=ign,
+                       identical_rows=ident, uniform_rows=unif)
+    if BT > 8:
+        hi = W.bf16_bits_rne(np.array([150.0, 120.0], dtype=np.float32))
+        z[5, V // 3] = hi[0]
+        u[6, V - 5] = hi[1]
+        z[8, 1], u[8, 2] = hi[0], hi[1]
+    o, _ = fused_case(f"one-pass {BT}x{V}", z, u, t, in_place=in_place)
+    if ident:
+        assert o["tvd"][2] == 0.0 and o["sigma"][2] == 0.0
+    if unif:
+        assert abs(o["ce"][3] - math.log(V)) <= 1e-4
+
+
+@pytest.mark.parametrize("BT,V,dtype,teacher", [(520, 4099, "bf16", True), (520, 3000, "f32", True),
+                                                (6, 50001, "bf16", True), (520, 8200, "bf16", False),
+                                                (7, 1024, "f32", False)],
+                         ids=["bf16_V_not_8", "f32", "split_bf16", "ce_only", "tiny_f32_ce_only"])
+def test_two_pass_fallback_shapes(BT, V, dtype, teacher):
+    assert not one_pass(BT, V, dtype, teacher)
+    ign = [1, BT - 1] if BT > 4 else [1]
+    z, u, t = W.custom(BT, V, dtype, seed=BT + 5 * V, scale=3.0, teacher_noise=0.5, ignore_rows=ign)
+    fused_case(f"fallback {BT}x{V} {dtype}", z, u if teacher else None, t, g_ce=0.75, g_tvd=-0.5)
+
+
+def test_unaligned_gradient_takes_the_two_pass_path():
+    z, u, t = W.custom(520, 8200, "bf16", seed=3, scale=2.0, teacher_noise=0.5, ignore_rows=[4])
+    announce("fused with a gradient 2 bytes off a 16-byte boundary")
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    base = torch.zeros(520 * 8200 + 16, dtype=torch.bfloat16, device=DEV)
+    g = base[1:1 + 520 * 8200].view(520, 8200)
+    out, g = run_fused(zs, us, tg, 0.5, 1.5, grad=g)
+    check_forward(host(out), z, u, t, II, "unaligned grad")
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, "unaligned grad")
+
+
+def test_identical_rows_give_exactly_zero_total_variation():
+    z, _, t = W.custom(530, 16384, "bf16", seed=21, scale=3.0, ignore_rows=[7])
+    announce("fused, teacher == student: tvd, sigma and the tvd gradient exactly 0")
+    zs, tg = to_dev(z), to_dev(t)
+    out, g = run_fused(zs, zs.clone(), tg, 0.0, 1.0)
+    o = host(out)
+    assert np.all(o["tvd"] == 0.0) and np.all(o["sigma"] == 0.0)
+    assert torch.count_nonzero(g.view(torch.int16)) == 0
+
+
+def test_out_of_range_target_poisons_its_row_only():
+    z, u, t = W.custom(520, 8200, "bf16", seed=8, scale=2.0, teacher_noise=0.5)
+    t[5], t[9] = 8200, -3
+    announce("fused, targets out of range on rows 5 and 9")
+    out, g = run_fused(to_dev(z), to_dev(u), to_dev(t), 0.5, 0.5)
+    o = host(out)
+    assert np.isnan(o["ce"][5]) and np.isnan(o["ce"][9])
+    gf = g.float()
+    assert bool(torch.isnan(gf[5]).all()) and bool(torch.isnan(gf[9]).all())
+    ok = np.ones(520, bool)
+    ok[[5, 9]] = False
+    assert np.all(np.isfinite(o["ce"][ok])) and bool(torch.isfinite(gf[torch.from_numpy(ok).to(DEV)]).all())
+    for k in ("tvd", "lse_s", "lse_t", "sigma"):
+        assert np.all(np.isfinite(o[k])), k
+
+
+def test_deterministic_and_close_to_the_two_pass_result():
+    z, u, t = W.custom(600, 20000, "bf16", seed=44, scale=2.5, teacher_noise=0.5, ignore_rows=[3])
+    announce("fused: 3 repeats bitwise; vs forward + backward within the tolerances")
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    runs = []
+    for _ in range(3):
+        out, g = run_fused(zs, us, tg, 0.5, 1.5)
+        runs.append((host(out), g.view(torch.int16).cpu()))
+    for o, gb in runs[1:]:
+        for k in o:
+            assert np.array_equal(bits32(o[k]), bits32(runs[0][0][k])), k
+        assert torch.equal(gb, runs[0][1])
+    sep = outputs(600)
+    lx.lx_ce_tvd_forward(zs, us, tg, II, sep["ce"], sep["tvd"], sep["lse_s"], sep["lse_t"], sep["sigma"])
+    g2 = torch.empty_like(zs)
+    lx.lx_ce_tvd_backward(g2, zs, us, tg, II, sep["lse_s"], sep["lse_t"], sep["sigma"], 0.5, 1.5)
+    s = host(sep)
+    for k, tol in (("ce", 2e-4), ("lse_s", 2e-4), ("lse_t", 2e-4), ("tvd", 2e-5), ("sigma", 2e-5)):
+        assert np.max(np.abs(s[k] - runs[0][0][k])) <= tol, k
+    # gradients: both passes round once to bf16; elements at a near tie of p and q may
+    # take different sign branches in the two kernels (each is exempt against the
+    # oracle), which moves them by up to |g_tvd| * p
+    g1 = runs[0][1].view(torch.bfloat16).float().numpy().astype(np.float64)
+    d = np.abs(g2.float().cpu().numpy() - g1)
+    valid = t != II
+    p, mask, slack = tie_info(z, u, valid)
+    tol = 2.0 ** -7 * np.abs(g1) + 2e-6
+    tol[valid] += 1.5 * p * (1 + 2.0 ** -7) * (mask + slack[:, None])
+    assert np.all(d <= tol), f"{np.sum(d > tol)} gradient elements differ"
+
+
+def test_count_valid():
+    t = np.full(1000, II, dtype=np.int64)
+    t[::3] = 5
+    tg = to_dev(t)
+    n = torch.zeros(1, dtype=torch.int64, device=DEV)
+    inv = torch.zeros(1, dtype=torch.float32, device=DEV)
+    lx.lx_ce_tvd_count_valid(tg, II, n, inv)
+    assert int(n.item()) == 334 and inv.item() == np.float32(1.0 / 334)
+    lx.lx_ce_tvd_count_valid(torch.full((10,), II, dtype=torch.int64, device=DEV), II, n, inv)
+    assert int(n.item()) == 0 and inv.item() == 0.0
+
+
+def _sample_rows(w, n=40):
+    rng = np.random.default_rng(4321)
+    rows = set(rng.choice(w.BT, size=min(n, w.BT), replace=False).tolist()) | {0, w.BT - 1}
+    ro = W.roles(w)
+    for role in (W.ROLE_IGNORED, W.ROLE_IDENTICAL, W.ROLE_UNIFORM):
+        rows |= set(np.nonzero(ro == role)[0][:4].tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["train", "pr", "ties", "hugev"])
+def test_full_workload_fused(name):
+    """As benchmarked: count the valid rows, then one fused pass with g_scale = 1/n_valid
+    (in place for the pr workload)."""
+    w = W.get(name)
+    announce(f"fused workload {name} {w.BT}x{w.V}: generating inputs")
+    z, u, t = W.full(w)
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    del z, u
+    inv = torch.zeros(1, dtype=torch.float32, device=DEV)
+    lx.lx_ce_tvd_count_valid(tg, II, None, inv)
+    in_place = name == "pr"
+    rows = _sample_rows(w)
+    zr, ur = W.rows(w, rows)  # before an in-place pass overwrites the logits
+    vmax = zs.float().amax(1).cpu().numpy()
+    announce(f"fused workload {name}: one pass (in place: {in_place})")
+    out, grad = run_fused(zs, us, tg, 1.0, 1.0, grad=zs if in_place else torch.empty_like(zs), g_scale=inv)
+    o = host(out)
+    valid = t != II
+    n_valid = int(valid.sum())
+    ro = W.roles(w)
+    assert np.all(bits32(o["ce"][~valid]) == 0) and np.all(o["ce"][valid] >= -1e-5)
+    assert np.all(o["lse_s"][valid] >= vmax[valid] - 1e-4)
+    assert np.all(o["lse_s"][valid] <= vmax[valid] + math.log(w.V) + 1e-4)
+    assert np.all((o["tvd"] >= 0) & (o["tvd"] <= 1 + 1e-6)) and np.all(np.abs(o["sigma"]) <= 1 + 1e-5)
+    ident = ro == W.ROLE_IDENTICAL
+    assert np.all(o["tvd"][ident] == 0.0) and np.all(o["sigma"][ident] == 0.0)
+    assert np.all(np.abs(o["ce"][ro == W.ROLE_UNIFORM] - math.log(w.V)) <= 1e-4)
+    gs = grad.float()
+    rs, ra = gs.sum(1).abs().cpu().numpy(), gs.abs().sum(1).cpu().numpy()
+    del gs
+    assert np.all(rs <= 2.0 ** -8 * ra + w.V * 1e-6 / n_valid + 1e-9)
+    if (~valid).any():
+        assert np.all(grad_bits(grad[torch.from_numpy(np.nonzero(~valid)[0]).to(DEV)]) == 0)
+    sel = torch.from_numpy(rows).to(DEV)
+    gb, gh = grad_bits(grad[sel]), grad_to_host(grad[sel])
+    announce(f"fused workload {name}: oracle on {len(rows)} sampled rows")
+    check_forward({k: v[rows] for k, v in o.items()}, zr, ur, t[rows], II, f"fused {name}")
+    check_grad(gh, gb, zr, ur, t[rows], II, 1.0 / n_valid, 1.0 / n_valid, f"fused {name}")
