@@ -107,7 +107,7 @@ def run_mode(w, zs, us, tg, n_valid, steps, warmup, teacher):
     return res
 
 
-def run_fused(w, zs, us, tg, n_valid, steps, warmup):
+def run_fused(w, zs, us, tg, n_valid, steps, warmup, teacher=True):
     """One step = count the valid rows (1/n_valid on the device) -> one fused forward +
     backward pass -> mean of the per-row losses."""
     import torch
@@ -116,12 +116,14 @@ def run_fused(w, zs, us, tg, n_valid, steps, warmup):
     BT, V = w.BT, w.V
     dev = zs.device
     f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
-    ce, lse_s, tvd, lse_t, sigma = f(), f(), f(), f(), f()
+    ce, lse_s = f(), f()
+    tvd, lse_t, sigma = (f(), f(), f()) if teacher else (None, None, None)
+    u = us if teacher else None
     mean = torch.empty(2, dtype=torch.float32, device=dev)
     inv = torch.empty(1, dtype=torch.float32, device=dev)
     grad = torch.empty_like(zs)
     dt = lx.LX_BF16 if w.dtype == "bf16" else lx.LX_F32
-    nws = lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, True)
+    nws = lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -131,7 +133,7 @@ def run_fused(w, zs, us, tg, n_valid, steps, warmup):
         lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
         if ev is not None:
             ev[1].record(stream)
-        lx.lx_ce_tvd_forward_backward(zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, grad, 1.0, 1.0, inv, ws,
+        lx.lx_ce_tvd_forward_backward(zs, u, tg, -100, ce, tvd, lse_s, lse_t, sigma, grad, 1.0, 1.0, inv, ws,
                                       stream)
         if ev is not None:
             ev[2].record(stream)
@@ -152,7 +154,8 @@ def run_fused(w, zs, us, tg, n_valid, steps, warmup):
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     red_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     n_ign = BT - n_valid
-    alg = n_valid * 3 * V * w.esize + n_ign * V * w.esize + BT * 8 + BT * 4 * 5 + 4
+    streams = 2 if teacher else 1
+    alg = n_valid * (streams + 1) * V * w.esize + n_ign * V * w.esize + BT * 8 + BT * 4 * (5 if teacher else 2) + 4
     return {"ms_per_step": wall * 1e3 / steps, "tokens_per_s": BT * steps / wall, "count_ms": cnt_ms,
             "fused_ms": fb_ms, "reduce_ms": red_ms, "fused_GBs": alg / fb_ms / 1e6,
             "fused_pct_peak": 100.0 * alg / fb_ms / 1e6 / HBM_PEAK_GBS, "alg_bytes": alg,
@@ -285,6 +288,10 @@ def main():
         extra["ce_only"] = {k: ce_res[k] for k in ("tokens_per_s", "ms_per_step", "forward_ms", "backward_ms",
                                                     "forward_GBs", "backward_GBs", "forward_pct_peak",
                                                     "backward_pct_peak")}
+        if not args.no_fused:
+            cf = run_fused(w, zs, us, tg, n_valid, args.steps, args.warmup, teacher=False)
+            extra["ce_only"]["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cf.items()
+                                         if k != "mean"}
     if teacher and not args.no_fused:
         fu = run_fused(w, zs, us, tg, n_valid, args.steps, args.warmup)
         extra["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in fu.items()}

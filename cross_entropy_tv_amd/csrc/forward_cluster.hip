@@ -51,7 +51,6 @@ constexpr unsigned kSpinLimit = 1u << 18;   // polls (each one a device-coherent
 
 constexpr int kRsrcFlags = 0x00020000;      // buffer resource word 3 for gfx9-family raw buffers
 constexpr int kStreamPolicy = 2;            // cache policy of the loads: non-temporal (streamed once)
-
 // Buffer resource covering `bytes` bytes from p: loads past the end return 0
 // without touching memory, so a thread's loads need no branch around them
 // (which would also keep the compiler from waiting on them one at a time).
@@ -329,34 +328,38 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
   }
 }
 
-// ---------------------------------------------------------------- kept-exponential variant
+// ---------------------------------------------------------------- one-pass forward + backward
 //
-// Keeps E = exp(x - m) (fp32, twice the registers of the bf16 logits) instead
-// of the logits, m being the thread's exact maximum over its groups (taken
-// while the chunk is unpacked, so no exponential can overflow), so that step 2
-// forms P = p * 2^126 as E * (exp(m - lse) *
-// 2^126), one multiply per element instead of an exponential.  The 2^126
-// scale makes sign(p - q) a plain med3(P - Q, -1, 1): a nonzero difference of
-// two scaled probabilities is at least 1 in magnitude unless both p and q are
-// below 2^-103.  Products are never contracted into the differences, so
-// bit-identical student and teacher rows give P == Q exactly.
+// For a loss whose upstream gradients are known before it runs, the forward
+// outputs and the student gradient of the "Backward Pass" section,
+// g = p * (alpha + beta * s) - k * g_ce * [v == t], come out of one pass over
+// the logits.  Each member keeps E = exp(x - m) (fp32, twice the registers of
+// the bf16 logits), m being the thread's exact maximum over its groups (taken
+// while the chunk is unpacked, so no exponential can overflow); p is then
+// E * exp(m - lse), one multiply per element instead of an exponential.
 //
-// FUSED additionally writes the student gradient of the "Backward Pass"
-// section, g = p * (alpha + beta * s) - k * g_ce * [v == t], from the kept
-// exponentials: every member waits for the K step-2 pairs (so all members hold
-// the same sigma), then stores its chunk of the gradient.  Each member has
-// read its whole chunk, and member 0 the target logit, before any member
-// stores, so the gradient may overwrite the student logits.
-template <int NT, int G, int WPE, bool FUSED>
+// With a teacher (TEACHER): step 2 forms P = p * 2^126 the same way and sums
+// |P - Q| and P * sign(P - Q); the 2^126 scale makes sign(p - q) a plain
+// med3(P - Q, -1, 1), a nonzero difference of two scaled probabilities being
+// at least 1 in magnitude unless both p and q are below 2^-103.  Products are
+// never contracted into the differences, so bit-identical student and teacher
+// rows give P == Q exactly.  Every member waits for the K step-2 pairs, so all
+// members hold the same sigma, then stores its chunk of the gradient.
+// CE-only (!TEACHER): one exchange (the student lse), then g = k*g_ce*(p - onehot).
+//
+// Each member has read its whole chunk, and member 0 the target logit, before
+// any member stores, so the gradient may overwrite the student logits.
+template <int NT, int G, int WPE, bool TEACHER>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
-                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
-                        float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
-                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
-                        uint16_t* grad, float g_ce, float g_tvd, const float* __restrict__ g_scale,
-                        uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
-                        unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
+void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
+                          const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
+                          float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
+                          float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
+                          uint16_t* grad, float g_ce, float g_tvd, const float* __restrict__ g_scale,
+                          uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
+                          unsigned* __restrict__ ticket) {
   constexpr int W = NT / 64;
+  constexpr int NS = TEACHER ? 2 : 1;  // exchange-1 slots per member
   __shared__ Lse red_z[W], red_u[W];
   __shared__ float red_a[W], red_s[W];
   __shared__ uint64_t got[2 * kClusterMaxK];
@@ -376,15 +379,15 @@ void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ te
   const int ge = min(NG, gb + gpm);
   const int64_t row = r * (int64_t)V;
   const bool t_ok = t >= 0 && t < V;
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
-      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
+      ce[r] = 0.f;
+      lse_s_out[r] = 0.f;
+      if (TEACHER) { tvd[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f; }
     }
-    if (FUSED) {
-      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
 #pragma unroll
-      for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
-    }
+    for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
     return;
   }
   const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
@@ -392,24 +395,25 @@ void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ te
   if (j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
 
   // ---- load the chunk; unpack it into the E registers and take this thread's exact maxima
-  float ez[G][8], eu[G][8];
+  float ez[G][8], eu[TEACHER ? G : 1][8];
   float mz = kMFloor, mu = kMFloor;
   {
     const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
-    const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
-    u32x4_t rz[G], ru[G];
+    u32x4_t rz[G], ru[TEACHER ? G : 1];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
-      ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+    for (int i = 0; i < G; ++i) rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+    if (TEACHER) {
+      const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
+#pragma unroll
+      for (int i = 0; i < G; ++i) ru[TEACHER ? i : 0] = ld_stream(rsu, (tid + i * NT) * 16);
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       unpack8(rz[i], ez[i]);
-      unpack8(ru[i], eu[i]);
+      if (TEACHER) unpack8(ru[TEACHER ? i : 0], eu[TEACHER ? i : 0]);
       if (i < n) {
         mz = fmaxf(mz, max8(ez[i]));
-        mu = fmaxf(mu, max8(eu[i]));
+        if (TEACHER) mu = fmaxf(mu, max8(eu[TEACHER ? i : 0]));
       }
     }
   }
@@ -422,22 +426,25 @@ void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ te
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ez[i][e] = exp2_hw(__builtin_fmaf(ez[i][e], kLog2e, nbz));
-        eu[i][e] = exp2_hw(__builtin_fmaf(eu[i][e], kLog2e, nbu));
+        if (TEACHER) eu[TEACHER ? i : 0][e] = exp2_hw(__builtin_fmaf(eu[TEACHER ? i : 0][e], kLog2e, nbu));
       }
       if (i < n) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           sz0 += ez[i][e];
           sz1 += ez[i][e + 1];
-          su0 += eu[i][e];
-          su1 += eu[i][e + 1];
+          if (TEACHER) {
+            su0 += eu[TEACHER ? i : 0][e];
+            su1 += eu[TEACHER ? i : 0][e + 1];
+          }
         }
       }
     }
   }
   {
     Lse pz = wave_lse(Lse{mz, sz0 + sz1});
-    Lse pu = wave_lse(Lse{mu, su0 + su1});
+    Lse pu{0.f, 0.f};
+    if (TEACHER) pu = wave_lse(Lse{mu, su0 + su1});
     if ((tid & 63) == 0) {
       red_z[tid >> 6] = pz;
       red_u[tid >> 6] = pu;
@@ -447,96 +454,68 @@ void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ te
     if (tid == 0) s_zt = zt;
   }
   __syncthreads();
-  uint64_t* s1 = slot1 + r * (int64_t)K * 2;
+  uint64_t* s1 = slot1 + r * (int64_t)K * NS;
   if (tid == 0) {
     Lse fz = red_z[0], fu = red_u[0];
 #pragma unroll
     for (int w = 1; w < W; ++w) {
       lse_merge(fz, red_z[w]);
-      lse_merge(fu, red_u[w]);
+      if (TEACHER) lse_merge(fu, red_u[w]);
     }
-    publish(s1 + 2 * j, pack2(fz.m, fz.s));
-    publish(s1 + 2 * j + 1, pack2(fu.m, fu.s));
+    publish(s1 + NS * j, pack2(fz.m, fz.s));
+    if (TEACHER) publish(s1 + NS * j + 1, pack2(fu.m, fu.s));
   }
 
   // ---- exchange 1: the row's K (max, sum-exp) pairs, merged in member order
-  if (tid < 64) wait_slots(s1, 2 * K, got);
+  if (tid < 64) wait_slots(s1, NS * K, got);
   __syncthreads();
   if (tid == 0) {
-    Lse fz{lo_f(got[0]), hi_f(got[0])}, fu{lo_f(got[1]), hi_f(got[1])};
-    for (int k = 1; k < K; ++k) {
-      lse_merge(fz, Lse{lo_f(got[2 * k]), hi_f(got[2 * k])});
-      lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
-    }
+    Lse fz{lo_f(got[0]), hi_f(got[0])};
+    for (int k = 1; k < K; ++k) lse_merge(fz, Lse{lo_f(got[NS * k]), hi_f(got[NS * k])});
     s_bc[0] = lse_value(fz);
-    s_bc[1] = lse_value(fu);
+    if (TEACHER) {
+      Lse fu{lo_f(got[1]), hi_f(got[1])};
+      for (int k = 1; k < K; ++k) lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
+      s_bc[1] = lse_value(fu);
+    }
   }
   __syncthreads();
-  const float lse_s = s_bc[0], lse_t = s_bc[1];
-
-  // ---- step 2: P = E * (exp(m - lse) * 2^126), sum |P - Q| and P * sign(P - Q)
+  const float lse_s = s_bc[0];
+  const float lse_t = TEACHER ? s_bc[1] : 0.f;
   const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(lse_s)));
-  const float cu = exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t)));
-  {
-    const float czs = cz * 0x1p126f, cus = cu * 0x1p126f;
-    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+  const float cu = TEACHER ? exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t))) : 0.f;
+
+  float sigma = 0.f;
+  if (TEACHER) {
+    // ---- step 2: P = E * (exp(m - lse) * 2^126), sum |P - Q| and P * sign(P - Q)
+    {
+      const float czs = cz * 0x1p126f, cus = cu * 0x1p126f;
+      float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      if (i < n) {
+      for (int i = 0; i < G; ++i) {
+        if (i < n) {
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float P0 = ez[i][e] * czs, Q0 = eu[i][e] * cus;
-          const float P1 = ez[i][e + 1] * czs, Q1 = eu[i][e + 1] * cus;
-          const float D0 = P0 - Q0, D1 = P1 - Q1;
-          A0 += fabsf(D0);
-          A1 += fabsf(D1);
-          S0 = __builtin_fmaf(P0, __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f), S0);
-          S1 = __builtin_fmaf(P1, __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f), S1);
+          for (int e = 0; e < 8; e += 2) {
+            const float P0 = ez[i][e] * czs, Q0 = eu[TEACHER ? i : 0][e] * cus;
+            const float P1 = ez[i][e + 1] * czs, Q1 = eu[TEACHER ? i : 0][e + 1] * cus;
+            const float D0 = P0 - Q0, D1 = P1 - Q1;
+            A0 += fabsf(D0);
+            A1 += fabsf(D1);
+            S0 = __builtin_fmaf(P0, __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f), S0);
+            S1 = __builtin_fmaf(P1, __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f), S1);
+          }
         }
       }
-    }
-    const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
-    if ((tid & 63) == 0) {
-      red_a[tid >> 6] = A;
-      red_s[tid >> 6] = S;
-    }
-  }
-  __syncthreads();
-  uint64_t* s2 = slot2 + r * (int64_t)K;
-  if (!FUSED) {
-    // ---- exchange 2: the last member to arrive adds the K pairs in member order
-    if (tid >= 64) return;
-    unsigned old = 0;
-    if (tid == 0) {
-      float A = red_a[0], S = red_s[0];
-#pragma unroll
-      for (int w = 1; w < W; ++w) {
-        A += red_a[w];
-        S += red_s[w];
+      const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
+      if ((tid & 63) == 0) {
+        red_a[tid >> 6] = A;
+        red_s[tid >> 6] = S;
       }
-      publish(s2 + j, pack2(A, S));
-      old = __hip_atomic_fetch_add(arrived + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    old = __shfl(old, 0, 64);
-    if (old != (unsigned)(K - 1)) return;
-    if (tid == 0 && t_ok) zt = load1(student + row + t);
-    wait_slots(s2, K, got);
-    if (tid == 0) {
-      float A = lo_f(got[0]), S = hi_f(got[0]);
-      for (int k = 1; k < K; ++k) {
-        A += lo_f(got[k]);
-        S += hi_f(got[k]);
-      }
-      if (t_ok) ce[r] = lse_s - zt; else store_nan(ce + r);
-      tvd[r] = 0.5f * A * 0x1p-126f;
-      lse_s_out[r] = lse_s;
-      lse_t_out[r] = lse_t;
-      sigma_out[r] = S * 0x1p-126f;
-    }
-    return;
-  } else {
+    __syncthreads();
     // ---- exchange 2: every member sums the K pairs in member order (identical sigma)
+    uint64_t* s2 = slot2 + r * (int64_t)K;
     if (tid == 0) {
       float A = red_a[0], S = red_s[0];
 #pragma unroll
@@ -556,49 +535,57 @@ void cluster_exp_kernel(const uint16_t* student, const uint16_t* __restrict__ te
       }
       s_bc[2] = 0.5f * A * 0x1p-126f;
       s_bc[3] = S * 0x1p-126f;
-      if (j == 0) {
-        if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
-        tvd[r] = s_bc[2];
-        lse_s_out[r] = lse_s;
-        lse_t_out[r] = lse_t;
-        sigma_out[r] = s_bc[3];
-      }
     }
     __syncthreads();
-    // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
-    const float k = g_scale ? *g_scale : 1.0f;
-    const float kce = k * g_ce;
-    const float beta = 0.5f * k * g_tvd;
-    const float alpha = kce - beta * s_bc[3];
-    const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
-    const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
+    sigma = s_bc[3];
+  }
+  if (j == 0 && tid == 0) {
+    if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
+    lse_s_out[r] = lse_s;
+    if (TEACHER) {
+      tvd[r] = s_bc[2];
+      lse_t_out[r] = lse_t;
+      sigma_out[r] = sigma;
+    }
+  }
+
+  // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
+  const float k = g_scale ? *g_scale : 1.0f;
+  const float kce = k * g_ce;
+  const float beta = TEACHER ? 0.5f * k * g_tvd : 0.f;
+  const float alpha = kce - beta * sigma;
+  const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int g = tid + i * NT;
-      float o[8];
-      {
+  for (int i = 0; i < G; ++i) {
+    const int g = tid + i * NT;
+    float o[8];
+    {
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = ez[i][e] * cz, q = eu[i][e] * cu;
+      for (int e = 0; e < 8; ++e) {
+        const float p = ez[i][e] * cz;
+        if (TEACHER) {
+          const float q = eu[TEACHER ? i : 0][e] * cu;
           o[e] = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+        } else {
+          o[e] = p * alpha;
         }
       }
-      const int rel = trel - 8 * g;
-      if ((unsigned)rel < 8u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
-      }
-      u32x4_t w;
-      if (t_ok) {
-        w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
-        w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
-      } else {
-        const unsigned h = kQNaN16 | (kQNaN16 << 16);
-        w = (u32x4_t){h, h, h, h};
-      }
-      st_stream(rsg, g * 16, w);
     }
+    const int rel = trel - 8 * g;
+    if ((unsigned)rel < 8u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+    }
+    u32x4_t w;
+    if (t_ok) {
+      w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
+      w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
+    } else {
+      const unsigned h = kQNaN16 | (kQNaN16 << 16);
+      w = (u32x4_t){h, h, h, h};
+    }
+    st_stream(rsg, g * 16, w);
   }
 }
 
@@ -620,24 +607,21 @@ __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restri
 constexpr int kClThreads = 256;
 constexpr int kClGroups = 16;
 constexpr int kClWavesPerSimd = 3;
-// The forward keeps logits (false) or exponentials (true, cluster_exp_kernel).
-// Keeping exponentials halves the elements a thread holds, so more members
-// share a row, and measured slower (1.20 ms at 256 x 8 x 3).
-constexpr bool kFwdKeepExp = false;
-constexpr int kFwdExpThreads = 256;
-constexpr int kFwdExpGroups = 8;
-constexpr int kFwdExpWavesPerSimd = 3;
-// Fused forward + backward kernel (keeps exponentials; step 3 then needs no
-// exponential).  Measured: 256 x 8 x 3 (K = 10) 1.72 ms, 256 x 6 x 4 1.79 ms,
-// 256 x 12 x 2 1.82 ms, 512 x 4 x 4 2.04 ms, 128 x 8 x 3 2.02 ms.
+// One-pass forward + backward kernel (keeps exponentials; step 3 then needs no
+// exponential).  With a teacher, measured on the training batch: 256 x 8 x 3
+// (K = 10) 1.72 ms, 256 x 6 x 4 1.79 ms, 256 x 12 x 2 1.82 ms, 512 x 4 x 4
+// 2.04 ms, 128 x 8 x 3 2.02 ms; a persistent variant streaming the next chunk
+// into LDS during the exchanges (two workgroups per compute unit) 2.10 ms.
+// CE-only keeps one tensor, so twice the groups fit.
 constexpr int kFusedThreads = 256;
 constexpr int kFusedGroups = 8;
 constexpr int kFusedWavesPerSimd = 3;
+constexpr int kFusedCeGroups = 16;
 constexpr int64_t kClTargetTiles = 2048;  // enough workgroups to fill 256 compute units several times
 
-static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, bool teacher, int nt, int groups) {
+static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups) {
   ClusterPlan c{0, 0, 0};
-  if (!teacher || esize != 2 || V % 8 != 0 || BT <= 0) return c;
+  if (esize != 2 || V % 8 != 0 || BT <= 0) return c;
   const int64_t NG = V / 8;
   if (NG < nt) return c;  // short rows: the one-workgroup-per-row path is as good
   const int64_t cap = (int64_t)nt * groups;
@@ -659,12 +643,12 @@ static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, bool teacher, int 
 }
 
 ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
-  return kFwdKeepExp ? plan_cfg(BT, V, esize, teacher, kFwdExpThreads, kFwdExpGroups)
-                     : plan_cfg(BT, V, esize, teacher, kClThreads, kClGroups);
+  if (!teacher) return ClusterPlan{0, 0, 0};  // CE-only: one stream, the row path already reads it once
+  return plan_cfg(BT, V, esize, kClThreads, kClGroups);
 }
 
 ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher) {
-  return plan_cfg(BT, V, esize, teacher, kFusedThreads, kFusedGroups);
+  return plan_cfg(BT, V, esize, kFusedThreads, teacher ? kFusedGroups : kFusedCeGroups);
 }
 
 // Workspace: slot1 [BT][K][2] | slot2 [BT][K] (64-bit) | arrived [BT] | ticket (32-bit)
@@ -692,28 +676,29 @@ hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStr
   const auto* zs = static_cast<const uint16_t*>(a.student);
   const auto* us = static_cast<const uint16_t*>(a.teacher);
   const unsigned tiles = (unsigned)(a.BT * (int64_t)c.K);
-  if (kFwdKeepExp) {
-    hipLaunchKernelGGL((cluster_exp_kernel<kFwdExpThreads, kFwdExpGroups, kFwdExpWavesPerSimd, false>), dim3(tiles),
-                       dim3(kFwdExpThreads), 0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
-                       a.tvd, a.lse_s, a.lse_t, a.sigma, nullptr, 0.f, 0.f, nullptr, w.slot1, w.slot2, w.arrived,
-                       w.ticket);
-  } else {
-    hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd>), dim3(tiles), dim3(kClThreads),
-                       0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t,
-                       a.sigma, w.slot1, w.slot2, w.arrived, w.ticket);
-  }
+  hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd>), dim3(tiles), dim3(kClThreads), 0,
+                     st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t,
+                     a.sigma, w.slot1, w.slot2, w.arrived, w.ticket);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
-  hipLaunchKernelGGL((cluster_exp_kernel<kFusedThreads, kFusedGroups, kFusedWavesPerSimd, true>),
-                     dim3((unsigned)(a.BT * (int64_t)c.K)), dim3(kFusedThreads), 0, st,
-                     static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher), a.target,
-                     (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
-                     static_cast<uint16_t*>(g.grad), g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.arrived,
-                     w.ticket);
+  const dim3 grid((unsigned)(a.BT * (int64_t)c.K));
+  const auto* zs = static_cast<const uint16_t*>(a.student);
+  const auto* us = static_cast<const uint16_t*>(a.teacher);
+  auto* gr = static_cast<uint16_t*>(g.grad);
+  if (a.teacher) {
+    hipLaunchKernelGGL((fused_cluster_kernel<kFusedThreads, kFusedGroups, kFusedWavesPerSimd, true>), grid,
+                       dim3(kFusedThreads), 0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
+                       a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.ticket);
+  } else {
+    hipLaunchKernelGGL((fused_cluster_kernel<kFusedThreads, kFusedCeGroups, kFusedWavesPerSimd, false>), grid,
+                       dim3(kFusedThreads), 0, st, zs, nullptr, a.target, (int)a.V, a.ignore_index, c.K, c.gpm,
+                       a.ce, nullptr, a.lse_s, nullptr, nullptr, gr, g.g_ce, 0.f, g.g_scale, w.slot1, w.slot2,
+                       w.ticket);
+  }
   return hipGetLastError();
 }
 

@@ -156,9 +156,10 @@ size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtyp
  * Computes exactly what lx_ce_tvd_forward followed by lx_ce_tvd_backward
  * computes, combining the "Forward Pass" and "Backward Pass" sections of the
  * PR #1384 analysis page into one pass over the logits where the shape allows:
- * for bf16 logits with a teacher, V % 8 == 0 and student, teacher and grad
- * 16-byte aligned, each row is read from HBM once and its gradient written
- * once; any other shape runs the two passes back to back on `stream`.
+ * for bf16 logits (with or without a teacher), V % 8 == 0, V >= 2048 and
+ * student, teacher and grad 16-byte aligned, each row is read from HBM once and
+ * its gradient written once; any other shape runs the two passes back to back
+ * on `stream`.
  *
  * Inputs : as lx_ce_tvd_forward, plus g_ce, g_tvd and g_scale as
  *          lx_ce_tvd_backward (g_scale: optional device float, e.g. the

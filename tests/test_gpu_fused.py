@@ -50,10 +50,11 @@ def host(out):
 
 
 def one_pass(BT, V, dtype="bf16", teacher=True):
-    """True when the shape takes the one-pass kernel (it needs a workspace)."""
+    """True when the shape takes the one-pass kernel (bf16 rows of at least 2048
+    classes, V % 8 == 0; it needs a workspace)."""
     dt = lx.LX_BF16 if dtype == "bf16" else lx.LX_F32
-    return teacher and dtype == "bf16" and V % 8 == 0 and \
-        lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, True) > 0 and V // 8 >= 256
+    return dtype == "bf16" and V % 8 == 0 and V >= 2048 and \
+        lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher) > 0
 
 
 def fused_case(label, z, u, t, g_ce=0.5, g_tvd=1.5, in_place=False):
@@ -67,13 +68,14 @@ def fused_case(label, z, u, t, g_ce=0.5, g_tvd=1.5, in_place=False):
     return o, g
 
 
+@pytest.mark.parametrize("teacher", [True, False], ids=["ce_tvd", "ce_only"])
 @pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
 @pytest.mark.parametrize("BT,V", [(520, 8200), (600, 20000), (3, 65536), (40, 151936)],
                          ids=["520x8200", "600x20000", "3x65536", "40x151936"])
-def test_one_pass_shapes(BT, V, in_place):
+def test_one_pass_shapes(BT, V, in_place, teacher):
     """One-pass kernel: ragged last member, ignored / identical / uniform rows and rows
-    whose logits span more than a thread's exponent range (the overflow reload)."""
-    assert one_pass(BT, V)
+    whose logits span far more than the exponent range of fp32 from one reference."""
+    assert one_pass(BT, V, teacher=teacher)
     ign = [0, BT - 1] if BT > 4 else [1]
     ident = [2] if BT > 4 else []
     unif = [3] if BT > 4 else []
@@ -84,17 +86,18 @@ def test_one_pass_shapes(BT, V, in_place):
         z[5, V // 3] = hi[0]
         u[6, V - 5] = hi[1]
         z[8, 1], u[8, 2] = hi[0], hi[1]
-    o, _ = fused_case(f"one-pass {BT}x{V}", z, u, t, in_place=in_place)
-    if ident:
+    o, _ = fused_case(f"one-pass {BT}x{V}", z, u if teacher else None, t, in_place=in_place)
+    if ident and teacher:
         assert o["tvd"][2] == 0.0 and o["sigma"][2] == 0.0
     if unif:
         assert abs(o["ce"][3] - math.log(V)) <= 1e-4
 
 
 @pytest.mark.parametrize("BT,V,dtype,teacher", [(520, 4099, "bf16", True), (520, 3000, "f32", True),
-                                                (6, 50001, "bf16", True), (520, 8200, "bf16", False),
-                                                (7, 1024, "f32", False)],
-                         ids=["bf16_V_not_8", "f32", "split_bf16", "ce_only", "tiny_f32_ce_only"])
+                                                (6, 50001, "bf16", True), (520, 4099, "bf16", False),
+                                                (7, 1024, "f32", False), (515, 1024, "bf16", True)],
+                         ids=["bf16_V_not_8", "f32", "split_bf16", "ce_only_V_not_8", "tiny_f32_ce_only",
+                              "short_rows"])
 def test_two_pass_fallback_shapes(BT, V, dtype, teacher):
     assert not one_pass(BT, V, dtype, teacher)
     ign = [1, BT - 1] if BT > 4 else [1]
@@ -191,14 +194,16 @@ def _sample_rows(w, n=40):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["train", "pr", "ties", "hugev"])
-def test_full_workload_fused(name):
+@pytest.mark.parametrize("name,teacher", [("train", True), ("pr", True), ("ties", True), ("hugev", True),
+                                          ("train", False), ("hugev", False)])
+def test_full_workload_fused(name, teacher):
     """As benchmarked: count the valid rows, then one fused pass with g_scale = 1/n_valid
     (in place for the pr workload)."""
     w = W.get(name)
-    announce(f"fused workload {name} {w.BT}x{w.V}: generating inputs")
+    announce(f"fused workload {name} {w.BT}x{w.V} teacher={teacher}: generating inputs")
     z, u, t = W.full(w)
-    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    zs, tg = to_dev(z), to_dev(t)
+    us = to_dev(u) if teacher else None
     del z, u
     inv = torch.zeros(1, dtype=torch.float32, device=DEV)
     lx.lx_ce_tvd_count_valid(tg, II, None, inv)
@@ -208,6 +213,8 @@ def test_full_workload_fused(name):
     vmax = zs.float().amax(1).cpu().numpy()
     announce(f"fused workload {name}: one pass (in place: {in_place})")
     out, grad = run_fused(zs, us, tg, 1.0, 1.0, grad=zs if in_place else torch.empty_like(zs), g_scale=inv)
+    if not teacher:
+        ur = None
     o = host(out)
     valid = t != II
     n_valid = int(valid.sum())
@@ -215,9 +222,10 @@ def test_full_workload_fused(name):
     assert np.all(bits32(o["ce"][~valid]) == 0) and np.all(o["ce"][valid] >= -1e-5)
     assert np.all(o["lse_s"][valid] >= vmax[valid] - 1e-4)
     assert np.all(o["lse_s"][valid] <= vmax[valid] + math.log(w.V) + 1e-4)
-    assert np.all((o["tvd"] >= 0) & (o["tvd"] <= 1 + 1e-6)) and np.all(np.abs(o["sigma"]) <= 1 + 1e-5)
-    ident = ro == W.ROLE_IDENTICAL
-    assert np.all(o["tvd"][ident] == 0.0) and np.all(o["sigma"][ident] == 0.0)
+    if teacher:
+        assert np.all((o["tvd"] >= 0) & (o["tvd"] <= 1 + 1e-6)) and np.all(np.abs(o["sigma"]) <= 1 + 1e-5)
+        ident = ro == W.ROLE_IDENTICAL
+        assert np.all(o["tvd"][ident] == 0.0) and np.all(o["sigma"][ident] == 0.0)
     assert np.all(np.abs(o["ce"][ro == W.ROLE_UNIFORM] - math.log(w.V)) <= 1e-4)
     gs = grad.float()
     rs, ra = gs.sum(1).abs().cpu().numpy(), gs.abs().sum(1).cpu().numpy()
