@@ -86,8 +86,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
       const int g = g0 + j * NT + tid;
       if (g < g1) {
         float x[8], y[8], o[8];
-        load8(zb + 8 * g, x);
-        if (TEACHER) load8(ub + 8 * g, y);
+        load8_stream(zb + 8 * g, x);
+        if (TEACHER) load8_stream(ub + 8 * g, y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = prob(x[e], nbs);
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
         }
-        store8(gb + 8 * g, o);
+        store8_stream(gb + 8 * g, o);
       }
     }
   }

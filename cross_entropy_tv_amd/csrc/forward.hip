@@ -111,6 +111,13 @@ __device__ __forceinline__ void store_ce(float* ce, const T* z, int64_t t, int V
 
 // ---------------------------------------------------------------- row path
 
+// Step-1 load of the row path: a CE-only row is read exactly once (streamed),
+// a CE+TVD row is read again by step 2 and keeps the default cache policy.
+template <bool STREAM, typename T>
+__device__ __forceinline__ void load8_row(const T* p, float (&x)[8]) {
+  if (STREAM) load8_stream(p, x); else load8(p, x);
+}
+
 template <typename T, bool TEACHER, int NT>
 __global__ __launch_bounds__(NT) void fwd_row_kernel(
     const T* __restrict__ student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
@@ -149,8 +156,8 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
     int g = tid;
     for (; g + NT < L.groups; g += 2 * NT) {
       float x0[8], x1[8], y0[8], y1[8];
-      load8(zb + 8 * g, x0);
-      load8(zb + 8 * (g + NT), x1);
+      load8_row<!TEACHER>(zb + 8 * g, x0);
+      load8_row<!TEACHER>(zb + 8 * (g + NT), x1);
       if (TEACHER) { load8(ub + 8 * g, y0); load8(ub + 8 * (g + NT), y1); }
       lse_add8(as, x0);
       lse_add8(as, x1);
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
     }
     if (g < L.groups) {
       float x0[8], y0[8];
-      load8(zb + 8 * g, x0);
+      load8_row<!TEACHER>(zb + 8 * g, x0);
       if (TEACHER) load8(ub + 8 * g, y0);
       lse_add8(as, x0);
       if (TEACHER) lse_add8(at, y0);

@@ -343,8 +343,10 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
 // med3(P - Q, -1, 1), a nonzero difference of two scaled probabilities being
 // at least 1 in magnitude unless both p and q are below 2^-103.  Products are
 // never contracted into the differences, so bit-identical student and teacher
-// rows give P == Q exactly.  Every member waits for the K step-2 pairs, so all
-// members hold the same sigma, then stores its chunk of the gradient.
+// rows give P == Q exactly.  Step 2 leaves sign(P - Q) in the teacher's
+// registers, so the gradient uses the very signs sigma was summed with.  Every
+// member waits for the K step-2 pairs, so all members hold the same sigma,
+// then stores its chunk of the gradient.
 // CE-only (!TEACHER): one exchange (the student lse), then g = k*g_ce*(p - onehot).
 //
 // Each member has read its whole chunk, and member 0 the target logit, before
@@ -483,7 +485,7 @@ void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ 
   const float lse_s = s_bc[0];
   const float lse_t = TEACHER ? s_bc[1] : 0.f;
   const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(lse_s)));
-  const float cu = TEACHER ? exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t))) : 0.f;
+  const float cu = TEACHER ? exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t))) : 0.f;  // q = E_u * cu
 
   float sigma = 0.f;
   if (TEACHER) {
@@ -500,10 +502,16 @@ void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ 
             const float P0 = ez[i][e] * czs, Q0 = eu[TEACHER ? i : 0][e] * cus;
             const float P1 = ez[i][e + 1] * czs, Q1 = eu[TEACHER ? i : 0][e + 1] * cus;
             const float D0 = P0 - Q0, D1 = P1 - Q1;
+            const float s0 = __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f);
+            const float s1 = __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f);
             A0 += fabsf(D0);
             A1 += fabsf(D1);
-            S0 = __builtin_fmaf(P0, __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f), S0);
-            S1 = __builtin_fmaf(P1, __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f), S1);
+            S0 = __builtin_fmaf(P0, s0, S0);
+            S1 = __builtin_fmaf(P1, s1, S1);
+            // the teacher's exponentials are not needed again: keep the sign in
+            // their place for step 3 (the same signs sigma was summed with)
+            eu[TEACHER ? i : 0][e] = s0;
+            eu[TEACHER ? i : 0][e + 1] = s1;
           }
         }
       }
@@ -565,8 +573,7 @@ void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ 
       for (int e = 0; e < 8; ++e) {
         const float p = ez[i][e] * cz;
         if (TEACHER) {
-          const float q = eu[TEACHER ? i : 0][e] * cu;
-          o[e] = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+          o[e] = p * __builtin_fmaf(eu[TEACHER ? i : 0][e], beta, alpha);  // eu holds sign(p - q)
         } else {
           o[e] = p * alpha;
         }
