@@ -122,6 +122,41 @@ __device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float 
   }
 }
 
+// As tv8, and returns the eight signs in wu (as bf16: -1, 0 and 1 are exact),
+// in place of the teacher's logits, which are not needed again.
+__device__ __forceinline__ void tv8_signs(const u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& A0,
+                                          float& A1, float& S0, float& S1) {
+  float x[8], y[8], sg[8];
+  unpack8(wz, x);
+  unpack8(wu, y);
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float p0 = prob(x[e], nbs), q0 = prob(y[e], nbt);
+    const float p1 = prob(x[e + 1], nbs), q1 = prob(y[e + 1], nbt);
+    const float d0 = p0 - q0, d1 = p1 - q1;
+    sg[e] = sign0(d0);
+    sg[e + 1] = sign0(d1);
+    A0 += fabsf(d0);
+    A1 += fabsf(d1);
+    S0 = __builtin_fmaf(p0, sg[e], S0);
+    S1 = __builtin_fmaf(p1, sg[e + 1], S1);
+  }
+  wu.x = pack_bf16x2(sg[0], sg[1]);
+  wu.y = pack_bf16x2(sg[2], sg[3]);
+  wu.z = pack_bf16x2(sg[4], sg[5]);
+  wu.w = pack_bf16x2(sg[6], sg[7]);
+}
+
+// eight gradients rounded to bf16 (nearest even), and eight bf16 quiet NaNs
+__device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
+  return (u32x4_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                   pack_bf16x2(o[6], o[7])};
+}
+__device__ __forceinline__ u32x4_t nan8() {
+  const unsigned h = kQNaN16 | (kQNaN16 << 16);
+  return (u32x4_t){h, h, h, h};
+}
+
 // Lanes [0, n) of wave 0 poll slots sl[0..n) until none is empty (or the
 // bounded wait gives up) and store what they read in got[]; n <= 64.
 // Returns true, in wave 0, when the wait gave up.
@@ -148,20 +183,34 @@ __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* 
 
 // NT threads per workgroup, G groups of 8 elements per thread and tensor, WPE
 // waves per SIMD (occupancy the register budget is sized for).
-template <int NT, int G, int WPE>
+//
+// FUSED = false: the forward.  Exchange 2 has the last member to arrive add
+// the K (sum |p - q|, sum p * sign) pairs in member order and write the five
+// outputs; the other members leave.
+// FUSED = true: the forward and the student gradient of the "Backward Pass"
+// section, g = p * (alpha + beta * s) - k * g_ce * [v == t], in the same pass
+// (the loss's upstream gradients are known up front).  Step 2 keeps the signs
+// s = sign(p - q), which are -1, 0 or 1 and so exact in bf16, in the
+// registers that held the teacher's logits; every member waits for the K
+// step-2 pairs, so all of them hold the same sigma, then step 3 recomputes p
+// from the student's logits and stores the gradient of its chunk.  Each member
+// has read its whole chunk, and member 0 the target logit, before any member
+// stores, so the gradient may overwrite the student logits.
+template <int NT, int G, int WPE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __restrict__ teacher,
-                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
-                        float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
-                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
-                        uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
-                        unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
+void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
+                    const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
+                    float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
+                    float* __restrict__ lse_t_out, float* __restrict__ sigma_out, uint16_t* grad, float g_ce,
+                    float g_tvd, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
+                    uint64_t* __restrict__ slot2, unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
   constexpr int W = NT / 64;
   __shared__ Lse red_z[W], red_u[W];
   __shared__ float red_a[W], red_s[W];
   __shared__ uint64_t got[2 * kClusterMaxK];
   __shared__ unsigned s_tile;
-  __shared__ float s_lse[2];
+  __shared__ float s_bc[4];
+  __shared__ float s_zt;
 
   const int tid = threadIdx.x;
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -170,19 +219,27 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
   const int64_t r = tile / (unsigned)K;
   const int j = (int)(tile - (unsigned)r * (unsigned)K);
   const int64_t t = target[r];
-  if (t == ignore_index) {
-    if (j == 0 && tid == 0) {
-      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
-    }
-    return;
-  }
 
   // ---- this member's chunk: groups [gb, ge) of the row; thread tid owns gb + tid + i * NT
   const int NG = V >> 3;
   const int gb = j * gpm;
   const int ge = min(NG, gb + gpm);
-  const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
   const int64_t row = r * (int64_t)V;
+  if (t == ignore_index) {
+    if (j == 0 && tid == 0) {
+      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
+    }
+    if (FUSED) {
+      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+#pragma unroll
+      for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
+    }
+    return;
+  }
+  const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
+  const bool t_ok = t >= 0 && t < V;
+  float zt = 0.f;
+  if (FUSED && j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
   const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
   const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
   u32x4_t rz[G], ru[G];
@@ -191,7 +248,6 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
     rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
     ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
   }
-  const bool t_ok = t >= 0 && t < V;
 
   // ---- step 1: sums of exponentials against this thread's reference maxima
   float mz = kMFloor, mu = kMFloor;
@@ -246,6 +302,9 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
       red_z[tid >> 6] = pz;
       red_u[tid >> 6] = pu;
     }
+    // the target logit has been read (not merely requested) before this member
+    // publishes anything, hence before any member can store a gradient over it
+    if (FUSED && tid == 0) s_zt = zt;
   }
   __syncthreads();
   uint64_t* s1 = slot1 + r * (int64_t)K * 2;
@@ -269,24 +328,25 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
       lse_merge(fz, Lse{lo_f(got[2 * k]), hi_f(got[2 * k])});
       lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
     }
-    s_lse[0] = lse_value(fz);
-    s_lse[1] = lse_value(fu);
+    s_bc[0] = lse_value(fz);
+    s_bc[1] = lse_value(fu);
   }
   __syncthreads();
-  const float lse_s = s_lse[0], lse_t = s_lse[1];
+  const float lse_s = s_bc[0], lse_t = s_bc[1];
 
-  // ---- step 2 over the kept chunk
+  // ---- step 2 over the kept chunk (FUSED: the signs replace the teacher's logits)
   const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
-  float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    if (i < n) {
-      launder(rz[i]);
-      launder(ru[i]);
-      tv8(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
-    }
-  }
   {
+    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        if (FUSED) tv8_signs(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
+        else tv8(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
+      }
+    }
     const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
     if ((tid & 63) == 0) {
       red_a[tid >> 6] = A;
@@ -294,11 +354,41 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
     }
   }
   __syncthreads();
-  if (tid >= 64) return;
-
-  // ---- exchange 2: the last member to arrive adds the K pairs in member order
   uint64_t* s2 = slot2 + r * (int64_t)K;
-  unsigned old = 0;
+  if (!FUSED) {
+    // ---- exchange 2: the last member to arrive adds the K pairs in member order
+    if (tid >= 64) return;
+    unsigned old = 0;
+    if (tid == 0) {
+      float A = red_a[0], S = red_s[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        A += red_a[w];
+        S += red_s[w];
+      }
+      publish(s2 + j, pack2(A, S));
+      old = __hip_atomic_fetch_add(arrived + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = __shfl(old, 0, 64);
+    if (old != (unsigned)(K - 1)) return;
+    if (tid == 0 && t_ok) zt = load1(student + row + t);
+    wait_slots(s2, K, got);
+    if (tid == 0) {
+      float A = lo_f(got[0]), S = hi_f(got[0]);
+      for (int k = 1; k < K; ++k) {
+        A += lo_f(got[k]);
+        S += hi_f(got[k]);
+      }
+      if (t_ok) ce[r] = lse_s - zt; else store_nan(ce + r);
+      tvd[r] = 0.5f * A;
+      lse_s_out[r] = lse_s;
+      lse_t_out[r] = lse_t;
+      sigma_out[r] = S;
+    }
+    return;
+  }
+
+  // ---- exchange 2 (FUSED): every member sums the K pairs in member order (identical sigma)
   if (tid == 0) {
     float A = red_a[0], S = red_s[0];
 #pragma unroll
@@ -307,66 +397,72 @@ void fwd_cluster_kernel(const uint16_t* __restrict__ student, const uint16_t* __
       S += red_s[w];
     }
     publish(s2 + j, pack2(A, S));
-    old = __hip_atomic_fetch_add(arrived + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  old = __shfl(old, 0, 64);
-  if (old != (unsigned)(K - 1)) return;
-  float zt = 0.f;
-  if (tid == 0 && t_ok) zt = load1(student + row + t);
-  wait_slots(s2, K, got);
+  if (tid < 64) wait_slots(s2, K, got);
+  __syncthreads();
   if (tid == 0) {
     float A = lo_f(got[0]), S = hi_f(got[0]);
     for (int k = 1; k < K; ++k) {
       A += lo_f(got[k]);
       S += hi_f(got[k]);
     }
-    if (t_ok) ce[r] = lse_s - zt; else store_nan(ce + r);
-    tvd[r] = 0.5f * A;
-    lse_s_out[r] = lse_s;
-    lse_t_out[r] = lse_t;
-    sigma_out[r] = S;
+    s_bc[2] = S;
+    if (j == 0) {
+      if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
+      tvd[r] = 0.5f * A;
+      lse_s_out[r] = lse_s;
+      lse_t_out[r] = lse_t;
+      sigma_out[r] = S;
+    }
+  }
+  __syncthreads();
+
+  // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
+  const float k = g_scale ? *g_scale : 1.0f;
+  const float kce = k * g_ce;
+  const float beta = 0.5f * k * g_tvd;
+  const float alpha = kce - beta * s_bc[2];
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int g = tid + i * NT;
+    launder(rz[i]);
+    launder(ru[i]);
+    float x[8], sg[8], o[8];
+    unpack8(rz[i], x);
+    unpack8(ru[i], sg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
+    const int rel = trel - 8 * g;
+    if ((unsigned)rel < 8u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+    }
+    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
   }
 }
 
-// ---------------------------------------------------------------- one-pass forward + backward
+// ---------------------------------------------------------------- one-pass CE-only forward + backward
 //
-// For a loss whose upstream gradients are known before it runs, the forward
-// outputs and the student gradient of the "Backward Pass" section,
-// g = p * (alpha + beta * s) - k * g_ce * [v == t], come out of one pass over
-// the logits.  Each member keeps E = exp(x - m) (fp32, twice the registers of
-// the bf16 logits), m being the thread's exact maximum over its groups (taken
-// while the chunk is unpacked, so no exponential can overflow); p is then
-// E * exp(m - lse), one multiply per element instead of an exponential.
-//
-// With a teacher (TEACHER): step 2 forms P = p * 2^126 the same way and sums
-// |P - Q| and P * sign(P - Q); the 2^126 scale makes sign(p - q) a plain
-// med3(P - Q, -1, 1), a nonzero difference of two scaled probabilities being
-// at least 1 in magnitude unless both p and q are below 2^-103.  Products are
-// never contracted into the differences, so bit-identical student and teacher
-// rows give P == Q exactly.  Step 2 leaves sign(P - Q) in the teacher's
-// registers, so the gradient uses the very signs sigma was summed with.  Every
-// member waits for the K step-2 pairs, so all members hold the same sigma,
-// then stores its chunk of the gradient.
-// CE-only (!TEACHER): one exchange (the student lse), then g = k*g_ce*(p - onehot).
-//
-// Each member has read its whole chunk, and member 0 the target logit, before
-// any member stores, so the gradient may overwrite the student logits.
-template <int NT, int G, int WPE, bool TEACHER>
+// With no teacher the one pass needs a single exchange (the student lse).
+// Each member keeps E = exp(x - m) (fp32), m being the thread's exact maximum
+// over its groups (taken while the chunk is unpacked, so no exponential can
+// overflow); after the exchange p = E * exp(m - lse) is one multiply per
+// element and g = k * g_ce * (p - [v == t]).  Member 0 has read the target
+// logit, and every member its whole chunk, before any member stores, so the
+// gradient may overwrite the student logits.
+template <int NT, int G, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
-                          const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
-                          float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
-                          float* __restrict__ lse_t_out, float* __restrict__ sigma_out,
-                          uint16_t* grad, float g_ce, float g_tvd, const float* __restrict__ g_scale,
-                          uint64_t* __restrict__ slot1, uint64_t* __restrict__ slot2,
-                          unsigned* __restrict__ ticket) {
+void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target, int V, int64_t ignore_index,
+                     int K, int gpm, float* __restrict__ ce, float* __restrict__ lse_s_out, uint16_t* grad,
+                     float g_ce, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
+                     unsigned* __restrict__ ticket) {
   constexpr int W = NT / 64;
-  constexpr int NS = TEACHER ? 2 : 1;  // exchange-1 slots per member
-  __shared__ Lse red_z[W], red_u[W];
-  __shared__ float red_a[W], red_s[W];
-  __shared__ uint64_t got[2 * kClusterMaxK];
+  __shared__ Lse red_z[W];
+  __shared__ uint64_t got[kClusterMaxK];
   __shared__ unsigned s_tile;
-  __shared__ float s_bc[4];
+  __shared__ float s_lse;
   __shared__ float s_zt;
 
   const int tid = threadIdx.x;
@@ -386,7 +482,6 @@ void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ 
     if (j == 0 && tid == 0) {
       ce[r] = 0.f;
       lse_s_out[r] = 0.f;
-      if (TEACHER) { tvd[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f; }
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
@@ -396,203 +491,84 @@ void fused_cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ 
   float zt = 0.f;
   if (j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
 
-  // ---- load the chunk; unpack it into the E registers and take this thread's exact maxima
-  float ez[G][8], eu[TEACHER ? G : 1][8];
-  float mz = kMFloor, mu = kMFloor;
+  // ---- load the chunk; unpack it into the E registers and take this thread's exact maximum
+  float ez[G][8];
+  float mz = kMFloor;
   {
     const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
-    u32x4_t rz[G], ru[TEACHER ? G : 1];
+    u32x4_t rz[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
-    if (TEACHER) {
-      const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
-#pragma unroll
-      for (int i = 0; i < G; ++i) ru[TEACHER ? i : 0] = ld_stream(rsu, (tid + i * NT) * 16);
-    }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       unpack8(rz[i], ez[i]);
-      if (TEACHER) unpack8(ru[TEACHER ? i : 0], eu[TEACHER ? i : 0]);
-      if (i < n) {
-        mz = fmaxf(mz, max8(ez[i]));
-        if (TEACHER) mu = fmaxf(mu, max8(eu[TEACHER ? i : 0]));
-      }
+      if (i < n) mz = fmaxf(mz, max8(ez[i]));
     }
   }
-  // ---- step 1: E = exp(x - m) in place (every E <= 1: no overflow), and its sums
-  float sz0 = 0.f, sz1 = 0.f, su0 = 0.f, su1 = 0.f;
+  // ---- E = exp(x - m) in place (every E <= 1: no overflow), and its sum
+  float s0 = 0.f, s1v = 0.f;
   {
-    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+    const float nbz = -(mz * kLog2e);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ez[i][e] = exp2_hw(__builtin_fmaf(ez[i][e], kLog2e, nbz));
-        if (TEACHER) eu[TEACHER ? i : 0][e] = exp2_hw(__builtin_fmaf(eu[TEACHER ? i : 0][e], kLog2e, nbu));
-      }
+      for (int e = 0; e < 8; ++e) ez[i][e] = exp2_hw(__builtin_fmaf(ez[i][e], kLog2e, nbz));
       if (i < n) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          sz0 += ez[i][e];
-          sz1 += ez[i][e + 1];
-          if (TEACHER) {
-            su0 += eu[TEACHER ? i : 0][e];
-            su1 += eu[TEACHER ? i : 0][e + 1];
-          }
+          s0 += ez[i][e];
+          s1v += ez[i][e + 1];
         }
       }
     }
   }
   {
-    Lse pz = wave_lse(Lse{mz, sz0 + sz1});
-    Lse pu{0.f, 0.f};
-    if (TEACHER) pu = wave_lse(Lse{mu, su0 + su1});
-    if ((tid & 63) == 0) {
-      red_z[tid >> 6] = pz;
-      red_u[tid >> 6] = pu;
-    }
+    const Lse pz = wave_lse(Lse{mz, s0 + s1v});
+    if ((tid & 63) == 0) red_z[tid >> 6] = pz;
     // the target logit has been read (not merely requested) before this member
     // publishes anything, hence before any member can store a gradient over it
     if (tid == 0) s_zt = zt;
   }
   __syncthreads();
-  uint64_t* s1 = slot1 + r * (int64_t)K * NS;
+  uint64_t* s1 = slot1 + r * (int64_t)K;
   if (tid == 0) {
-    Lse fz = red_z[0], fu = red_u[0];
+    Lse fz = red_z[0];
 #pragma unroll
-    for (int w = 1; w < W; ++w) {
-      lse_merge(fz, red_z[w]);
-      if (TEACHER) lse_merge(fu, red_u[w]);
-    }
-    publish(s1 + NS * j, pack2(fz.m, fz.s));
-    if (TEACHER) publish(s1 + NS * j + 1, pack2(fu.m, fu.s));
+    for (int w = 1; w < W; ++w) lse_merge(fz, red_z[w]);
+    publish(s1 + j, pack2(fz.m, fz.s));
   }
 
-  // ---- exchange 1: the row's K (max, sum-exp) pairs, merged in member order
-  if (tid < 64) wait_slots(s1, NS * K, got);
+  // ---- the exchange: the row's K (max, sum-exp) pairs, merged in member order
+  if (tid < 64) wait_slots(s1, K, got);
   __syncthreads();
   if (tid == 0) {
     Lse fz{lo_f(got[0]), hi_f(got[0])};
-    for (int k = 1; k < K; ++k) lse_merge(fz, Lse{lo_f(got[NS * k]), hi_f(got[NS * k])});
-    s_bc[0] = lse_value(fz);
-    if (TEACHER) {
-      Lse fu{lo_f(got[1]), hi_f(got[1])};
-      for (int k = 1; k < K; ++k) lse_merge(fu, Lse{lo_f(got[2 * k + 1]), hi_f(got[2 * k + 1])});
-      s_bc[1] = lse_value(fu);
+    for (int k = 1; k < K; ++k) lse_merge(fz, Lse{lo_f(got[k]), hi_f(got[k])});
+    s_lse = lse_value(fz);
+    if (j == 0) {
+      if (t_ok) ce[r] = s_lse - s_zt; else store_nan(ce + r);
+      lse_s_out[r] = s_lse;
     }
   }
   __syncthreads();
-  const float lse_s = s_bc[0];
-  const float lse_t = TEACHER ? s_bc[1] : 0.f;
-  const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(lse_s)));
-  const float cu = TEACHER ? exp2_hw(__builtin_fmaf(mu, kLog2e, neg_scaled(lse_t))) : 0.f;  // q = E_u * cu
+  const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(s_lse)));  // p = E * cz
 
-  float sigma = 0.f;
-  if (TEACHER) {
-    // ---- step 2: P = E * (exp(m - lse) * 2^126), sum |P - Q| and P * sign(P - Q)
-    {
-      const float czs = cz * 0x1p126f, cus = cu * 0x1p126f;
-      float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        if (i < n) {
-#pragma clang fp contract(off)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float P0 = ez[i][e] * czs, Q0 = eu[TEACHER ? i : 0][e] * cus;
-            const float P1 = ez[i][e + 1] * czs, Q1 = eu[TEACHER ? i : 0][e + 1] * cus;
-            const float D0 = P0 - Q0, D1 = P1 - Q1;
-            const float s0 = __builtin_amdgcn_fmed3f(D0, -1.0f, 1.0f);
-            const float s1 = __builtin_amdgcn_fmed3f(D1, -1.0f, 1.0f);
-            A0 += fabsf(D0);
-            A1 += fabsf(D1);
-            S0 = __builtin_fmaf(P0, s0, S0);
-            S1 = __builtin_fmaf(P1, s1, S1);
-            // the teacher's exponentials are not needed again: keep the sign in
-            // their place for step 3 (the same signs sigma was summed with)
-            eu[TEACHER ? i : 0][e] = s0;
-            eu[TEACHER ? i : 0][e + 1] = s1;
-          }
-        }
-      }
-      const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
-      if ((tid & 63) == 0) {
-        red_a[tid >> 6] = A;
-        red_s[tid >> 6] = S;
-      }
-    }
-    __syncthreads();
-    // ---- exchange 2: every member sums the K pairs in member order (identical sigma)
-    uint64_t* s2 = slot2 + r * (int64_t)K;
-    if (tid == 0) {
-      float A = red_a[0], S = red_s[0];
-#pragma unroll
-      for (int w = 1; w < W; ++w) {
-        A += red_a[w];
-        S += red_s[w];
-      }
-      publish(s2 + j, pack2(A, S));
-    }
-    if (tid < 64) wait_slots(s2, K, got);
-    __syncthreads();
-    if (tid == 0) {
-      float A = lo_f(got[0]), S = hi_f(got[0]);
-      for (int k = 1; k < K; ++k) {
-        A += lo_f(got[k]);
-        S += hi_f(got[k]);
-      }
-      s_bc[2] = 0.5f * A * 0x1p-126f;
-      s_bc[3] = S * 0x1p-126f;
-    }
-    __syncthreads();
-    sigma = s_bc[3];
-  }
-  if (j == 0 && tid == 0) {
-    if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
-    lse_s_out[r] = lse_s;
-    if (TEACHER) {
-      tvd[r] = s_bc[2];
-      lse_t_out[r] = lse_t;
-      sigma_out[r] = sigma;
-    }
-  }
-
-  // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
-  const float k = g_scale ? *g_scale : 1.0f;
-  const float kce = k * g_ce;
-  const float beta = TEACHER ? 0.5f * k * g_tvd : 0.f;
-  const float alpha = kce - beta * sigma;
+  // ---- g = k * g_ce * (p - [v == t])
+  const float kce = (g_scale ? *g_scale : 1.0f) * g_ce;
+  const float alpha = kce * cz;
   const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int g = tid + i * NT;
     float o[8];
-    {
-#pragma clang fp contract(off)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = ez[i][e] * cz;
-        if (TEACHER) {
-          o[e] = p * __builtin_fmaf(eu[TEACHER ? i : 0][e], beta, alpha);  // eu holds sign(p - q)
-        } else {
-          o[e] = p * alpha;
-        }
-      }
-    }
+    for (int e = 0; e < 8; ++e) o[e] = ez[i][e] * alpha;
     const int rel = trel - 8 * g;
     if ((unsigned)rel < 8u) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
     }
-    u32x4_t w;
-    if (t_ok) {
-      w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
-      w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
-    } else {
-      const unsigned h = kQNaN16 | (kQNaN16 << 16);
-      w = (u32x4_t){h, h, h, h};
-    }
-    st_stream(rsg, g * 16, w);
+    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
   }
 }
 
@@ -614,16 +590,15 @@ __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restri
 constexpr int kClThreads = 256;
 constexpr int kClGroups = 16;
 constexpr int kClWavesPerSimd = 3;
-// One-pass forward + backward kernel (keeps exponentials; step 3 then needs no
-// exponential).  With a teacher, measured on the training batch: 256 x 8 x 3
-// (K = 10) 1.72 ms, 256 x 6 x 4 1.79 ms, 256 x 12 x 2 1.82 ms, 512 x 4 x 4
-// 2.04 ms, 128 x 8 x 3 2.02 ms; a persistent variant streaming the next chunk
-// into LDS during the exchanges (two workgroups per compute unit) 2.10 ms.
-// CE-only keeps one tensor, so twice the groups fit.
-constexpr int kFusedThreads = 256;
-constexpr int kFusedGroups = 8;
-constexpr int kFusedWavesPerSimd = 3;
+// One-pass forward + backward.  With a teacher it is the forward's kernel
+// (FUSED), chunked the same way; measured on the training batch, 1.48 ms
+// against 1.68 ms for a variant that keeps fp32 exponentials (twice the
+// registers per element, so K = 10 members per row instead of 5, and each
+// row waits on its slowest member twice).  CE-only keeps exponentials of
+// one tensor (fused_ce_kernel), 16 groups per thread.
+constexpr int kFusedCeThreads = 256;
 constexpr int kFusedCeGroups = 16;
+constexpr int kFusedCeWavesPerSimd = 3;
 constexpr int64_t kClTargetTiles = 2048;  // enough workgroups to fill 256 compute units several times
 
 static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups) {
@@ -655,7 +630,8 @@ ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
 }
 
 ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher) {
-  return plan_cfg(BT, V, esize, kFusedThreads, teacher ? kFusedGroups : kFusedCeGroups);
+  return teacher ? plan_cfg(BT, V, esize, kClThreads, kClGroups)
+                 : plan_cfg(BT, V, esize, kFusedCeThreads, kFusedCeGroups);
 }
 
 // Workspace: slot1 [BT][K][2] | slot2 [BT][K] (64-bit) | arrived [BT] | ticket (32-bit)
@@ -680,12 +656,11 @@ static ClusterWs cluster_ws(void* ws, int64_t BT, int K, hipStream_t st) {
 hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
-  const auto* zs = static_cast<const uint16_t*>(a.student);
-  const auto* us = static_cast<const uint16_t*>(a.teacher);
   const unsigned tiles = (unsigned)(a.BT * (int64_t)c.K);
-  hipLaunchKernelGGL((fwd_cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd>), dim3(tiles), dim3(kClThreads), 0,
-                     st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t,
-                     a.sigma, w.slot1, w.slot2, w.arrived, w.ticket);
+  hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd, false>), dim3(tiles), dim3(kClThreads),
+                     0, st, static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher),
+                     a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
+                     nullptr, 0.f, 0.f, nullptr, w.slot1, w.slot2, w.arrived, w.ticket);
   return hipGetLastError();
 }
 
@@ -694,17 +669,16 @@ hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const Clus
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
   const dim3 grid((unsigned)(a.BT * (int64_t)c.K));
   const auto* zs = static_cast<const uint16_t*>(a.student);
-  const auto* us = static_cast<const uint16_t*>(a.teacher);
   auto* gr = static_cast<uint16_t*>(g.grad);
   if (a.teacher) {
-    hipLaunchKernelGGL((fused_cluster_kernel<kFusedThreads, kFusedGroups, kFusedWavesPerSimd, true>), grid,
-                       dim3(kFusedThreads), 0, st, zs, us, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
-                       a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.ticket);
+    hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd, true>), grid, dim3(kClThreads), 0,
+                       st, zs, static_cast<const uint16_t*>(a.teacher), a.target, (int)a.V, a.ignore_index, c.K,
+                       c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce, g.g_tvd, g.g_scale, w.slot1,
+                       w.slot2, w.arrived, w.ticket);
   } else {
-    hipLaunchKernelGGL((fused_cluster_kernel<kFusedThreads, kFusedCeGroups, kFusedWavesPerSimd, false>), grid,
-                       dim3(kFusedThreads), 0, st, zs, nullptr, a.target, (int)a.V, a.ignore_index, c.K, c.gpm,
-                       a.ce, nullptr, a.lse_s, nullptr, nullptr, gr, g.g_ce, 0.f, g.g_scale, w.slot1, w.slot2,
-                       w.ticket);
+    hipLaunchKernelGGL((fused_ce_kernel<kFusedCeThreads, kFusedCeGroups, kFusedCeWavesPerSimd>), grid,
+                       dim3(kFusedCeThreads), 0, st, zs, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
+                       a.lse_s, gr, g.g_ce, g.g_scale, w.slot1, w.ticket);
   }
   return hipGetLastError();
 }
