@@ -196,7 +196,7 @@ __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* 
 // from the student's logits and stores the gradient of its chunk.  Each member
 // has read its whole chunk, and member 0 the target logit, before any member
 // stores, so the gradient may overwrite the student logits.
-template <int NT, int G, int WPE, bool FUSED>
+template <int NT, int G, int GL, int WPE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
 void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
                     const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
@@ -211,6 +211,7 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   __shared__ unsigned s_tile;
   __shared__ float s_bc[4];
   __shared__ float s_zt;
+  __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
 
   const int tid = threadIdx.x;
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -232,11 +233,14 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     if (FUSED) {
       const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
 #pragma unroll
-      for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
+      for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
     }
     return;
   }
-  const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
+  // groups tid + i * NT of the chunk: i < G in registers, G <= i < G + GL in LDS
+  const int cnt = ge - gb;
+  const int n = tid < cnt ? min(G, (cnt - tid - 1) / NT + 1) : 0;
+  const int nl = NT * G + tid < cnt ? min(GL, (cnt - NT * G - tid - 1) / NT + 1) : 0;
   const bool t_ok = t >= 0 && t < V;
   float zt = 0.f;
   if (FUSED && j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
@@ -247,6 +251,20 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   for (int i = 0; i < G; ++i) {
     rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
     ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+  }
+  if (GL > 0 && cnt > NT * G) {
+    // the rest of the chunk goes straight to LDS, 64 groups (1 KB) per load
+    const int lcnt = cnt - NT * G;
+    const int64_t lo = row + 8 * (int64_t)(gb + NT * G);
+    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + lo, lcnt * 16);
+    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + lo, lcnt * 16);
+    const int lane = tid & 63;
+    for (int b = tid >> 6; b < (lcnt + 63) >> 6; b += NT / 64) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrz, (__attribute__((address_space(3))) void*)&lz[b * 64], 16,
+                                               (b * 64 + lane) * 16, 0, 0, kStreamPolicy);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lru, (__attribute__((address_space(3))) void*)&lu[b * 64], 16,
+                                               (b * 64 + lane) * 16, 0, 0, kStreamPolicy);
+    }
   }
 
   // ---- step 1: sums of exponentials against this thread's reference maxima
@@ -268,6 +286,16 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
         expsum8(ru[i], nbu, su0, su1);
       }
     }
+    if (GL > 0) {
+      __syncthreads();  // every wave's loads into LDS have landed
+#pragma unroll
+      for (int i = 0; i < GL; ++i) {
+        if (i < nl) {
+          expsum8(lz[tid + i * NT], nbz, sz0, sz1);
+          expsum8(lu[tid + i * NT], nbu, su0, su1);
+        }
+      }
+    }
   }
   if (!(sz0 + sz1 < 3.0e38f) || !(su0 + su1 < 3.0e38f)) {
     // a logit far above the first group's maximum: redo against the true maxima
@@ -283,6 +311,13 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
         mu = fmaxf(mu, max8(y));
       }
     }
+    for (int i = 0; i < nl; ++i) {
+      float x[8], y[8];
+      unpack8(lz[tid + i * NT], x);
+      unpack8(lu[tid + i * NT], y);
+      mz = fmaxf(mz, max8(x));
+      mu = fmaxf(mu, max8(y));
+    }
     const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
     sz0 = sz1 = su0 = su1 = 0.f;
 #pragma unroll
@@ -293,6 +328,10 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
         expsum8(rz[i], nbz, sz0, sz1);
         expsum8(ru[i], nbu, su0, su1);
       }
+    }
+    for (int i = 0; i < nl; ++i) {
+      expsum8(lz[tid + i * NT], nbz, sz0, sz1);
+      expsum8(lu[tid + i * NT], nbu, su0, su1);
     }
   }
   {
@@ -345,6 +384,18 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
         launder(ru[i]);
         if (FUSED) tv8_signs(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
         else tv8(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      if (i < nl) {
+        u32x4_t wu = lu[tid + i * NT];
+        if (FUSED) {
+          tv8_signs(lz[tid + i * NT], wu, nbs, nbt, A0, A1, S0, S1);
+          lu[tid + i * NT] = wu;  // this thread's own slot: read back by it in step 3
+        } else {
+          tv8(lz[tid + i * NT], wu, nbs, nbt, A0, A1, S0, S1);
+        }
       }
     }
     const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
@@ -432,6 +483,21 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     float x[8], sg[8], o[8];
     unpack8(rz[i], x);
     unpack8(ru[i], sg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
+    const int rel = trel - 8 * g;
+    if ((unsigned)rel < 8u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+    }
+    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
+  }
+#pragma unroll
+  for (int i = 0; i < GL; ++i) {
+    const int g = NT * G + tid + i * NT;
+    float x[8], sg[8], o[8];
+    unpack8(lz[tid + i * NT], x);
+    unpack8(lu[tid + i * NT], sg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
     const int rel = trel - 8 * g;
@@ -583,12 +649,17 @@ __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restri
 
 // ---------------------------------------------------------------- planning and launch
 
-// Forward kernel: NT threads x G groups of bf16 logits per thread and tensor,
-// WPE waves per SIMD (three 256-thread workgroups per compute unit).  Measured
-// on the 8192 x 151936 training batch: 256 x 16 x 3 (K = 5) 1.03 ms, 256 x 10
-// x 4 (K = 8) 1.06 ms, 512 x 10 x 4 (K = 4) 1.14 ms, 1024 x 10 x 4 1.23 ms.
+// Read-once kernel: NT threads x (G in registers + GL in LDS) groups of bf16
+// logits per thread and tensor, WPE waves per SIMD (three 256-thread
+// workgroups per compute unit, 24 KB of LDS each).  Measured on the 8192 x
+// 151936 training batch (forward / one pass): 256 x (16 + 3) x 3 (K = 4)
+// 0.985 / 1.41 ms; 256 x (13 + 6) x 3 (K = 4) 0.984 / 1.41; 256 x (11 + 4) x 4
+// (K = 5) 0.995 / 1.42; 256 x 16 x 3 without LDS (K = 5) 1.02 / 1.46; 256 x
+// (24 + 2) x 2 (K = 3) 1.09 / 1.61; 256 x 10 x 4 (K = 8) 1.06 / -; 512 x 10 x
+// 4 (K = 4) 1.14 / -; 384 and 768 threads (K = 4, 2) 1.76 / 2.52, 1.27 / 1.99.
 constexpr int kClThreads = 256;
 constexpr int kClGroups = 16;
+constexpr int kClLdsGroups = 3;
 constexpr int kClWavesPerSimd = 3;
 // One-pass forward + backward.  With a teacher it is the forward's kernel
 // (FUSED), chunked the same way; measured on the training batch, 1.48 ms
@@ -626,11 +697,11 @@ static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups
 
 ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
   if (!teacher) return ClusterPlan{0, 0, 0};  // CE-only: one stream, the row path already reads it once
-  return plan_cfg(BT, V, esize, kClThreads, kClGroups);
+  return plan_cfg(BT, V, esize, kClThreads, kClGroups + kClLdsGroups);
 }
 
 ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher) {
-  return teacher ? plan_cfg(BT, V, esize, kClThreads, kClGroups)
+  return teacher ? plan_cfg(BT, V, esize, kClThreads, kClGroups + kClLdsGroups)
                  : plan_cfg(BT, V, esize, kFusedCeThreads, kFusedCeGroups);
 }
 
@@ -657,7 +728,7 @@ hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStr
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
   const unsigned tiles = (unsigned)(a.BT * (int64_t)c.K);
-  hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd, false>), dim3(tiles), dim3(kClThreads),
+  hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, false>), dim3(tiles), dim3(kClThreads),
                      0, st, static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher),
                      a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
                      nullptr, 0.f, 0.f, nullptr, w.slot1, w.slot2, w.arrived, w.ticket);
@@ -671,7 +742,7 @@ hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const Clus
   const auto* zs = static_cast<const uint16_t*>(a.student);
   auto* gr = static_cast<uint16_t*>(g.grad);
   if (a.teacher) {
-    hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClWavesPerSimd, true>), grid, dim3(kClThreads), 0,
+    hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, true>), grid, dim3(kClThreads), 0,
                        st, zs, static_cast<const uint16_t*>(a.teacher), a.target, (int)a.V, a.ignore_index, c.K,
                        c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce, g.g_tvd, g.g_scale, w.slot1,
                        w.slot2, w.arrived, w.ticket);

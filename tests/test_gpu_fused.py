@@ -93,6 +93,35 @@ def test_one_pass_shapes(BT, V, in_place, teacher):
         assert abs(o["ce"][3] - math.log(V)) <= 1e-4
 
 
+@pytest.mark.parametrize("V", [38400, 72000], ids=["K1_V38400", "K2_V72000"])
+def test_lds_part_of_the_chunk(V):
+    """2048 rows make each row a single-digit number of members whose chunks are longer
+    than the registers hold, so their tails live in LDS; in place, with special rows,
+    compared with the oracle on sampled rows (and row properties on all of them)."""
+    BT = 2048
+    special = {"ignore_rows": [0, 9, BT - 1], "identical_rows": [2, 10], "uniform_rows": [3]}
+    z, u, t = W.custom(BT, V, "bf16", seed=V, scale=3.0, teacher_noise=0.5, **special)
+    hi = W.bf16_bits_rne(np.array([150.0, 120.0], dtype=np.float32))
+    z[5, V - 7] = hi[0]   # in the LDS part of the last member: far above the thread's reference
+    u[6, V - 100] = hi[1]
+    rows = np.array(sorted({0, 2, 3, 5, 6, 9, 10, 11, 777, 1500, BT - 2, BT - 1}))
+    zr, ur = z[rows].copy(), u[rows].copy()
+    announce(f"fused LDS part {BT}x{V} in place")
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    out, g = run_fused(zs, us, tg, 0.5, 1.5, grad=zs)
+    o = host(out)
+    assert o["tvd"][2] == 0.0 and o["sigma"][2] == 0.0 and o["tvd"][10] == 0.0
+    assert abs(o["ce"][3] - math.log(V)) <= 1e-4
+    valid = t != II
+    gs = g.float()
+    rs, ra = gs.sum(1).abs().cpu().numpy(), gs.abs().sum(1).cpu().numpy()
+    del gs
+    assert np.all(rs[valid] <= 2.0 ** -8 * ra[valid] + V * 1e-6 + 1e-9)
+    sel = torch.from_numpy(rows).to(DEV)
+    check_forward({k: v[rows] for k, v in o.items()}, zr, ur, t[rows], II, f"LDS part {V}")
+    check_grad(grad_to_host(g[sel]), grad_bits(g[sel]), zr, ur, t[rows], II, 0.5, 1.5, f"LDS part {V}")
+
+
 @pytest.mark.parametrize("BT,V,dtype,teacher", [(520, 4099, "bf16", True), (520, 3000, "f32", True),
                                                 (6, 50001, "bf16", True), (520, 4099, "bf16", False),
                                                 (7, 1024, "f32", False), (515, 1024, "bf16", True)],

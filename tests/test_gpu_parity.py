@@ -133,6 +133,22 @@ def test_cluster_path_shapes(BT, V):
     assert abs(o["ce"][3] - math.log(V)) <= 1e-4
 
 
+@pytest.mark.parametrize("V", [38400, 72000], ids=["K1_V38400", "K2_V72000"])
+def test_cluster_path_lds_part(V):
+    """Rows whose member chunks are longer than the registers hold (tails in LDS),
+    forward outputs on sampled rows against the oracle."""
+    BT = 2048
+    z, u, t = W.custom(BT, V, "bf16", seed=V + 1, scale=3.0, teacher_noise=0.5, ignore_rows=[0, BT - 1],
+                       identical_rows=[2], uniform_rows=[3])
+    hi = W.bf16_bits_rne(np.array([150.0], dtype=np.float32))
+    z[5, V - 7] = hi[0]
+    announce(f"read-once forward, LDS part {BT}x{V}")
+    o = host(run_fwd(to_dev(z), to_dev(u), to_dev(t)))
+    rows = np.array([0, 1, 2, 3, 4, 5, 6, 999, BT - 2, BT - 1])
+    check_forward({k: v[rows] for k, v in o.items()}, z[rows], u[rows], t[rows], II, f"LDS part {V}")
+    assert o["tvd"][2] == 0.0 and abs(o["ce"][3] - math.log(V)) <= 1e-4
+
+
 def test_cluster_path_deterministic_and_matches_row_path():
     z, u, t = W.custom(530, 16384, "bf16", seed=77, scale=2.0, offset_range=10.0, ignore_rows=[4])
     announce("cluster path: 3 repeats bitwise, and vs the two-stream row path on unaligned copies")
