@@ -670,7 +670,11 @@ constexpr int kClWavesPerSimd = 3;
 constexpr int kFusedCeThreads = 256;
 constexpr int kFusedCeGroups = 16;
 constexpr int kFusedCeWavesPerSimd = 3;
-constexpr int64_t kClTargetTiles = 2048;  // enough workgroups to fill 256 compute units several times
+// Fewest (row, member) tiles worth splitting rows further for: with few long
+// rows more members per row means more, smaller tiles but more stragglers to
+// wait for.  64 x 262144: 512 tiles (K = 8) 36 / 42 us (forward / one pass),
+// 1024 (K = 16) 44 / 59 us, 2048 (K = 32) 59 / 81 us, 256 (K = 7) 38 / 44 us.
+constexpr int64_t kClTargetTiles = 512;
 
 static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups) {
   ClusterPlan c{0, 0, 0};
