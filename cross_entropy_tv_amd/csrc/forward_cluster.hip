@@ -122,30 +122,66 @@ __device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float 
   }
 }
 
-// As tv8, and returns the eight signs in wu (as bf16: -1, 0 and 1 are exact),
-// in place of the teacher's logits, which are not needed again.
-__device__ __forceinline__ void tv8_signs(const u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& A0,
-                                          float& A1, float& S0, float& S1) {
-  float x[8], y[8], sg[8];
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, (h2_t){(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ h2_t as_h2(unsigned v) { return __builtin_bit_cast(h2_t, v); }
+// (the words are copied out first: a bit cast applied to the element
+// expression w.y itself is compiled as a cast of w.x)
+__device__ __forceinline__ void unpack8_f16(const u32x4_t& w, float (&x)[8]) {
+  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  const h2_t a = as_h2(w0), b = as_h2(w1), c = as_h2(w2), d = as_h2(w3);
+  x[0] = (float)a.x; x[1] = (float)a.y; x[2] = (float)b.x; x[3] = (float)b.y;
+  x[4] = (float)c.x; x[5] = (float)c.y; x[6] = (float)d.x; x[7] = (float)d.y;
+}
+
+// Step 2 forms every probability scaled by 2^kPScale (the exponent bias is
+// raised by kPScale): the sums come back to scale with an exact power-of-two
+// multiply, and the one-pass kernel can keep 2^kPScale * p in fp16 for step 3,
+// normal down to p = 2^-29 and below 32768 for p <= 1.
+constexpr float kPScale = 15.0f;
+constexpr float kInvPScale = 0x1p-15f;
+
+// fp16 p is good enough for the gradient only while its error stays inside
+// the absolute part of the gradient's bound (2^-8 relative + 1e-6).  With
+// u = 2^-8 the unit roundoff of bf16 and e <= 2^-11 + 2e-6 the relative error
+// of g before its one rounding to bf16 (fp16 p, plus the fp32 terms), the
+// stored value is within u |g| + (e (1 + u / (1 + u)) - u^2 / (1 + u)) |g|
+// = u |g| + 4.77e-4 |g| of g, and every |g| = p * |alpha + beta * s| is at
+// most M = k * (|g_ce| + |g_tvd|).  M <= 2.08e-3 keeps the excess below
+// 9.92e-7.  A mean-reduced loss over 962 or more rows (k = 1/n_valid, unit
+// g_ce and g_tvd) is within this everywhere; with a larger M only elements
+// with p > kKeepP16Bound / M (at most M / kKeepP16Bound of them per row) can
+// exceed it, and step 3 recomputes the groups that hold one from their logits.
+constexpr float kKeepP16Bound = 2.08e-3f;
+
+// As tv8, and keeps what step 3 needs in place of the two groups' logits:
+// 2^kPScale * p in wz and the signs in wu, both as fp16 (-1, 0 and 1 are
+// exact).  nbs and nbt carry the kPScale bias.
+__device__ __forceinline__ void tv8_signs(u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& A0, float& A1,
+                                          float& S0, float& S1) {
+  float x[8], y[8], p[8], sg[8];
   unpack8(wz, x);
   unpack8(wu, y);
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    const float p0 = prob(x[e], nbs), q0 = prob(y[e], nbt);
-    const float p1 = prob(x[e + 1], nbs), q1 = prob(y[e + 1], nbt);
-    const float d0 = p0 - q0, d1 = p1 - q1;
+    p[e] = prob(x[e], nbs);
+    p[e + 1] = prob(x[e + 1], nbs);
+    const float q0 = prob(y[e], nbt), q1 = prob(y[e + 1], nbt);
+    const float d0 = p[e] - q0, d1 = p[e + 1] - q1;
     sg[e] = sign0(d0);
     sg[e + 1] = sign0(d1);
     A0 += fabsf(d0);
     A1 += fabsf(d1);
-    S0 = __builtin_fmaf(p0, sg[e], S0);
-    S1 = __builtin_fmaf(p1, sg[e + 1], S1);
+    S0 = __builtin_fmaf(p[e], sg[e], S0);
+    S1 = __builtin_fmaf(p[e + 1], sg[e + 1], S1);
   }
-  wu.x = pack_bf16x2(sg[0], sg[1]);
-  wu.y = pack_bf16x2(sg[2], sg[3]);
-  wu.z = pack_bf16x2(sg[4], sg[5]);
-  wu.w = pack_bf16x2(sg[6], sg[7]);
+  wz = (u32x4_t){pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
+  wu = (u32x4_t){pack_f16x2(sg[0], sg[1]), pack_f16x2(sg[2], sg[3]), pack_f16x2(sg[4], sg[5]),
+                 pack_f16x2(sg[6], sg[7])};
 }
+
 
 // eight gradients rounded to bf16 (nearest even), and eight bf16 quiet NaNs
 __device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
@@ -155,6 +191,51 @@ __device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
 __device__ __forceinline__ u32x4_t nan8() {
   const unsigned h = kQNaN16 | (kQNaN16 << 16);
   return (u32x4_t){h, h, h, h};
+}
+
+// Step 3 over one group: g = p * (alpha + beta * s) from the fp16 pair kept by
+// tv8_signs (a15, b15 are alpha and beta times 2^-kPScale), and at the target
+// element (rel in [0, 8)) g = pt * (alpha + beta * s) - kce with pt in fp32:
+// there p may be close to 1 and the difference small.  zero is +0 hidden from
+// the optimiser: p * t + zero is the product (a zero product comes out +0)
+// but, unlike p * t, maps to one mixed-precision multiply-add that reads the
+// fp16 half directly.
+__device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, float a15, float b15, float zero,
+                                        int rel, float pt, float alpha, float beta, float kce) {
+  float p[8], sg[8], o[8];
+  unpack8_f16(wp, p);
+  unpack8_f16(ws, sg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p[e], __builtin_fmaf(sg[e], b15, a15), zero);
+  if ((unsigned)rel < 8u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], beta, alpha) - kce : o[e];
+  }
+  return pack8(o);
+}
+
+// true when one of the eight fp16 values of w exceeds thr
+__device__ __forceinline__ bool any_above(const u32x4_t& w, _Float16 thr) {
+  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  const h2_t m = __builtin_elementwise_max(__builtin_elementwise_max(as_h2(w0), as_h2(w1)),
+                                           __builtin_elementwise_max(as_h2(w2), as_h2(w3)));
+  return m.x > thr || m.y > thr;
+}
+
+// As grad8 with p recomputed in fp32 from the student's bf16 logits wz (nbs
+// without the kPScale bias), so the target element needs only - kce.
+__device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t& ws, float nbs, int rel, float alpha,
+                                              float beta, float kce) {
+  float x[8], sg[8], o[8];
+  unpack8(wz, x);
+  unpack8_f16(ws, sg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
+  if ((unsigned)rel < 8u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+  }
+  return pack8(o);
 }
 
 // Lanes [0, n) of wave 0 poll slots sl[0..n) until none is empty (or the
@@ -189,13 +270,17 @@ __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* 
 // outputs; the other members leave.
 // FUSED = true: the forward and the student gradient of the "Backward Pass"
 // section, g = p * (alpha + beta * s) - k * g_ce * [v == t], in the same pass
-// (the loss's upstream gradients are known up front).  Step 2 keeps the signs
-// s = sign(p - q), which are -1, 0 or 1 and so exact in bf16, in the
-// registers that held the teacher's logits; every member waits for the K
-// step-2 pairs, so all of them hold the same sigma, then step 3 recomputes p
-// from the student's logits and stores the gradient of its chunk.  Each member
-// has read its whole chunk, and member 0 the target logit, before any member
-// stores, so the gradient may overwrite the student logits.
+// (the loss's upstream gradients are known up front).  Step 2 keeps, as fp16,
+// 2^15 * p in the registers that held the student's logits and the signs
+// s = sign(p - q) in those that held the teacher's; every member waits for
+// the K step-2 pairs, so all of them hold the same sigma, then step 3 forms
+// the gradient of its chunk with two mixed-precision multiply-adds per
+// element (the target element from its logit, in fp32); where the gradient's
+// scale puts an element beyond what fp16 p allows (kKeepP16Bound), its group
+// is formed from p recomputed out of the student logits, read again.
+// Each member has read its whole chunk, and the member holding the target its
+// logit, before any member stores, so the gradient may overwrite the student
+// logits.
 template <int NT, int G, int GL, int WPE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
 void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
@@ -242,8 +327,13 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   const int n = tid < cnt ? min(G, (cnt - tid - 1) / NT + 1) : 0;
   const int nl = NT * G + tid < cnt ? min(GL, (cnt - NT * G - tid - 1) / NT + 1) : 0;
   const bool t_ok = t >= 0 && t < V;
+  // the member whose chunk holds the target (member 0 if it is out of range)
+  // reads its logit and, in the one-pass kernel, writes the row's outputs
+  const int jt = t_ok ? (int)(t >> 3) / gpm : 0;
   float zt = 0.f;
-  if (FUSED && j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
+  if (FUSED && j == jt && tid == 0 && t_ok) zt = load1(student + row + t);
+
+
   const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
   const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
   u32x4_t rz[G], ru[G];
@@ -373,32 +463,35 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   __syncthreads();
   const float lse_s = s_bc[0], lse_t = s_bc[1];
 
-  // ---- step 2 over the kept chunk (FUSED: the signs replace the teacher's logits)
+  // ---- step 2 over the kept chunk, probabilities scaled by 2^kPScale
+  // (FUSED: p and the signs replace the logits)
   const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
   {
+    const float nbs2 = nbs + kPScale, nbt2 = nbt + kPScale;
     float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       if (i < n) {
         launder(rz[i]);
         launder(ru[i]);
-        if (FUSED) tv8_signs(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
-        else tv8(rz[i], ru[i], nbs, nbt, A0, A1, S0, S1);
+        if (FUSED) tv8_signs(rz[i], ru[i], nbs2, nbt2, A0, A1, S0, S1);
+        else tv8(rz[i], ru[i], nbs2, nbt2, A0, A1, S0, S1);
       }
     }
 #pragma unroll
     for (int i = 0; i < GL; ++i) {
       if (i < nl) {
-        u32x4_t wu = lu[tid + i * NT];
+        u32x4_t wz = lz[tid + i * NT], wu = lu[tid + i * NT];
         if (FUSED) {
-          tv8_signs(lz[tid + i * NT], wu, nbs, nbt, A0, A1, S0, S1);
-          lu[tid + i * NT] = wu;  // this thread's own slot: read back by it in step 3
+          tv8_signs(wz, wu, nbs2, nbt2, A0, A1, S0, S1);
+          lz[tid + i * NT] = wz;  // this thread's own slots: read back by it in step 3
+          lu[tid + i * NT] = wu;
         } else {
-          tv8(lz[tid + i * NT], wu, nbs, nbt, A0, A1, S0, S1);
+          tv8(wz, wu, nbs2, nbt2, A0, A1, S0, S1);
         }
       }
     }
-    const float A = wave_sum(A0 + A1), S = wave_sum(S0 + S1);
+    const float A = wave_sum(A0 + A1) * kInvPScale, S = wave_sum(S0 + S1) * kInvPScale;
     if ((tid & 63) == 0) {
       red_a[tid >> 6] = A;
       red_s[tid >> 6] = S;
@@ -458,7 +551,7 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       S += hi_f(got[k]);
     }
     s_bc[2] = S;
-    if (j == 0) {
+    if (j == jt) {
       if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
       tvd[r] = 0.5f * A;
       lse_s_out[r] = lse_s;
@@ -473,39 +566,59 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   const float kce = k * g_ce;
   const float beta = 0.5f * k * g_tvd;
   const float alpha = kce - beta * s_bc[2];
+  const float a15 = alpha * kInvPScale, b15 = beta * kInvPScale;
   const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
-  const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
+  // target element relative to the chunk; only the member holding it reads pt
+  const int trel = j == jt ? (int)(t - 8 * (int64_t)gb) : -1;
+  if (!t_ok) {
+    // a target outside [0, V) makes the row's gradient NaN
+#pragma unroll
+    for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, nan8());
+    return;
+  }
+  const float pt = prob(s_zt, nbs);
+  float zero = 0.f;
+  asm volatile("" : "+v"(zero));
+  const float M = k * (fabsf(g_ce) + fabsf(g_tvd));
+  if (!(M <= kKeepP16Bound)) {
+    // A group holding a 2^kPScale * p above thr (p > kKeepP16Bound / M, less
+    // a margin for the fp16 roundings) is formed from its logits, loaded
+    // again: the thread loads the group before it stores the group's
+    // gradient, and no other member touches this chunk, so this holds in
+    // place too.
+    const _Float16 thr = (_Float16)(0x1p15f * kKeepP16Bound * (1.0f - 0x1p-9f) / M);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int g = tid + i * NT;
+      launder(rz[i]);
+      launder(ru[i]);
+      const u32x4_t o = any_above(rz[i], thr)
+                            ? grad8_exact(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, alpha, beta, kce)
+                            : grad8(rz[i], ru[i], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce);
+      st_stream(rsg, g * 16, o);
+    }
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      const int g = NT * G + tid + i * NT;
+      const u32x4_t wp = lz[tid + i * NT], ws = lu[tid + i * NT];
+      const u32x4_t o = any_above(wp, thr)
+                            ? grad8_exact(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, alpha, beta, kce)
+                            : grad8(wp, ws, a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce);
+      st_stream(rsg, g * 16, o);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int g = tid + i * NT;
     launder(rz[i]);
     launder(ru[i]);
-    float x[8], sg[8], o[8];
-    unpack8(rz[i], x);
-    unpack8(ru[i], sg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
-    const int rel = trel - 8 * g;
-    if ((unsigned)rel < 8u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
-    }
-    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
+    st_stream(rsg, g * 16, grad8(rz[i], ru[i], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce));
   }
 #pragma unroll
   for (int i = 0; i < GL; ++i) {
     const int g = NT * G + tid + i * NT;
-    float x[8], sg[8], o[8];
-    unpack8(lz[tid + i * NT], x);
-    unpack8(lu[tid + i * NT], sg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
-    const int rel = trel - 8 * g;
-    if ((unsigned)rel < 8u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
-    }
-    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
+    st_stream(rsg, g * 16, grad8(lz[tid + i * NT], lu[tid + i * NT], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce));
   }
 }
 
