@@ -65,21 +65,26 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
       continue;
     }
 
-    const float nbs = neg_scaled(lse_s[r]);
-    const float nbt = TEACHER ? neg_scaled(lse_t[r]) : 0.0f;
+    // with a teacher p' = 2^kPqBias * p and the sign come from the biased
+    // arguments the forward used (sign_eps), so alpha and beta are rescaled:
+    // g = p' * (a' + b' * s') = p * (alpha + beta * sign)
+    const float nbs = TEACHER ? pq_bias(lse_s[r]) : neg_scaled(lse_s[r]);
+    const float nbt = TEACHER ? pq_bias(lse_t[r]) : 0.0f;
     const float kce = k * g_ce;
     const float beta = TEACHER ? 0.5f * k * g_tvd : 0.0f;
     const float alpha = TEACHER ? kce - beta * sigma[r] : kce;
+    const float a1 = TEACHER ? alpha * 0x1p-15f : alpha;
+    const float b1 = beta * kTvScale;
+    static_assert(kPqBias == 15.0f, "a1 undoes the bias");
 
     for (int i = s0 + tid; i < s1; i += NT) {
       const int e = scalar_elem(L, i);
-      const float p = prob(load1(z + e), nbs);
+      const float ap = exparg(load1(z + e), nbs);
       float gv;
       if (TEACHER) {
-        const float q = prob(load1(u + e), nbt);
-        gv = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+        gv = exp2_hw(ap) * __builtin_fmaf(sign_eps(ap, exparg(load1(u + e), nbt)), b1, a1);
       } else {
-        gv = p * alpha;
+        gv = exp2_hw(ap) * a1;
       }
       if (e == t) gv -= kce;
       store1(gr + e, gv);
@@ -94,12 +99,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
         if (TEACHER) load8_stream(ub + 8 * g, y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = prob(x[e], nbs);
+          const float ap = exparg(x[e], nbs);
           if (TEACHER) {
-            const float q = prob(y[e], nbt);
-            o[e] = p * __builtin_fmaf(sign0(p - q), beta, alpha);
+            o[e] = exp2_hw(ap) * __builtin_fmaf(sign_eps(ap, exparg(y[e], nbt)), b1, a1);
           } else {
-            o[e] = p * alpha;
+            o[e] = exp2_hw(ap) * a1;
           }
         }
         const int rel = (int)(t - (int64_t)(L.head + 8 * g));

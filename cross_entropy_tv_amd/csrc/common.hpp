@@ -8,9 +8,17 @@
 //   * running maxima start at kMFloor, a finite floor, so every rescale factor
 //     exp2((m_old - m_new) * log2 e) is finite (no inf - inf) even for rows
 //     holding -inf entries;
-//   * sign(p - q) with sign(0) = 0 is med3(d * 2^126, -1, 1): exact for every
-//     d that is 0 or at least 2^-126 in magnitude; p - q is never a nonzero
-//     number below that unless both p and q are below 2^-103.
+//   * the total variation forms p and q scaled by 2^15 (the exponent bias
+//     raised by 15, pq_bias) from the arguments a = fma(x, log2 e, bias), and
+//     reads sign(p - q) off the arguments: p - q has the sign of a_p - a_q
+//     wherever fp32 resolves the two (elsewhere |p / q - 1| is a few 2^-20, a
+//     near tie), and med3(a_p - a_q, -2^-24, 2^-24) is 2^-24 * sign, with
+//     sign 0 exactly when the arguments are equal, and a fraction of 2^-24
+//     only where |a_p - a_q| < 2^-24 (|p / q - 1| < 4e-8).  The forward sums
+//     S = sum p s and Q = sum q s, so sum |p - q| = S - Q; the backward needs
+//     no q at all.  Forward and backward form the arguments from the same
+//     stored lse with the same instructions, so sigma and the backward's
+//     signs agree element for element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -121,11 +129,19 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // -lse * log2(e): the bias every probability of the row is formed with.
 __device__ __forceinline__ float neg_scaled(float lse) { return -(lse * kLog2e); }
 
-// exp(x - lse) given nb = neg_scaled(lse).
-__device__ __forceinline__ float prob(float x, float nb) { return exp2_hw(__builtin_fmaf(x, kLog2e, nb)); }
 
-// sign(d) with sign(0) = 0 (see header comment).
-__device__ __forceinline__ float sign0(float d) { return __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.0f, 1.0f); }
+// Total-variation arguments (see the header comment): p' = exp2(exparg(x,
+// pq_bias(lse))) = 2^kPqBias * exp(x - lse), and sign_eps(a_p, a_q) =
+// kSignEps * sign(p - q).  Sums of p' * sign_eps come back to sums of
+// p * sign with the factor kTvScale.
+constexpr float kPqBias = 15.0f;
+constexpr float kSignEps = 0x1p-24f;
+constexpr float kTvScale = 0x1p9f;  // 2^24 * 2^-15
+__device__ __forceinline__ float pq_bias(float lse) { return neg_scaled(lse) + kPqBias; }
+__device__ __forceinline__ float exparg(float x, float nb) { return __builtin_fmaf(x, kLog2e, nb); }
+__device__ __forceinline__ float sign_eps(float ap, float aq) {
+  return __builtin_amdgcn_fmed3f(ap - aq, -kSignEps, kSignEps);
+}
 
 __device__ __forceinline__ float max8(const float (&x)[8]) {
   return fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -169,13 +185,17 @@ __device__ __forceinline__ float lse_value(const Lse& a) { return a.m + logf(a.s
 
 // ------------------------------------------------------------------ wave / block reductions
 
+// The wave's (max, sum-exp): the maximum first, then each lane's sum rescaled
+// to it once and the sums added (one exponential per lane instead of two per
+// butterfly step).  Every lane ends with the same pair.
 __device__ __forceinline__ Lse wave_lse(Lse a) {
+  float m = a.m;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Lse b{__shfl_xor(a.m, off, 64), __shfl_xor(a.s, off, 64)};
-    lse_merge(a, b);
-  }
-  return a;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float s = a.s * exp2_hw((a.m - m) * kLog2e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return Lse{m, s};
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -77,26 +77,28 @@ __device__ __forceinline__ float block_sum_t0(float v, float* red) {
   return f;  // valid in thread 0
 }
 
-// step-2 accumulation for one group of 8
+// step-2 accumulation for one group of 8, nbs and nbt from pq_bias:
+// S += p' * s' and Q += q' * s' (s' = sign_eps), so that, scaled by
+// kTvScale, S is sum p * sign and S - Q is sum |p - q|
 __device__ __forceinline__ void tv_add8(const float (&x)[8], const float (&y)[8], float nbs, float nbt,
-                                        float& A0, float& A1, float& S0, float& S1) {
+                                        float& Q0, float& Q1, float& S0, float& S1) {
 #pragma unroll
   for (int k = 0; k < 8; k += 2) {
-    const float p0 = prob(x[k], nbs), q0 = prob(y[k], nbt);
-    const float p1 = prob(x[k + 1], nbs), q1 = prob(y[k + 1], nbt);
-    const float d0 = p0 - q0, d1 = p1 - q1;
-    A0 += fabsf(d0);
-    A1 += fabsf(d1);
-    S0 = __builtin_fmaf(p0, sign0(d0), S0);
-    S1 = __builtin_fmaf(p1, sign0(d1), S1);
+    const float ap0 = exparg(x[k], nbs), aq0 = exparg(y[k], nbt);
+    const float ap1 = exparg(x[k + 1], nbs), aq1 = exparg(y[k + 1], nbt);
+    const float s0 = sign_eps(ap0, aq0), s1 = sign_eps(ap1, aq1);
+    S0 = __builtin_fmaf(exp2_hw(ap0), s0, S0);
+    Q0 = __builtin_fmaf(exp2_hw(aq0), s0, Q0);
+    S1 = __builtin_fmaf(exp2_hw(ap1), s1, S1);
+    Q1 = __builtin_fmaf(exp2_hw(aq1), s1, Q1);
   }
 }
 
-__device__ __forceinline__ void tv_add1(float x, float y, float nbs, float nbt, float& A, float& S) {
-  const float p = prob(x, nbs), q = prob(y, nbt);
-  const float d = p - q;
-  A += fabsf(d);
-  S = __builtin_fmaf(p, sign0(d), S);
+__device__ __forceinline__ void tv_add1(float x, float y, float nbs, float nbt, float& Q, float& S) {
+  const float ap = exparg(x, nbs), aq = exparg(y, nbt);
+  const float s = sign_eps(ap, aq);
+  S = __builtin_fmaf(exp2_hw(ap), s, S);
+  Q = __builtin_fmaf(exp2_hw(aq), s, Q);
 }
 
 // ce = lse_s - z[t]; a target outside [0, V) stores NaN (as bits)
@@ -184,11 +186,11 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
     }
 
     // ---- step 2: total variation and sigma, walking the groups backwards
-    const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
-    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+    const float nbs = pq_bias(lse_s), nbt = pq_bias(lse_t);
+    float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
     for (int i = tid; i < nsc; i += NT) {
       const int e = scalar_elem(L, i);
-      tv_add1(load1(z + e), load1(u + e), nbs, nbt, A0, S0);
+      tv_add1(load1(z + e), load1(u + e), nbs, nbt, Q0, S0);
     }
     if (tid < L.groups) {
       int gl = tid + ((L.groups - 1 - tid) / NT) * NT;  // this thread's last group
@@ -198,24 +200,24 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
         load8(zb + 8 * (gl - NT), x1);
         load8(ub + 8 * gl, y0);
         load8(ub + 8 * (gl - NT), y1);
-        tv_add8(x0, y0, nbs, nbt, A0, A1, S0, S1);
-        tv_add8(x1, y1, nbs, nbt, A0, A1, S0, S1);
+        tv_add8(x0, y0, nbs, nbt, Q0, Q1, S0, S1);
+        tv_add8(x1, y1, nbs, nbt, Q0, Q1, S0, S1);
       }
       if (gl >= 0) {
         float x0[8], y0[8];
         load8(zb + 8 * gl, x0);
         load8(ub + 8 * gl, y0);
-        tv_add8(x0, y0, nbs, nbt, A0, A1, S0, S1);
+        tv_add8(x0, y0, nbs, nbt, Q0, Q1, S0, S1);
       }
     }
-    const float A = block_sum_t0<NT>(A0 + A1, red_f[0]);
+    const float Q = block_sum_t0<NT>(Q0 + Q1, red_f[0]);
     const float S = block_sum_t0<NT>(S0 + S1, red_f[1]);
     if (tid == 0) {
       store_ce(ce + r, z, t, V, lse_s);
-      tvd[r] = 0.5f * A;
+      tvd[r] = 0.5f * ((S - Q) * kTvScale);
       lse_s_out[r] = lse_s;
       lse_t_out[r] = lse_t;
-      sigma_out[r] = S;
+      sigma_out[r] = S * kTvScale;
     }
     __syncthreads();  // shared buffers are reused by the next row
   }
@@ -329,11 +331,11 @@ __global__ __launch_bounds__(NT) void fwd_split_stage2(
     const T* u = teacher + r * (int64_t)V;
     const RowLayout L = row_layout(z, V, vec);
     const ChunkRange R = chunk_range(L, c, S);
-    const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
-    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+    const float nbs = pq_bias(lse_s), nbt = pq_bias(lse_t);
+    float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
     for (int i = R.s0 + tid; i < R.s1; i += NT) {
       const int e = scalar_elem(L, i);
-      tv_add1(load1(z + e), load1(u + e), nbs, nbt, A0, S0);
+      tv_add1(load1(z + e), load1(u + e), nbs, nbt, Q0, S0);
     }
     const T* zb = z + L.head;
     const T* ub = u + L.head;
@@ -341,13 +343,13 @@ __global__ __launch_bounds__(NT) void fwd_split_stage2(
       float x[8], y[8];
       load8(zb + 8 * g, x);
       load8(ub + 8 * g, y);
-      tv_add8(x, y, nbs, nbt, A0, A1, S0, S1);
+      tv_add8(x, y, nbs, nbt, Q0, Q1, S0, S1);
     }
-    const float A = block_sum_t0<NT>(A0 + A1, red_f[0]);
+    const float Q = block_sum_t0<NT>(Q0 + Q1, red_f[0]);
     const float Sg = block_sum_t0<NT>(S0 + S1, red_f[1]);
     if (tid == 0) {
-      ws2[tile * 2 + 0] = A;
-      ws2[tile * 2 + 1] = Sg;
+      ws2[tile * 2 + 0] = (Sg - Q) * kTvScale;  // this chunk's sum |p - q|
+      ws2[tile * 2 + 1] = Sg * kTvScale;        // and sum p * sign
     }
     __syncthreads();
   }

@@ -104,21 +104,23 @@ __device__ __forceinline__ void expsum8(const u32x4_t& w, float nb, float& s0, f
   }
 }
 
-// step-2 accumulation of one group pair: |p - q| and p * sign(p - q)
-__device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float nbs, float nbt, float& A0,
-                                    float& A1, float& S0, float& S1) {
+// step-2 accumulation of one group pair (nbs, nbt from pq_bias): S += p' s'
+// and Q += q' s', so that, times kTvScale, S is sum p * sign(p - q) and
+// S - Q is sum |p - q|
+__device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float nbs, float nbt, float& Q0,
+                                    float& Q1, float& S0, float& S1) {
   float x[8], y[8];
   unpack8(wz, x);
   unpack8(wu, y);
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    const float p0 = prob(x[e], nbs), q0 = prob(y[e], nbt);
-    const float p1 = prob(x[e + 1], nbs), q1 = prob(y[e + 1], nbt);
-    const float d0 = p0 - q0, d1 = p1 - q1;
-    A0 += fabsf(d0);
-    A1 += fabsf(d1);
-    S0 = __builtin_fmaf(p0, sign0(d0), S0);
-    S1 = __builtin_fmaf(p1, sign0(d1), S1);
+    const float ap0 = exparg(x[e], nbs), aq0 = exparg(y[e], nbt);
+    const float ap1 = exparg(x[e + 1], nbs), aq1 = exparg(y[e + 1], nbt);
+    const float s0 = sign_eps(ap0, aq0), s1 = sign_eps(ap1, aq1);
+    S0 = __builtin_fmaf(exp2_hw(ap0), s0, S0);
+    Q0 = __builtin_fmaf(exp2_hw(aq0), s0, Q0);
+    S1 = __builtin_fmaf(exp2_hw(ap1), s1, S1);
+    Q1 = __builtin_fmaf(exp2_hw(aq1), s1, Q1);
   }
 }
 
@@ -136,12 +138,11 @@ __device__ __forceinline__ void unpack8_f16(const u32x4_t& w, float (&x)[8]) {
   x[4] = (float)c.x; x[5] = (float)c.y; x[6] = (float)d.x; x[7] = (float)d.y;
 }
 
-// Step 2 forms every probability scaled by 2^kPScale (the exponent bias is
-// raised by kPScale): the sums come back to scale with an exact power-of-two
-// multiply, and the one-pass kernel can keep 2^kPScale * p in fp16 for step 3,
-// normal down to p = 2^-29 and below 32768 for p <= 1.
-constexpr float kPScale = 15.0f;
-constexpr float kInvPScale = 0x1p-15f;
+// The one-pass kernel keeps p' = 2^kPqBias * p in fp16 for step 3: normal
+// down to p = 2^-29 and below 32768 for p <= 1.  The signs s' = 2^-24 * sign
+// are exact in fp16 too (its least subnormal).
+static_assert(kPqBias == 15.0f && kSignEps == 0x1p-24f, "fp16 ranges of p' and s'");
+constexpr float kInvPqBias = 0x1p-15f;
 
 // fp16 p is good enough for the gradient only while its error stays inside
 // the absolute part of the gradient's bound (2^-8 relative + 1e-6).  With
@@ -157,31 +158,32 @@ constexpr float kInvPScale = 0x1p-15f;
 constexpr float kKeepP16Bound = 2.08e-3f;
 
 // As tv8, and keeps what step 3 needs in place of the two groups' logits:
-// 2^kPScale * p in wz and the signs in wu, both as fp16 (-1, 0 and 1 are
-// exact).  nbs and nbt carry the kPScale bias.
-__device__ __forceinline__ void tv8_signs(u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& A0, float& A1,
+// p' in wz and s' in wu, both as fp16, one 32-bit word (two elements) at a
+// time so that few values are live at once.
+__device__ __forceinline__ void tv2_signs(unsigned& zw, unsigned& uw, float nbs, float nbt, float& Q0, float& Q1,
                                           float& S0, float& S1) {
-  float x[8], y[8], p[8], sg[8];
-  unpack8(wz, x);
-  unpack8(wu, y);
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    p[e] = prob(x[e], nbs);
-    p[e + 1] = prob(x[e + 1], nbs);
-    const float q0 = prob(y[e], nbt), q1 = prob(y[e + 1], nbt);
-    const float d0 = p[e] - q0, d1 = p[e + 1] - q1;
-    sg[e] = sign0(d0);
-    sg[e + 1] = sign0(d1);
-    A0 += fabsf(d0);
-    A1 += fabsf(d1);
-    S0 = __builtin_fmaf(p[e], sg[e], S0);
-    S1 = __builtin_fmaf(p[e + 1], sg[e + 1], S1);
-  }
-  wz = (u32x4_t){pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
-  wu = (u32x4_t){pack_f16x2(sg[0], sg[1]), pack_f16x2(sg[2], sg[3]), pack_f16x2(sg[4], sg[5]),
-                 pack_f16x2(sg[6], sg[7])};
+  const float ap0 = exparg(__uint_as_float(zw << 16), nbs), ap1 = exparg(__uint_as_float(zw & 0xffff0000u), nbs);
+  const float aq0 = exparg(__uint_as_float(uw << 16), nbt), aq1 = exparg(__uint_as_float(uw & 0xffff0000u), nbt);
+  const float s0 = sign_eps(ap0, aq0), s1 = sign_eps(ap1, aq1);
+  const float p0 = exp2_hw(ap0), p1 = exp2_hw(ap1);
+  S0 = __builtin_fmaf(p0, s0, S0);
+  Q0 = __builtin_fmaf(exp2_hw(aq0), s0, Q0);
+  S1 = __builtin_fmaf(p1, s1, S1);
+  Q1 = __builtin_fmaf(exp2_hw(aq1), s1, Q1);
+  zw = pack_f16x2(p0, p1);
+  uw = pack_f16x2(s0, s1);
 }
-
+__device__ __forceinline__ void tv8_signs(u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& Q0, float& Q1,
+                                          float& S0, float& S1) {
+  unsigned z0 = wz.x, z1 = wz.y, z2 = wz.z, z3 = wz.w;
+  unsigned u0 = wu.x, u1 = wu.y, u2 = wu.z, u3 = wu.w;
+  tv2_signs(z0, u0, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs(z1, u1, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs(z2, u2, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs(z3, u3, nbs, nbt, Q0, Q1, S0, S1);
+  wz = (u32x4_t){z0, z1, z2, z3};
+  wu = (u32x4_t){u0, u1, u2, u3};
+}
 
 // eight gradients rounded to bf16 (nearest even), and eight bf16 quiet NaNs
 __device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
@@ -193,23 +195,24 @@ __device__ __forceinline__ u32x4_t nan8() {
   return (u32x4_t){h, h, h, h};
 }
 
-// Step 3 over one group: g = p * (alpha + beta * s) from the fp16 pair kept by
-// tv8_signs (a15, b15 are alpha and beta times 2^-kPScale), and at the target
-// element (rel in [0, 8)) g = pt * (alpha + beta * s) - kce with pt in fp32:
-// there p may be close to 1 and the difference small.  zero is +0 hidden from
+// Step 3 over one group: g = p * (alpha + beta * sign) = p' * (a1 + b1 * s')
+// from the fp16 pair kept by tv8_signs (a1 = alpha / 2^kPqBias, b1 = beta *
+// kTvScale), and at the target element (rel in [0, 8)) g = pt' * (a1 + b1 *
+// s') - kce with pt' in fp32: there p may be close to 1 and the difference
+// small.  zero is +0 hidden from
 // the optimiser: p * t + zero is the product (a zero product comes out +0)
 // but, unlike p * t, maps to one mixed-precision multiply-add that reads the
 // fp16 half directly.
-__device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, float a15, float b15, float zero,
-                                        int rel, float pt, float alpha, float beta, float kce) {
+__device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, float a1, float b1, float zero,
+                                        int rel, float pt, float kce) {
   float p[8], sg[8], o[8];
   unpack8_f16(wp, p);
   unpack8_f16(ws, sg);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p[e], __builtin_fmaf(sg[e], b15, a15), zero);
+  for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p[e], __builtin_fmaf(sg[e], b1, a1), zero);
   if ((unsigned)rel < 8u) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], beta, alpha) - kce : o[e];
+    for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], b1, a1) - kce : o[e];
   }
   return pack8(o);
 }
@@ -222,15 +225,15 @@ __device__ __forceinline__ bool any_above(const u32x4_t& w, _Float16 thr) {
   return m.x > thr || m.y > thr;
 }
 
-// As grad8 with p recomputed in fp32 from the student's bf16 logits wz (nbs
-// without the kPScale bias), so the target element needs only - kce.
-__device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t& ws, float nbs, int rel, float alpha,
-                                              float beta, float kce) {
+// As grad8 with p' recomputed in fp32 from the student's bf16 logits wz (nbs
+// from pq_bias), so the target element needs only - kce.
+__device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t& ws, float nbs, int rel, float a1,
+                                              float b1, float kce) {
   float x[8], sg[8], o[8];
   unpack8(wz, x);
   unpack8_f16(ws, sg);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = prob(x[e], nbs) * __builtin_fmaf(sg[e], beta, alpha);
+  for (int e = 0; e < 8; ++e) o[e] = exp2_hw(exparg(x[e], nbs)) * __builtin_fmaf(sg[e], b1, a1);
   if ((unsigned)rel < 8u) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
@@ -463,19 +466,17 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   __syncthreads();
   const float lse_s = s_bc[0], lse_t = s_bc[1];
 
-  // ---- step 2 over the kept chunk, probabilities scaled by 2^kPScale
-  // (FUSED: p and the signs replace the logits)
-  const float nbs = neg_scaled(lse_s), nbt = neg_scaled(lse_t);
+  // ---- step 2 over the kept chunk (FUSED: p' and s' replace the logits)
+  const float nbs = pq_bias(lse_s), nbt = pq_bias(lse_t);
   {
-    const float nbs2 = nbs + kPScale, nbt2 = nbt + kPScale;
-    float A0 = 0.f, A1 = 0.f, S0 = 0.f, S1 = 0.f;
+    float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       if (i < n) {
         launder(rz[i]);
         launder(ru[i]);
-        if (FUSED) tv8_signs(rz[i], ru[i], nbs2, nbt2, A0, A1, S0, S1);
-        else tv8(rz[i], ru[i], nbs2, nbt2, A0, A1, S0, S1);
+        if (FUSED) tv8_signs(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
+        else tv8(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
       }
     }
 #pragma unroll
@@ -483,18 +484,20 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       if (i < nl) {
         u32x4_t wz = lz[tid + i * NT], wu = lu[tid + i * NT];
         if (FUSED) {
-          tv8_signs(wz, wu, nbs2, nbt2, A0, A1, S0, S1);
+          tv8_signs(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
           lz[tid + i * NT] = wz;  // this thread's own slots: read back by it in step 3
           lu[tid + i * NT] = wu;
         } else {
-          tv8(wz, wu, nbs2, nbt2, A0, A1, S0, S1);
+          tv8(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
         }
       }
     }
-    const float A = wave_sum(A0 + A1) * kInvPScale, S = wave_sum(S0 + S1) * kInvPScale;
+    // this wave's sum |p - q| = (S - Q) * kTvScale and sum p * sign = S * kTvScale
+    const float Q = wave_sum(Q0 + Q1), S = wave_sum(S0 + S1);
+    const float A = (S - Q) * kTvScale;
     if ((tid & 63) == 0) {
       red_a[tid >> 6] = A;
-      red_s[tid >> 6] = S;
+      red_s[tid >> 6] = S * kTvScale;
     }
   }
   __syncthreads();
@@ -561,12 +564,13 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   }
   __syncthreads();
 
-  // ---- step 3: g = p * (alpha + beta * s) - k * g_ce * [v == t]
+  // ---- step 3: g = p * (alpha + beta * sign) - k * g_ce * [v == t]
+  //             = p' * (a1 + b1 * s') - k * g_ce * [v == t]
   const float k = g_scale ? *g_scale : 1.0f;
   const float kce = k * g_ce;
   const float beta = 0.5f * k * g_tvd;
   const float alpha = kce - beta * s_bc[2];
-  const float a15 = alpha * kInvPScale, b15 = beta * kInvPScale;
+  const float a1 = alpha * kInvPqBias, b1 = beta * kTvScale;
   const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
   // target element relative to the chunk; only the member holding it reads pt
   const int trel = j == jt ? (int)(t - 8 * (int64_t)gb) : -1;
@@ -576,12 +580,12 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, nan8());
     return;
   }
-  const float pt = prob(s_zt, nbs);
+  const float pt = exp2_hw(exparg(s_zt, nbs));
   float zero = 0.f;
   asm volatile("" : "+v"(zero));
   const float M = k * (fabsf(g_ce) + fabsf(g_tvd));
   if (!(M <= kKeepP16Bound)) {
-    // A group holding a 2^kPScale * p above thr (p > kKeepP16Bound / M, less
+    // A group holding a p' = 2^kPqBias * p above thr (p > kKeepP16Bound / M, less
     // a margin for the fp16 roundings) is formed from its logits, loaded
     // again: the thread loads the group before it stores the group's
     // gradient, and no other member touches this chunk, so this holds in
@@ -593,8 +597,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       launder(rz[i]);
       launder(ru[i]);
       const u32x4_t o = any_above(rz[i], thr)
-                            ? grad8_exact(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, alpha, beta, kce)
-                            : grad8(rz[i], ru[i], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce);
+                            ? grad8_exact(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, a1, b1, kce)
+                            : grad8(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce);
       st_stream(rsg, g * 16, o);
     }
 #pragma unroll
@@ -602,8 +606,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       const int g = NT * G + tid + i * NT;
       const u32x4_t wp = lz[tid + i * NT], ws = lu[tid + i * NT];
       const u32x4_t o = any_above(wp, thr)
-                            ? grad8_exact(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, alpha, beta, kce)
-                            : grad8(wp, ws, a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce);
+                            ? grad8_exact(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, a1, b1, kce)
+                            : grad8(wp, ws, a1, b1, zero, trel - 8 * g, pt, kce);
       st_stream(rsg, g * 16, o);
     }
     return;
@@ -613,12 +617,12 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     const int g = tid + i * NT;
     launder(rz[i]);
     launder(ru[i]);
-    st_stream(rsg, g * 16, grad8(rz[i], ru[i], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce));
+    st_stream(rsg, g * 16, grad8(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce));
   }
 #pragma unroll
   for (int i = 0; i < GL; ++i) {
     const int g = NT * G + tid + i * NT;
-    st_stream(rsg, g * 16, grad8(lz[tid + i * NT], lu[tid + i * NT], a15, b15, zero, trel - 8 * g, pt, alpha, beta, kce));
+    st_stream(rsg, g * 16, grad8(lz[tid + i * NT], lu[tid + i * NT], a1, b1, zero, trel - 8 * g, pt, kce));
   }
 }
 
@@ -764,21 +768,23 @@ __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restri
 
 // Read-once kernel: NT threads x (G in registers + GL in LDS) groups of bf16
 // logits per thread and tensor, WPE waves per SIMD (three 256-thread
-// workgroups per compute unit, 24 KB of LDS each).  Measured on the 8192 x
-// 151936 training batch (forward / one pass): 256 x (16 + 3) x 3 (K = 4)
-// 0.985 / 1.41 ms; 256 x (13 + 6) x 3 (K = 4) 0.984 / 1.41; 256 x (11 + 4) x 4
+// workgroups per compute unit, 33 KB of LDS each).  15 + 4 rather than 16 + 3
+// leaves the one-pass kernel's step 2 enough registers not to spill (the two
+// run at the same speed otherwise).  Measured on the 8192 x 151936 training
+// batch (forward / one pass), before the one pass kept p in fp16:
+// 256 x (16 + 3) x 3 (K = 4) 0.985 / 1.41 ms; 256 x (13 + 6) x 3 (K = 4) 0.984 / 1.41; 256 x (11 + 4) x 4
 // (K = 5) 0.995 / 1.42; 256 x 16 x 3 without LDS (K = 5) 1.02 / 1.46; 256 x
 // (24 + 2) x 2 (K = 3) 1.09 / 1.61; 256 x 10 x 4 (K = 8) 1.06 / -; 512 x 10 x
 // 4 (K = 4) 1.14 / -; 384 and 768 threads (K = 4, 2) 1.76 / 2.52, 1.27 / 1.99.
 constexpr int kClThreads = 256;
-constexpr int kClGroups = 16;
-constexpr int kClLdsGroups = 3;
+constexpr int kClGroups = 15;
+constexpr int kClLdsGroups = 4;
 constexpr int kClWavesPerSimd = 3;
 // One-pass forward + backward.  With a teacher it is the forward's kernel
-// (FUSED), chunked the same way; measured on the training batch, 1.48 ms
-// against 1.68 ms for a variant that keeps fp32 exponentials (twice the
-// registers per element, so K = 10 members per row instead of 5, and each
-// row waits on its slowest member twice).  CE-only keeps exponentials of
+// (FUSED), chunked the same way; measured on the training batch (then with
+// K = 5), 1.48 ms against 1.68 ms for a variant that keeps fp32 exponentials
+// (twice the registers per element, so K = 10 members per row, and each row
+// waits on its slowest member twice).  CE-only keeps exponentials of
 // one tensor (fused_ce_kernel), 16 groups per thread.
 constexpr int kFusedCeThreads = 256;
 constexpr int kFusedCeGroups = 16;
