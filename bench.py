@@ -162,6 +162,71 @@ def run_fused(w, zs, us, tg, n_valid, steps, warmup, teacher=True):
             "mean": mean.cpu().tolist()}
 
 
+def run_vocab_parallel(w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
+    """The per-device passes of an n_shards-way vocabulary-parallel layout at its real
+    shape: one device's column shard (BT, V / n_shards) of the same logits.  One step =
+    step-1 partials -> merge of the n_shards gathered partials -> step-2 partials ->
+    merge -> backward of the shard (the exchanges between devices are not run here)."""
+    import torch
+    import cross_entropy_tv_amd as lx
+
+    BT, V = w.BT, w.V
+    Vs = V // n_shards
+    dev = zs.device
+    zsh, ush = zs[:, :Vs].contiguous(), us[:, :Vs].contiguous()
+    stats = torch.empty((n_shards, BT, 5), dtype=torch.float32, device=dev)
+    tv = torch.empty((n_shards, BT, 2), dtype=torch.float32, device=dev)
+    f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
+    ce, lse_s, lse_t, tvd, sigma = f(), f(), f(), f(), f()
+    inv = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty_like(zsh)
+    stream = torch.cuda.current_stream()
+    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
+    for n in range(n_shards):  # stand-ins for the other devices' partials
+        lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, -100, stats[n], stream)
+    lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, -100, ce, lse_s, lse_t, stream)
+    for n in range(n_shards):
+        lx.lx_ce_tvd_vp_tv(zsh, ush, tg, -100, lse_s, lse_t, tv[n], stream)
+
+    def step(ev=None):
+        calls = (lambda: lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, -100, stats[0], stream),
+                 lambda: lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, -100, ce, lse_s, lse_t, stream),
+                 lambda: lx.lx_ce_tvd_vp_tv(zsh, ush, tg, -100, lse_s, lse_t, tv[0], stream),
+                 lambda: lx.lx_ce_tvd_vp_merge_tv(tv, tg, -100, tvd, sigma, stream),
+                 lambda: lx.lx_ce_tvd_backward_shard(grad, zsh, ush, tg, 0, V, -100, lse_s, lse_t, sigma, 1.0,
+                                                     1.0, inv, stream))
+        for k, c in enumerate(calls):
+            if ev is not None:
+                ev[k].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(5)]
+    n_ign = BT - n_valid
+    es = w.esize
+    alg = {"stats": n_valid * 2 * Vs * es + BT * 8 + BT * 20,
+           "merge_stats": BT * (8 + n_shards * 20 + 12),
+           "tv": n_valid * 2 * Vs * es + BT * (8 + 8 + 8),
+           "merge_tv": BT * (8 + n_shards * 8 + 8),
+           "backward": n_valid * 3 * Vs * es + n_ign * Vs * es + BT * (8 + 12) + 4}
+    out = {"shard": f"{BT}x{Vs} {w.dtype} (1 of {n_shards} column shards)"}
+    for (name, b), t in zip(alg.items(), ms):
+        out[f"{name}_ms"] = round(t, 4)
+        out[f"{name}_GBs"] = round(b / t / 1e6, 1)
+        if name in ("stats", "tv", "backward"):
+            out[f"{name}_pct_peak"] = round(100.0 * b / t / 1e6 / HBM_PEAK_GBS, 2)
+    out["device_step_ms"] = round(sum(ms), 4)
+    return out
+
+
 def copy_ceiling(dev, nbytes=2 << 30, reps=10):
     """Achieved GB/s of a plain device copy (read + write), the practical streaming ceiling."""
     import torch
@@ -252,6 +317,7 @@ def main():
     ap.add_argument("--no-ce-only", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-vocab-parallel", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
@@ -295,6 +361,8 @@ def main():
     if teacher and not args.no_fused:
         fu = run_fused(w, zs, us, tg, n_valid, args.steps, args.warmup)
         extra["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in fu.items()}
+    if teacher and not args.no_vocab_parallel and w.V % 8 == 0:
+        extra["vocab_parallel"] = run_vocab_parallel(w, zs, us, tg, n_valid, args.steps, args.warmup)
     if not args.no_ceiling:
         extra["copy_ceiling_GBs"] = copy_ceiling(dev)
 

@@ -66,6 +66,16 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_forward_backward.restype = i32
     L.lx_ce_tvd_count_valid.argtypes = [p, i64, i64, p, p, p]
     L.lx_ce_tvd_count_valid.restype = i32
+    L.lx_ce_tvd_vp_stats.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, p]
+    L.lx_ce_tvd_vp_stats.restype = i32
+    L.lx_ce_tvd_vp_merge_stats.argtypes = [p, i64, p, i64, i64, i64, i32, p, p, p, p]
+    L.lx_ce_tvd_vp_merge_stats.restype = i32
+    L.lx_ce_tvd_vp_tv.argtypes = [p, p, p, i64, i64, i64, p, p, i32, p, p]
+    L.lx_ce_tvd_vp_tv.restype = i32
+    L.lx_ce_tvd_vp_merge_tv.argtypes = [p, i64, p, i64, i64, p, p, p]
+    L.lx_ce_tvd_vp_merge_tv.restype = i32
+    L.lx_ce_tvd_backward_shard.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, p, p, f32, f32, p, i32, p]
+    L.lx_ce_tvd_backward_shard.restype = i32
     return L
 
 
@@ -195,9 +205,64 @@ def lx_ce_tvd_reduce_mean(ce, tvd, target, ignore_index, mean_out, n_valid=None,
            "lx_ce_tvd_reduce_mean")
 
 
+def lx_vp_stats_floats(has_teacher: bool) -> int:
+    return 5 if has_teacher else 3
+
+
+def lx_ce_tvd_vp_stats(student, teacher, target, v0, ignore_index, stats, stream=None) -> None:
+    """Step-1 partials of a column shard (student / teacher (BT, V_shard), the shard's
+    first column v0) into ``stats``, float32 [BT, 5] (CE-only: [BT, 3])."""
+    BT, Vs = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if teacher is not None and (teacher.shape != student.shape or teacher.dtype != student.dtype):
+        raise ValueError("teacher must match student in shape and dtype")
+    _check(lib.lx_ce_tvd_vp_stats(_ptr(student), _ptr(teacher), _ptr(target), BT, Vs, int(v0), int(ignore_index),
+                                  dt, _ptr(stats), _stream(stream)), "lx_ce_tvd_vp_stats")
+
+
+def lx_ce_tvd_vp_merge_stats(stats, target, V, ignore_index, ce, lse_s, lse_t=None, stream=None) -> None:
+    """Merge of gathered step-1 partials, ``stats`` float32 [n_shards, BT, 5 or 3]."""
+    n, BT, P = stats.shape
+    _check(lib.lx_ce_tvd_vp_merge_stats(_ptr(stats), n, _ptr(target), BT, int(V), int(ignore_index), int(P == 5),
+                                        _ptr(ce), _ptr(lse_s), _ptr(lse_t), _stream(stream)),
+           "lx_ce_tvd_vp_merge_stats")
+
+
+def lx_ce_tvd_vp_tv(student, teacher, target, ignore_index, lse_s, lse_t, tv, stream=None) -> None:
+    """Step-2 partials of a column shard into ``tv``, float32 [BT, 2]."""
+    BT, Vs = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if teacher is None or teacher.shape != student.shape or teacher.dtype != student.dtype:
+        raise ValueError("teacher must be given and match student in shape and dtype")
+    _check(lib.lx_ce_tvd_vp_tv(_ptr(student), _ptr(teacher), _ptr(target), BT, Vs, int(ignore_index), _ptr(lse_s),
+                               _ptr(lse_t), dt, _ptr(tv), _stream(stream)), "lx_ce_tvd_vp_tv")
+
+
+def lx_ce_tvd_vp_merge_tv(tv, target, ignore_index, tvd, sigma, stream=None) -> None:
+    """Merge of gathered step-2 partials, ``tv`` float32 [n_shards, BT, 2]."""
+    n, BT, _ = tv.shape
+    _check(lib.lx_ce_tvd_vp_merge_tv(_ptr(tv), n, _ptr(target), BT, int(ignore_index), _ptr(tvd), _ptr(sigma),
+                                     _stream(stream)), "lx_ce_tvd_vp_merge_tv")
+
+
+def lx_ce_tvd_backward_shard(grad, student, teacher, target, v0, V, ignore_index, lse_s, lse_t, sigma,
+                             g_ce: float, g_tvd: float, g_scale=None, stream=None) -> None:
+    """Backward of a column shard (columns [v0, v0 + V_shard) of rows of V)."""
+    BT, Vs = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if grad.shape != student.shape or grad.dtype != student.dtype or not grad.is_contiguous():
+        raise ValueError("grad must match student in shape and dtype and be contiguous")
+    _check(lib.lx_ce_tvd_backward_shard(_ptr(grad), _ptr(student), _ptr(teacher), _ptr(target), BT, Vs, int(v0),
+                                        int(V), int(ignore_index), _ptr(lse_s), _ptr(lse_t), _ptr(sigma),
+                                        float(g_ce), float(g_tvd), _ptr(g_scale), dt, _stream(stream)),
+           "lx_ce_tvd_backward_shard")
+
+
 __all__ = [
     "LxError", "lib", "LIB_PATH", "LX_OK", "LX_ERR_INVALID_ARG", "LX_ERR_UNSUPPORTED_DTYPE", "LX_ERR_ALIAS",
     "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "lx_status_string", "lx_abi_version",
     "lx_ce_tvd_workspace_bytes", "lx_ce_tvd_forward", "lx_ce_tvd_backward", "lx_ce_tvd_reduce_mean",
     "lx_ce_tvd_forward_backward_workspace_bytes", "lx_ce_tvd_forward_backward", "lx_ce_tvd_count_valid",
+    "lx_vp_stats_floats", "lx_ce_tvd_vp_stats", "lx_ce_tvd_vp_merge_stats", "lx_ce_tvd_vp_tv", "lx_ce_tvd_vp_merge_tv",
+    "lx_ce_tvd_backward_shard",
 ]

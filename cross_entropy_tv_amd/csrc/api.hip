@@ -48,6 +48,54 @@ lx_status check_shape(int64_t BT, int64_t V, int es) {
   return LX_OK;
 }
 
+// The backward over rows of V columns that are columns [v0, v0 + V) of rows of
+// V_total (v0 = 0, V_total = V for whole rows).
+lx_status backward_impl(void* grad, const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                        int64_t V, int64_t v0, int64_t V_total, int64_t ignore_index, const float* lse_s,
+                        const float* lse_t, const float* sigma, float g_ce, float g_tvd, const float* g_scale,
+                        lx_dtype dt, void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = teacher != nullptr;
+  if (!grad || !student || !target || !lse_s) return LX_ERR_INVALID_ARG;
+  if (has_t && (!lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(grad, es) || !aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) ||
+      !aligned(lse_s, 4) || (has_t && (!aligned(lse_t, 4) || !aligned(sigma, 4))) ||
+      (g_scale && !aligned(g_scale, 4)))
+    return LX_ERR_INVALID_ARG;
+
+  const int64_t lb = BT * V * es, fb = BT * 4;
+  const Span g = span(grad, lb);
+  const Span ins[7] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(lse_s, fb),
+                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb), span(g_scale, 4)};
+  // in place (grad == student) is allowed; any other overlap is not
+  if (grad != student && overlaps(g, ins[0])) return LX_ERR_ALIAS;
+  for (int i = 1; i < 7; ++i)
+    if (overlaps(g, ins[i])) return LX_ERR_ALIAS;
+
+  lx::BwdArgs a;
+  a.grad = grad;
+  a.student = student;
+  a.teacher = teacher;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.g_ce = g_ce;
+  a.g_tvd = g_tvd;
+  a.g_scale = g_scale;
+  a.v0 = v0;
+  a.V_total = V_total;
+  const uintptr_t m = (uintptr_t)student & 15u;
+  a.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
+  return from_hip(lx::launch_backward(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,44 +173,17 @@ lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teache
                              int64_t BT, int64_t V, int64_t ignore_index, const float* lse_s, const float* lse_t,
                              const float* sigma, float g_ce, float g_tvd, const float* g_scale, lx_dtype dt,
                              void* stream) {
-  const int es = esize_of(dt);
-  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
-  if (lx_status s = check_shape(BT, V, es)) return s;
-  if (BT == 0) return LX_OK;
-  const bool has_t = teacher != nullptr;
-  if (!grad || !student || !target || !lse_s) return LX_ERR_INVALID_ARG;
-  if (has_t && (!lse_t || !sigma)) return LX_ERR_INVALID_ARG;
-  if (!aligned(grad, es) || !aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) ||
-      !aligned(lse_s, 4) || (has_t && (!aligned(lse_t, 4) || !aligned(sigma, 4))) ||
-      (g_scale && !aligned(g_scale, 4)))
-    return LX_ERR_INVALID_ARG;
+  return backward_impl(grad, student, teacher, target, BT, V, 0, V, ignore_index, lse_s, lse_t, sigma, g_ce, g_tvd,
+                       g_scale, dt, stream);
+}
 
-  const int64_t lb = BT * V * es, fb = BT * 4;
-  const Span g = span(grad, lb);
-  const Span ins[7] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(lse_s, fb),
-                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb), span(g_scale, 4)};
-  // in place (grad == student) is allowed; any other overlap is not
-  if (grad != student && overlaps(g, ins[0])) return LX_ERR_ALIAS;
-  for (int i = 1; i < 7; ++i)
-    if (overlaps(g, ins[i])) return LX_ERR_ALIAS;
-
-  lx::BwdArgs a;
-  a.grad = grad;
-  a.student = student;
-  a.teacher = teacher;
-  a.target = target;
-  a.BT = BT;
-  a.V = V;
-  a.ignore_index = ignore_index;
-  a.lse_s = lse_s;
-  a.lse_t = lse_t;
-  a.sigma = sigma;
-  a.g_ce = g_ce;
-  a.g_tvd = g_tvd;
-  a.g_scale = g_scale;
-  const uintptr_t m = (uintptr_t)student & 15u;
-  a.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
-  return from_hip(lx::launch_backward(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* teacher, const int64_t* target,
+                                   int64_t BT, int64_t V_shard, int64_t v0, int64_t V, int64_t ignore_index,
+                                   const float* lse_s, const float* lse_t, const float* sigma, float g_ce,
+                                   float g_tvd, const float* g_scale, lx_dtype dt, void* stream) {
+  if (v0 < 0 || V_shard < 1 || V < 1 || v0 > V - V_shard) return LX_ERR_INVALID_ARG;
+  return backward_impl(grad, student, teacher, target, BT, V_shard, v0, V, ignore_index, lse_s, lse_t, sigma, g_ce,
+                       g_tvd, g_scale, dt, stream);
 }
 
 size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher) {
@@ -246,6 +267,8 @@ lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, c
   b.g_ce = g_ce;
   b.g_tvd = g_tvd;
   b.g_scale = g_scale;
+  b.v0 = 0;
+  b.V_total = V;
   const uintptr_t m = (uintptr_t)student & 15u;
   b.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
   return from_hip(lx::launch_backward(b, dt == LX_BF16, st));
@@ -276,6 +299,88 @@ lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t
     for (int i = 0; i < 6; ++i)
       if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
   return from_hip(lx::launch_reduce_mean(ce, tvd, target, BT, ignore_index, mean_out, n_valid, inv_n_valid,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ vocabulary-parallel pieces
+
+lx_status lx_ce_tvd_vp_stats(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                             int64_t V_shard, int64_t v0, int64_t ignore_index, lx_dtype dt, float* stats,
+                             void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V_shard, es)) return s;
+  if (v0 < 0) return LX_ERR_INVALID_ARG;
+  if (BT == 0) return LX_OK;
+  const bool has_t = teacher != nullptr;
+  if (!student || !target || !stats) return LX_ERR_INVALID_ARG;
+  if (!aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) || !aligned(stats, 4))
+    return LX_ERR_INVALID_ARG;
+  const int64_t lb = BT * V_shard * es;
+  const Span out = span(stats, BT * (has_t ? 5 : 3) * 4);
+  const Span ins[3] = {span(student, lb), span(teacher, lb), span(target, BT * 8)};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(out, ins[i])) return LX_ERR_ALIAS;
+  lx::VpArgs a{student, teacher, target, BT, V_shard, v0, ignore_index, nullptr, nullptr, stats,
+               (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0};
+  return from_hip(lx::launch_vp_stats(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_ce_tvd_vp_merge_stats(const float* stats, int64_t n_shards, const int64_t* target, int64_t BT,
+                                   int64_t V, int64_t ignore_index, int has_teacher, float* ce, float* lse_s,
+                                   float* lse_t, void* stream) {
+  const int P = has_teacher ? 5 : 3;
+  if (BT < 0 || V < 1 || n_shards < 1 || n_shards > (int64_t)INT_MAX) return LX_ERR_INVALID_ARG;
+  if (BT > 0 && BT > INT64_MAX / n_shards / P / 4) return LX_ERR_INVALID_ARG;
+  if (BT == 0) return LX_OK;
+  if (!stats || !target || !ce || !lse_s || (has_teacher && !lse_t)) return LX_ERR_INVALID_ARG;
+  if (!aligned(stats, 4) || !aligned(target, 8) || !aligned(ce, 4) || !aligned(lse_s, 4) ||
+      (has_teacher && !aligned(lse_t, 4)))
+    return LX_ERR_INVALID_ARG;
+  const int64_t fb = BT * 4;
+  const Span sp[5] = {span(stats, n_shards * BT * P * 4), span(target, BT * 8), span(ce, fb), span(lse_s, fb),
+                      span(has_teacher ? lse_t : nullptr, fb)};
+  for (int o = 2; o < 5; ++o)
+    for (int i = 0; i < 5; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_vp_merge_stats(stats, n_shards, target, BT, V, ignore_index, has_teacher != 0, ce,
+                                            lse_s, has_teacher ? lse_t : nullptr, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_ce_tvd_vp_tv(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                          int64_t V_shard, int64_t ignore_index, const float* lse_s, const float* lse_t, lx_dtype dt,
+                          float* tv, void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V_shard, es)) return s;
+  if (BT == 0) return LX_OK;
+  if (!student || !teacher || !target || !lse_s || !lse_t || !tv) return LX_ERR_INVALID_ARG;
+  if (!aligned(student, es) || !aligned(teacher, es) || !aligned(target, 8) || !aligned(lse_s, 4) ||
+      !aligned(lse_t, 4) || !aligned(tv, 4))
+    return LX_ERR_INVALID_ARG;
+  const int64_t lb = BT * V_shard * es, fb = BT * 4;
+  const Span out = span(tv, BT * 2 * 4);
+  const Span ins[5] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(lse_s, fb), span(lse_t, fb)};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(out, ins[i])) return LX_ERR_ALIAS;
+  lx::VpArgs a{student, teacher, target, BT, V_shard, 0, ignore_index, lse_s, lse_t, tv,
+               ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u) ? 1 : 0};
+  return from_hip(lx::launch_vp_tv(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_ce_tvd_vp_merge_tv(const float* tv, int64_t n_shards, const int64_t* target, int64_t BT,
+                                int64_t ignore_index, float* tvd, float* sigma, void* stream) {
+  if (BT < 0 || n_shards < 1 || n_shards > (int64_t)INT_MAX) return LX_ERR_INVALID_ARG;
+  if (BT > 0 && BT > INT64_MAX / n_shards / 8) return LX_ERR_INVALID_ARG;
+  if (BT == 0) return LX_OK;
+  if (!tv || !target || !tvd || !sigma) return LX_ERR_INVALID_ARG;
+  if (!aligned(tv, 4) || !aligned(target, 8) || !aligned(tvd, 4) || !aligned(sigma, 4)) return LX_ERR_INVALID_ARG;
+  const int64_t fb = BT * 4;
+  const Span sp[4] = {span(tv, n_shards * BT * 8), span(target, BT * 8), span(tvd, fb), span(sigma, fb)};
+  for (int o = 2; o < 4; ++o)
+    for (int i = 0; i < 4; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_vp_merge_tv(tv, n_shards, target, BT, ignore_index, tvd, sigma,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -9,8 +9,13 @@
 //
 // is written, with the target element's -g_ce added by the lane that owns it.
 // Per row this is p_v * (alpha + beta * s_v) with alpha = k * (g_ce - 0.5 *
-// g_tvd * sigma) and beta = 0.5 * k * g_tvd, so each element costs two
-// exponentials, a sign and two FMAs.
+// g_tvd * sigma) and beta = 0.5 * k * g_tvd.  The sign is read off the
+// exponent arguments of p and q (common.hpp), so q itself is never formed:
+// each element costs one exponential, two argument FMAs, a clamp and two FMAs.
+//
+// The same kernel serves a column shard of a vocabulary-parallel layout: the
+// row then holds columns [v0, v0 + V) of V_total, the target still indexes
+// the whole row, and only the shard that holds it subtracts g_ce.
 //
 // Work is tiled over (row, chunk) with a grid-stride loop; each lane reads an
 // element group before it writes the same group, so the gradient may be the
@@ -33,7 +38,7 @@ constexpr int kMaxGrid = 1 << 20;
 template <typename T, bool TEACHER, int NT, int UNR>
 __global__ __launch_bounds__(NT) void bwd_kernel(
     T* grad, const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
-    int64_t BT, int V, int64_t ignore_index, int vec, int chunks_per_row,
+    int64_t BT, int V, int64_t v0, int64_t V_total, int64_t ignore_index, int vec, int chunks_per_row,
     const float* __restrict__ lse_s, const float* __restrict__ lse_t, const float* __restrict__ sigma,
     float g_ce, float g_tvd, const float* __restrict__ g_scale) {
   const int tid = threadIdx.x;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const T* zb = z + L.head;
     const T* ub = TEACHER ? u + L.head : nullptr;
 
-    if (t == ignore_index || t < 0 || t >= V) {
+    if (t == ignore_index || t < 0 || t >= V_total) {
       // ignored row: +0.0; invalid target: NaN (the loud failure of the ABI contract)
       const uint32_t fill = (t == ignore_index) ? 0u : kQNaN32;
       for (int i = s0 + tid; i < s1; i += NT) store_bits1(gr + scalar_elem(L, i), fill);
@@ -68,6 +73,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     // with a teacher p' = 2^kPqBias * p and the sign come from the biased
     // arguments the forward used (sign_eps), so alpha and beta are rescaled:
     // g = p' * (a' + b' * s') = p * (alpha + beta * sign)
+    // the target's column within this row's V columns, -1 when it lies outside
+    const int tc = (t >= v0 && t - v0 < V) ? (int)(t - v0) : -1;
     const float nbs = TEACHER ? pq_bias(lse_s[r]) : neg_scaled(lse_s[r]);
     const float nbt = TEACHER ? pq_bias(lse_t[r]) : 0.0f;
     const float kce = k * g_ce;
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
       } else {
         gv = exp2_hw(ap) * a1;
       }
-      if (e == t) gv -= kce;
+      if (e == tc) gv -= kce;
       store1(gr + e, gv);
     }
 
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
             o[e] = exp2_hw(ap) * a1;
           }
         }
-        const int rel = (int)(t - (int64_t)(L.head + 8 * g));
+        const int rel = tc - (L.head + 8 * g);
         if ((unsigned)rel < 8u) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
@@ -130,7 +137,7 @@ static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
   const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
   hipLaunchKernelGGL((bwd_kernel<T, TEACHER, kBwdThreads, kBwdUnroll>), dim3(grid), dim3(kBwdThreads), 0, st,
                      static_cast<T*>(a.grad), static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
-                     a.target, a.BT, V, a.ignore_index, a.vec, chunks, a.lse_s, a.lse_t, a.sigma, a.g_ce,
+                     a.target, a.BT, V, a.v0, a.V_total, a.ignore_index, a.vec, chunks, a.lse_s, a.lse_t, a.sigma, a.g_ce,
                      a.g_tvd, a.g_scale);
   return hipGetLastError();
 }

@@ -204,6 +204,59 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ------------------------------------------------------------------ block reductions and TV sums
+
+template <int NT>
+__device__ __forceinline__ Lse block_lse(Lse a, Lse* red) {
+  constexpr int W = NT / 64;
+  a = wave_lse(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  Lse f = red[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) lse_merge(f, red[w]);
+  return f;  // identical in every thread
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum_t0(float v, float* red) {
+  constexpr int W = NT / 64;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float f = 0.0f;
+  if (threadIdx.x == 0) {
+    f = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) f += red[w];
+  }
+  return f;  // valid in thread 0
+}
+
+// step-2 accumulation for one group of 8, nbs and nbt from pq_bias:
+// S += p' * s' and Q += q' * s' (s' = sign_eps), so that, scaled by
+// kTvScale, S is sum p * sign and S - Q is sum |p - q|
+__device__ __forceinline__ void tv_add8(const float (&x)[8], const float (&y)[8], float nbs, float nbt,
+                                        float& Q0, float& Q1, float& S0, float& S1) {
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    const float ap0 = exparg(x[k], nbs), aq0 = exparg(y[k], nbt);
+    const float ap1 = exparg(x[k + 1], nbs), aq1 = exparg(y[k + 1], nbt);
+    const float s0 = sign_eps(ap0, aq0), s1 = sign_eps(ap1, aq1);
+    S0 = __builtin_fmaf(exp2_hw(ap0), s0, S0);
+    Q0 = __builtin_fmaf(exp2_hw(aq0), s0, Q0);
+    S1 = __builtin_fmaf(exp2_hw(ap1), s1, S1);
+    Q1 = __builtin_fmaf(exp2_hw(aq1), s1, Q1);
+  }
+}
+
+__device__ __forceinline__ void tv_add1(float x, float y, float nbs, float nbt, float& Q, float& S) {
+  const float ap = exparg(x, nbs), aq = exparg(y, nbt);
+  const float s = sign_eps(ap, aq);
+  S = __builtin_fmaf(exp2_hw(ap), s, S);
+  Q = __builtin_fmaf(exp2_hw(aq), s, Q);
+}
+
 // ------------------------------------------------------------------ row layout
 
 // A row of V elements starting at `row` is cut into a scalar head [0, head),

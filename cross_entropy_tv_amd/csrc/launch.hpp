@@ -57,6 +57,9 @@ struct BwdArgs {
   float g_ce, g_tvd;
   const float* g_scale;
   int vec;
+  // Column shard: these V columns are columns [v0, v0 + V) of rows of V_total
+  // (v0 = 0 and V_total = V for whole rows).  Targets index the whole row.
+  int64_t v0, V_total;
 };
 
 hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream);
@@ -70,6 +73,25 @@ struct FusedGrad {
 };
 hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+// Vocabulary-parallel pieces (vocab_parallel.hip): the shard holds columns
+// [v0, v0 + Vs) of rows of the whole vocabulary.
+struct VpArgs {
+  const void* student;
+  const void* teacher;  // nullptr: CE-only (stats only)
+  const int64_t* target;
+  int64_t BT, Vs, v0, ignore_index;
+  const float *lse_s, *lse_t;  // vp_tv only
+  float* out;                  // stats [BT][5 or 3] or tv [BT][2]
+  int vec;
+};
+hipError_t launch_vp_stats(const VpArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_vp_tv(const VpArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
+                                 int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
+                                 hipStream_t stream);
+hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,
+                              float* tvd, float* sigma, hipStream_t stream);
+
 hipError_t launch_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
                               int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,
                               hipStream_t stream);

@@ -1,0 +1,252 @@
+// Vocabulary-parallel (column-sharded) pieces of the fused CE + TVD loss.
+//
+// With the vocabulary split over N devices (a sharded lm_head), device n holds
+// columns [v0_n, v0_n + Vs_n) of every row.  The two steps of the "Forward
+// Pass" section of the Liger-Kernel PR #1384 analysis page then each need one
+// exchange across the shards:
+//
+//   1. vp_stats: per row and shard, the (max, sum-exp) pairs of student and
+//      teacher over the shard, and the target logit if the shard holds the
+//      target column (+0 otherwise).  vp_merge_stats merges the N partials in
+//      shard order (the (max, sum-exp) merge of step 1, and a plain sum of the
+//      target-logit parts, exactly one of which is non-zero) into lse_s,
+//      lse_t and ce = lse_s - z_t.
+//   2. vp_tv: per row and shard, (sum |p - q|, sum p * sign(p - q)) over the
+//      shard from the global log-sum-exps, with the same arguments and sign
+//      rule as every other kernel here (common.hpp).  vp_merge_tv adds the N
+//      partials in shard order into tvd = 0.5 * sum |p - q| and sigma.
+//
+// Between the steps the partials travel between devices (an all-gather of
+// 20 bytes per row and shard after step 1, 8 after step 2); on one device the
+// merge kernels read the gathered [N][BT][.] arrays directly.  The backward
+// needs no exchange (the backward kernel runs on the shard with the target
+// column offset).  Merges run in shard order, so results are deterministic
+// and do not depend on how the exchange is ordered.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lx {
+
+namespace {
+
+constexpr int kVpThreads = 256;
+constexpr int kVpMergeThreads = 256;
+constexpr int kMaxGrid = 1 << 20;
+
+// One workgroup per row (grid-stride over rows): the shard's (max, sum-exp)
+// pairs and its part of the target logit.  stats[r] = {m_s, s_s, m_t, s_t,
+// zt} with a teacher, {m_s, s_s, zt} without; ignored rows get zeros.
+template <typename T, bool TEACHER, int NT>
+__global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ student, const T* __restrict__ teacher,
+                                                      const int64_t* __restrict__ target, int64_t BT, int Vs,
+                                                      int64_t v0, int64_t ignore_index, int vec,
+                                                      float* __restrict__ stats) {
+  __shared__ Lse red_s[NT / 64];
+  __shared__ Lse red_t[NT / 64];
+  constexpr int P = TEACHER ? 5 : 3;
+  const int tid = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < BT; r += gridDim.x) {
+    const int64_t t = target[r];
+    float* o = stats + r * P;
+    if (t == ignore_index) {
+      if (tid < P) o[tid] = 0.0f;
+      continue;
+    }
+    const T* z = student + r * (int64_t)Vs;
+    const T* u = TEACHER ? teacher + r * (int64_t)Vs : nullptr;
+    const RowLayout L = row_layout(z, Vs, vec);
+    const int nsc = L.head + L.tail;
+    Lse as = lse_init(), at = lse_init();
+    for (int i = tid; i < nsc; i += NT) {
+      const int e = scalar_elem(L, i);
+      lse_add1(as, load1(z + e));
+      if (TEACHER) lse_add1(at, load1(u + e));
+    }
+    const T* zb = z + L.head;
+    const T* ub = TEACHER ? u + L.head : nullptr;
+#pragma unroll 2
+    for (int g = tid; g < L.groups; g += NT) {
+      float x[8], y[8];
+      load8(zb + 8 * g, x);
+      if (TEACHER) load8(ub + 8 * g, y);
+      lse_add8(as, x);
+      if (TEACHER) lse_add8(at, y);
+    }
+    const Lse fs = block_lse<NT>(as, red_s);
+    Lse ft{0.0f, 0.0f};
+    if (TEACHER) ft = block_lse<NT>(at, red_t);
+    if (tid == 0) {
+      o[0] = fs.m;
+      o[1] = fs.s;
+      if (TEACHER) {
+        o[2] = ft.m;
+        o[3] = ft.s;
+      }
+      const int64_t tc = t - v0;
+      o[P - 1] = (tc >= 0 && tc < Vs) ? load1(z + tc) : 0.0f;
+    }
+    __syncthreads();  // red_s / red_t are reused by the next row
+  }
+}
+
+// One thread per row: the N shards' stats merged in shard order.
+template <bool TEACHER>
+__global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
+    const float* __restrict__ stats, int N, int64_t BT, const int64_t* __restrict__ target, int64_t V,
+    int64_t ignore_index, float* __restrict__ ce, float* __restrict__ lse_s, float* __restrict__ lse_t) {
+  constexpr int P = TEACHER ? 5 : 3;
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < BT; r += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = target[r];
+    if (t == ignore_index) {
+      ce[r] = 0.0f;
+      lse_s[r] = 0.0f;
+      if (TEACHER) lse_t[r] = 0.0f;
+      continue;
+    }
+    const float* w = stats + r * P;
+    const int64_t shard_stride = BT * P;
+    Lse fs{w[0], w[1]};
+    Lse ft{TEACHER ? w[2] : 0.0f, TEACHER ? w[3] : 0.0f};
+    float zt = w[P - 1];
+    for (int n = 1; n < N; ++n) {
+      const float* wn = w + n * shard_stride;
+      lse_merge(fs, Lse{wn[0], wn[1]});
+      if (TEACHER) lse_merge(ft, Lse{wn[2], wn[3]});
+      zt += wn[P - 1];
+    }
+    const float ls = lse_value(fs);
+    if (t >= 0 && t < V) ce[r] = ls - zt; else store_nan(ce + r);
+    lse_s[r] = ls;
+    if (TEACHER) lse_t[r] = lse_value(ft);
+  }
+}
+
+// One workgroup per row: the shard's (sum |p - q|, sum p * sign) from the
+// global log-sum-exps; ignored rows get zeros.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void vp_tv_kernel(const T* __restrict__ student, const T* __restrict__ teacher,
+                                                   const int64_t* __restrict__ target, int64_t BT, int Vs,
+                                                   int64_t ignore_index, int vec, const float* __restrict__ lse_s,
+                                                   const float* __restrict__ lse_t, float* __restrict__ tv) {
+  __shared__ float red_f[2][NT / 64];
+  const int tid = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < BT; r += gridDim.x) {
+    const int64_t t = target[r];
+    if (t == ignore_index) {
+      if (tid < 2) tv[2 * r + tid] = 0.0f;
+      continue;
+    }
+    const T* z = student + r * (int64_t)Vs;
+    const T* u = teacher + r * (int64_t)Vs;
+    const RowLayout L = row_layout(z, Vs, vec);
+    const int nsc = L.head + L.tail;
+    const float nbs = pq_bias(lse_s[r]), nbt = pq_bias(lse_t[r]);
+    float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
+    for (int i = tid; i < nsc; i += NT) {
+      const int e = scalar_elem(L, i);
+      tv_add1(load1(z + e), load1(u + e), nbs, nbt, Q0, S0);
+    }
+    const T* zb = z + L.head;
+    const T* ub = u + L.head;
+#pragma unroll 2
+    for (int g = tid; g < L.groups; g += NT) {
+      float x[8], y[8];
+      load8(zb + 8 * g, x);
+      load8(ub + 8 * g, y);
+      tv_add8(x, y, nbs, nbt, Q0, Q1, S0, S1);
+    }
+    const float Q = block_sum_t0<NT>(Q0 + Q1, red_f[0]);
+    const float S = block_sum_t0<NT>(S0 + S1, red_f[1]);
+    if (tid == 0) {
+      tv[2 * r] = (S - Q) * kTvScale;
+      tv[2 * r + 1] = S * kTvScale;
+    }
+    __syncthreads();  // red_f is reused by the next row
+  }
+}
+
+// One thread per row: the N shards' (sum |p - q|, sum p * sign) added in
+// shard order.
+__global__ __launch_bounds__(kVpMergeThreads) void vp_merge_tv_kernel(
+    const float* __restrict__ tv, int N, int64_t BT, const int64_t* __restrict__ target, int64_t ignore_index,
+    float* __restrict__ tvd, float* __restrict__ sigma) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < BT; r += (int64_t)gridDim.x * blockDim.x) {
+    if (target[r] == ignore_index) {
+      tvd[r] = 0.0f;
+      sigma[r] = 0.0f;
+      continue;
+    }
+    float A = tv[2 * r], S = tv[2 * r + 1];
+    for (int n = 1; n < N; ++n) {
+      const float* w = tv + (int64_t)n * BT * 2 + 2 * r;
+      A += w[0];
+      S += w[1];
+    }
+    tvd[r] = 0.5f * A;
+    sigma[r] = S;
+  }
+}
+
+int row_grid(int64_t BT) { return (int)(BT < kMaxGrid ? BT : kMaxGrid); }
+int merge_grid(int64_t BT) {
+  const int64_t b = (BT + kVpMergeThreads - 1) / kVpMergeThreads;
+  return (int)(b < kMaxGrid ? b : kMaxGrid);
+}
+
+template <typename T>
+hipError_t launch_vp_stats_t(const VpArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  const T* z = static_cast<const T*>(a.student);
+  const T* u = static_cast<const T*>(a.teacher);
+  if (u) {
+    hipLaunchKernelGGL((vp_stats_kernel<T, true, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st, z,
+                       u, a.target, a.BT, (int)a.Vs, a.v0, a.ignore_index, a.vec, a.out);
+  } else {
+    hipLaunchKernelGGL((vp_stats_kernel<T, false, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
+                       z, u, a.target, a.BT, (int)a.Vs, a.v0, a.ignore_index, a.vec, a.out);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_vp_tv_t(const VpArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((vp_tv_kernel<T, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
+                     static_cast<const T*>(a.student), static_cast<const T*>(a.teacher), a.target, a.BT, (int)a.Vs,
+                     a.ignore_index, a.vec, a.lse_s, a.lse_t, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vp_stats(const VpArgs& a, bool bf16, hipStream_t st) {
+  return bf16 ? launch_vp_stats_t<uint16_t>(a, st) : launch_vp_stats_t<float>(a, st);
+}
+
+hipError_t launch_vp_tv(const VpArgs& a, bool bf16, hipStream_t st) {
+  return bf16 ? launch_vp_tv_t<uint16_t>(a, st) : launch_vp_tv_t<float>(a, st);
+}
+
+hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
+                                 int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
+                                 hipStream_t st) {
+  (void)hipGetLastError();
+  if (teacher) {
+    hipLaunchKernelGGL((vp_merge_stats_kernel<true>), dim3(merge_grid(BT)), dim3(kVpMergeThreads), 0, st, stats,
+                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t);
+  } else {
+    hipLaunchKernelGGL((vp_merge_stats_kernel<false>), dim3(merge_grid(BT)), dim3(kVpMergeThreads), 0, st, stats,
+                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,
+                              float* tvd, float* sigma, hipStream_t st) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(vp_merge_tv_kernel, dim3(merge_grid(BT)), dim3(kVpMergeThreads), 0, st, tv, (int)N, BT, target,
+                     ignore_index, tvd, sigma);
+  return hipGetLastError();
+}
+
+}  // namespace lx

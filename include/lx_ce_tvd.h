@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 2
+#define LX_CE_TVD_ABI_VERSION 3
 
 typedef enum lx_status {
   LX_OK = 0,
@@ -209,6 +209,97 @@ lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t
                                 int64_t BT, int64_t ignore_index,
                                 float* mean_out, int64_t* n_valid, float* inv_n_valid,
                                 void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Vocabulary-parallel pieces (a sharded lm_head): each device holds a column
+ * shard, columns [v0, v0 + V_shard) of every row of V = sum of the shard
+ * widths, as a contiguous (BT, V_shard) array.  The two steps of the page's
+ * "Forward Pass" section each become a per-shard partial, an exchange of the
+ * partials between devices (which the caller runs, e.g. an all-gather over
+ * RCCL), and a merge:
+ *
+ *   lx_ce_tvd_vp_stats        -> all-gather -> lx_ce_tvd_vp_merge_stats -> ce, lse_s, lse_t
+ *   lx_ce_tvd_vp_tv (teacher) -> all-gather -> lx_ce_tvd_vp_merge_tv    -> tvd, sigma
+ *
+ * and the backward of a shard, lx_ce_tvd_backward_shard, needs no exchange.
+ * The merges read the gathered partials as [n_shards][BT][...] in shard order
+ * and combine them in that order, so the results do not depend on the order of
+ * the exchange; they meet the same tolerances as lx_ce_tvd_forward on the
+ * whole rows (page sections "Forward Pass" and "Backward Pass").
+ */
+
+/* floats per row of the partials */
+#define LX_VP_STATS_FLOATS(has_teacher) ((has_teacher) ? 5 : 3)
+#define LX_VP_TV_FLOATS 2
+
+/*
+ * Per-shard step 1: for each row, the shard's maximum and sum of exp(x - max)
+ * of the student (and teacher), and the student's target logit when the
+ * target column lies in the shard (else +0).
+ *
+ * Inputs : student, teacher (NULL = CE-only) (BT, V_shard) dt; target int64[BT]
+ *          indexing the WHOLE row; v0 >= 0 the shard's first column.
+ * Output : stats float[BT][LX_VP_STATS_FLOATS(teacher != NULL)] =
+ *          {m_s, s_s, m_t, s_t, z_t part} (CE-only: {m_s, s_s, z_t part});
+ *          ignored rows are all +0.0.  Must not overlap an input.
+ * Errors : LX_ERR_INVALID_ARG, LX_ERR_UNSUPPORTED_DTYPE, LX_ERR_ALIAS, LX_ERR_HIP.
+ */
+lx_status lx_ce_tvd_vp_stats(const void* student, const void* teacher, const int64_t* target,
+                             int64_t BT, int64_t V_shard, int64_t v0, int64_t ignore_index,
+                             lx_dtype dt, float* stats, void* stream);
+
+/*
+ * Merge of the gathered step-1 partials of n_shards shards, in shard order:
+ * lse = M + log(sum_n s_n * exp(m_n - M)), ce = lse_s - sum_n (z_t part)_n.
+ *
+ * Inputs : stats float[n_shards][BT][LX_VP_STATS_FLOATS(has_teacher)];
+ *          target int64[BT]; V the whole vocabulary (a target outside [0, V)
+ *          that is not ignore_index gives ce = NaN).
+ * Outputs: ce, lse_s float[BT]; lse_t float[BT] with a teacher (may be NULL
+ *          without).  Ignored rows +0.0.  Outputs must not overlap the inputs
+ *          or each other.
+ */
+lx_status lx_ce_tvd_vp_merge_stats(const float* stats, int64_t n_shards, const int64_t* target,
+                                   int64_t BT, int64_t V, int64_t ignore_index, int has_teacher,
+                                   float* ce, float* lse_s, float* lse_t, void* stream);
+
+/*
+ * Per-shard step 2: for each row, the shard's sum |p - q| and sum p *
+ * sign(p - q), p and q formed from the whole-row lse_s and lse_t (as merged).
+ *
+ * Inputs : student, teacher (BT, V_shard) dt (teacher required); target;
+ *          lse_s, lse_t float[BT].
+ * Output : tv float[BT][LX_VP_TV_FLOATS]; ignored rows +0.0.  Must not overlap
+ *          an input.
+ */
+lx_status lx_ce_tvd_vp_tv(const void* student, const void* teacher, const int64_t* target,
+                          int64_t BT, int64_t V_shard, int64_t ignore_index,
+                          const float* lse_s, const float* lse_t, lx_dtype dt, float* tv, void* stream);
+
+/*
+ * Merge of the gathered step-2 partials, added in shard order:
+ * tvd = 0.5 * sum_n A_n, sigma = sum_n S_n.
+ *
+ * Inputs : tv float[n_shards][BT][LX_VP_TV_FLOATS]; target int64[BT].
+ * Outputs: tvd, sigma float[BT]; ignored rows +0.0; no overlaps.
+ */
+lx_status lx_ce_tvd_vp_merge_tv(const float* tv, int64_t n_shards, const int64_t* target,
+                                int64_t BT, int64_t ignore_index, float* tvd, float* sigma, void* stream);
+
+/*
+ * Backward of one column shard: lx_ce_tvd_backward restricted to columns
+ * [v0, v0 + V_shard) of rows of V columns, with the whole-row lse_s, lse_t
+ * and sigma (as merged).  Only the shard holding the target column subtracts
+ * g_ce; a target outside [0, V) that is not ignore_index poisons the row (NaN)
+ * in every shard.  Requires 0 <= v0 <= V - V_shard.  grad may EQUAL student.
+ */
+lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* teacher,
+                                   const int64_t* target, int64_t BT, int64_t V_shard, int64_t v0,
+                                   int64_t V, int64_t ignore_index,
+                                   const float* lse_s, const float* lse_t, const float* sigma,
+                                   float g_ce, float g_tvd, const float* g_scale,
+                                   lx_dtype dt, void* stream);
 
 #ifdef __cplusplus
 }

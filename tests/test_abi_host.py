@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 2
+    assert lx.lx_abi_version() == 3
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
                        (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP")):
         assert lx.lx_status_string(code) == name
@@ -145,3 +145,57 @@ def test_reduce_validation():
     assert r(A, A + 4096, A * 2, 4, -100, A + 8, None, None, None) == lx.LX_ERR_ALIAS
     assert r(A, A + 4096, A * 2, 4, -100, A * 3, A * 3, None, None) == lx.LX_ERR_ALIAS
     assert r(A, A + 4096, A * 2, 4, -100, A * 3, A * 3 + 12, None, None) == lx.LX_ERR_INVALID_ARG  # n_valid align
+
+
+def test_vocab_parallel_validation():
+    names = set(declared_functions())
+    assert {"lx_ce_tvd_vp_stats", "lx_ce_tvd_vp_merge_stats", "lx_ce_tvd_vp_tv", "lx_ce_tvd_vp_merge_tv",
+            "lx_ce_tvd_backward_shard"} <= names
+
+    def stats(student=A, teacher=A + (1 << 31), target=A * 3, BT=4, Vs=100, v0=0, dt=1, out=A * 4):
+        return L.lx_ce_tvd_vp_stats(student, teacher, target, BT, Vs, v0, -100, dt, out, None)
+
+    assert stats(BT=0) == lx.LX_OK
+    assert stats(dt=5) == lx.LX_ERR_UNSUPPORTED_DTYPE
+    assert stats(Vs=0) == lx.LX_ERR_INVALID_ARG
+    assert stats(v0=-1) == lx.LX_ERR_INVALID_ARG
+    assert stats(out=None) == lx.LX_ERR_INVALID_ARG
+    assert stats(student=A + 1) == lx.LX_ERR_INVALID_ARG
+    assert stats(out=A + 128) == lx.LX_ERR_ALIAS                     # inside the student shard
+    assert stats(out=A * 3 + 16) == lx.LX_ERR_ALIAS                  # overlapping target
+
+    def mstats(st=A, n=2, target=A * 3, BT=4, V=200, has_t=1, ce=A * 4, lse_s=A * 4 + 64, lse_t=A * 4 + 128):
+        return L.lx_ce_tvd_vp_merge_stats(st, n, target, BT, V, -100, has_t, ce, lse_s, lse_t, None)
+
+    assert mstats(BT=0) == lx.LX_OK
+    assert mstats(n=0) == lx.LX_ERR_INVALID_ARG
+    assert mstats(V=0) == lx.LX_ERR_INVALID_ARG
+    assert mstats(lse_t=None) == lx.LX_ERR_INVALID_ARG              # required with a teacher
+    assert mstats(ce=A + 16) == lx.LX_ERR_ALIAS                      # inside the partials
+    assert mstats(lse_s=A * 4) == lx.LX_ERR_ALIAS                    # two outputs share memory
+
+    def tv(student=A, teacher=A + (1 << 31), BT=4, Vs=100, lse_s=A * 4, lse_t=A * 4 + 64, out=A * 5):
+        return L.lx_ce_tvd_vp_tv(student, teacher, A * 3, BT, Vs, -100, lse_s, lse_t, 1, out, None)
+
+    assert tv(BT=0) == lx.LX_OK
+    assert tv(teacher=None) == lx.LX_ERR_INVALID_ARG                 # step 2 needs the teacher
+    assert tv(lse_t=None) == lx.LX_ERR_INVALID_ARG
+    assert tv(out=A * 4 + 8) == lx.LX_ERR_ALIAS
+
+    def mtv(t=A, n=3, BT=4, tvd=A * 4, sigma=A * 4 + 64):
+        return L.lx_ce_tvd_vp_merge_tv(t, n, A * 3, BT, -100, tvd, sigma, None)
+
+    assert mtv(BT=0) == lx.LX_OK
+    assert mtv(n=0) == lx.LX_ERR_INVALID_ARG
+    assert mtv(sigma=None) == lx.LX_ERR_INVALID_ARG
+    assert mtv(tvd=A + 8) == lx.LX_ERR_ALIAS                         # inside the 3 x 4 x 2 partials
+
+    def bshard(grad=A * 5, student=A, BT=4, Vs=100, v0=0, V=300):
+        return L.lx_ce_tvd_backward_shard(grad, student, A + (1 << 31), A * 3, BT, Vs, v0, V, -100, A * 4 + 128,
+                                          A * 4 + 192, A * 4 + 256, 1.0, 1.0, None, 1, None)
+
+    assert bshard(BT=0) == lx.LX_OK
+    assert bshard(v0=-1) == lx.LX_ERR_INVALID_ARG
+    assert bshard(v0=201) == lx.LX_ERR_INVALID_ARG                   # shard runs past the row
+    assert bshard(V=50) == lx.LX_ERR_INVALID_ARG
+    assert bshard(grad=A + 64) == lx.LX_ERR_ALIAS                    # partial overlap with the student
