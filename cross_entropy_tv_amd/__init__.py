@@ -23,6 +23,7 @@ LX_ERR_WORKSPACE = 4
 LX_ERR_HIP = 5
 LX_F32 = 0
 LX_BF16 = 1
+LX_F16 = 2
 
 
 class LxError(RuntimeError):
@@ -76,6 +77,13 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_vp_merge_tv.restype = i32
     L.lx_ce_tvd_backward_shard.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, p, p, f32, f32, p, i32, p]
     L.lx_ce_tvd_backward_shard.restype = i32
+    L.lx_ce_tvd_forward_ex.argtypes = [p, i64, p, i64, p, i64, i64, i64, p, p, p, p, p, i32, p, sz, p]
+    L.lx_ce_tvd_forward_ex.restype = i32
+    L.lx_ce_tvd_backward_ex.argtypes = [p, i64, p, i64, p, i64, p, i64, i64, i64, p, p, p, f32, f32, p, p, p, i32, p]
+    L.lx_ce_tvd_backward_ex.restype = i32
+    L.lx_ce_tvd_forward_backward_ex.argtypes = [p, i64, p, i64, p, i64, i64, i64, p, p, p, p, p, p, i64, f32, f32,
+                                                p, p, p, i32, p, sz, p]
+    L.lx_ce_tvd_forward_backward_ex.restype = i32
     return L
 
 
@@ -94,7 +102,9 @@ def _dtype_code(t) -> int:
         return LX_BF16
     if t.dtype == torch.float32:
         return LX_F32
-    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return LX_F16
+    raise TypeError(f"logits must be bfloat16, float16 or float32, got {t.dtype}")
 
 
 def _stream(stream):
@@ -108,6 +118,14 @@ def _logits2d(t, name):
     if t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name} must be a contiguous 2-D (BT, V) device tensor")
     return t.shape
+
+
+def _rows2d(t, name):
+    """(BT, V, row stride) of a 2-D device tensor whose rows are contiguous."""
+    if t.dim() != 2 or not t.is_cuda or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D (BT, V) device tensor with contiguous rows")
+    BT, V = t.shape
+    return BT, V, (t.stride(0) if BT > 1 else V)
 
 
 def _check(status: int, where: str) -> None:
@@ -258,11 +276,75 @@ def lx_ce_tvd_backward_shard(grad, student, teacher, target, v0, V, ignore_index
            "lx_ce_tvd_backward_shard")
 
 
+def lx_ce_tvd_forward_ex(student, teacher, target, ignore_index, ce, tvd, lse_s, lse_t, sigma,
+                         workspace=None, stream=None) -> None:
+    """lx_ce_tvd_forward on row-strided views: each of student / teacher may be any
+    2-D view with contiguous rows (its stride(0) is passed as the row stride)."""
+    BT, V, lds = _rows2d(student, "student")
+    dt = _dtype_code(student)
+    ldt = V
+    if teacher is not None:
+        if teacher.shape != student.shape or teacher.dtype != student.dtype:
+            raise ValueError("teacher must match student in shape and dtype")
+        ldt = _rows2d(teacher, "teacher")[2]
+    need = lx_ce_tvd_workspace_bytes(BT, V, dt, teacher is not None)
+    if workspace is None and need:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=student.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lx_ce_tvd_forward_ex(_ptr(student), lds, _ptr(teacher), ldt, _ptr(target), BT, V, int(ignore_index),
+                                    _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t), _ptr(sigma), dt,
+                                    _ptr(workspace), wbytes, _stream(stream)), "lx_ce_tvd_forward_ex")
+
+
+def lx_ce_tvd_backward_ex(grad, student, teacher, target, ignore_index, lse_s, lse_t, sigma, g_ce: float,
+                          g_tvd: float, grad_ce_rows=None, grad_tvd_rows=None, g_scale=None, stream=None) -> None:
+    """lx_ce_tvd_backward on row-strided views, with optional per-row factors
+    ``grad_ce_rows`` / ``grad_tvd_rows`` (float32 [BT] device tensors)."""
+    BT, V, lds = _rows2d(student, "student")
+    dt = _dtype_code(student)
+    if grad.shape != student.shape or grad.dtype != student.dtype:
+        raise ValueError("grad must match student in shape and dtype")
+    ldg = _rows2d(grad, "grad")[2]
+    ldt = V if teacher is None else _rows2d(teacher, "teacher")[2]
+    _check(lib.lx_ce_tvd_backward_ex(_ptr(grad), ldg, _ptr(student), lds, _ptr(teacher), ldt, _ptr(target), BT, V,
+                                     int(ignore_index), _ptr(lse_s), _ptr(lse_t), _ptr(sigma), float(g_ce),
+                                     float(g_tvd), _ptr(grad_ce_rows), _ptr(grad_tvd_rows), _ptr(g_scale), dt,
+                                     _stream(stream)), "lx_ce_tvd_backward_ex")
+
+
+def lx_ce_tvd_forward_backward_ex(student, teacher, target, ignore_index, ce, tvd, lse_s, lse_t, sigma, grad,
+                                  g_ce: float, g_tvd: float, grad_ce_rows=None, grad_tvd_rows=None, g_scale=None,
+                                  workspace=None, stream=None) -> None:
+    """lx_ce_tvd_forward_backward on row-strided views, with optional per-row factors."""
+    BT, V, lds = _rows2d(student, "student")
+    dt = _dtype_code(student)
+    ldt = V
+    if teacher is not None:
+        if teacher.shape != student.shape or teacher.dtype != student.dtype:
+            raise ValueError("teacher must match student in shape and dtype")
+        ldt = _rows2d(teacher, "teacher")[2]
+    if grad.shape != student.shape or grad.dtype != student.dtype:
+        raise ValueError("grad must match student in shape and dtype")
+    ldg = _rows2d(grad, "grad")[2]
+    need = lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher is not None)
+    if workspace is None and need:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=student.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lx_ce_tvd_forward_backward_ex(_ptr(student), lds, _ptr(teacher), ldt, _ptr(target), BT, V,
+                                             int(ignore_index), _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t),
+                                             _ptr(sigma), _ptr(grad), ldg, float(g_ce), float(g_tvd),
+                                             _ptr(grad_ce_rows), _ptr(grad_tvd_rows), _ptr(g_scale), dt,
+                                             _ptr(workspace), wbytes, _stream(stream)),
+           "lx_ce_tvd_forward_backward_ex")
+
+
 __all__ = [
     "LxError", "lib", "LIB_PATH", "LX_OK", "LX_ERR_INVALID_ARG", "LX_ERR_UNSUPPORTED_DTYPE", "LX_ERR_ALIAS",
-    "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "lx_status_string", "lx_abi_version",
+    "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "LX_F16", "lx_status_string", "lx_abi_version",
     "lx_ce_tvd_workspace_bytes", "lx_ce_tvd_forward", "lx_ce_tvd_backward", "lx_ce_tvd_reduce_mean",
     "lx_ce_tvd_forward_backward_workspace_bytes", "lx_ce_tvd_forward_backward", "lx_ce_tvd_count_valid",
     "lx_vp_stats_floats", "lx_ce_tvd_vp_stats", "lx_ce_tvd_vp_merge_stats", "lx_ce_tvd_vp_tv", "lx_ce_tvd_vp_merge_tv",
-    "lx_ce_tvd_backward_shard",
+    "lx_ce_tvd_backward_shard", "lx_ce_tvd_forward_ex", "lx_ce_tvd_backward_ex", "lx_ce_tvd_forward_backward_ex",
 ]

@@ -21,8 +21,13 @@ int esize_of(lx_dtype dt) {
   switch (dt) {
     case LX_F32: return 4;
     case LX_BF16: return 2;
+    case LX_F16: return 2;
     default: return 0;
   }
+}
+
+lx::Dt dt_of(lx_dtype dt) {
+  return dt == LX_BF16 ? lx::Dt::BF16 : dt == LX_F16 ? lx::Dt::F16 : lx::Dt::F32;
 }
 
 // byte range [lo, hi) of an array; empty when p is NULL
@@ -48,52 +53,238 @@ lx_status check_shape(int64_t BT, int64_t V, int es) {
   return LX_OK;
 }
 
-// The backward over rows of V columns that are columns [v0, v0 + V) of rows of
-// V_total (v0 = 0, V_total = V for whole rows).
-lx_status backward_impl(void* grad, const void* student, const void* teacher, const int64_t* target, int64_t BT,
-                        int64_t V, int64_t v0, int64_t V_total, int64_t ignore_index, const float* lse_s,
-                        const float* lse_t, const float* sigma, float g_ce, float g_tvd, const float* g_scale,
-                        lx_dtype dt, void* stream) {
+// A row stride ld >= V with the last row's end, (BT - 1) * ld + V elements,
+// addressable in bytes.
+bool stride_ok(int64_t BT, int64_t V, int64_t ld, int es) {
+  if (ld < V) return false;
+  if (BT <= 1) return true;
+  return BT - 1 <= (INT64_MAX / es - V) / ld;
+}
+// bytes from the first row's start to the last row's end
+int64_t strided_bytes(int64_t BT, int64_t V, int64_t ld, int es) { return ((BT - 1) * ld + V) * es; }
+
+// Row r of a tensor starts at base + r * ld * es bytes.  Two tensors' rows
+// share their address modulo 16 on every row when their bases do and, with
+// more than one row, their strides in bytes agree modulo 16.
+bool same_mod16(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t BT, int es) {
+  if ((((uintptr_t)a - (uintptr_t)b) & 15u) != 0) return false;
+  return BT <= 1 || (((lda - ldb) * es) & 15) == 0;
+}
+// every row starts on a 16-byte boundary
+bool rows16(const void* a, int64_t ld, int64_t BT, int es) {
+  return ((uintptr_t)a & 15u) == 0 && (BT <= 1 || ((ld * es) & 15) == 0);
+}
+
+struct Tensor {
+  const void* p;
+  int64_t ld;
+};
+
+lx_status forward_impl(Tensor zs, Tensor us, const int64_t* target, int64_t BT, int64_t V, int64_t ignore_index,
+                       float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma, lx_dtype dt,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   const int es = esize_of(dt);
   if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
   if (lx_status s = check_shape(BT, V, es)) return s;
   if (BT == 0) return LX_OK;
-  const bool has_t = teacher != nullptr;
-  if (!grad || !student || !target || !lse_s) return LX_ERR_INVALID_ARG;
-  if (has_t && (!lse_t || !sigma)) return LX_ERR_INVALID_ARG;
-  if (!aligned(grad, es) || !aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) ||
-      !aligned(lse_s, 4) || (has_t && (!aligned(lse_t, 4) || !aligned(sigma, 4))) ||
-      (g_scale && !aligned(g_scale, 4)))
+  const bool has_t = us.p != nullptr;
+  if (!stride_ok(BT, V, zs.ld, es) || (has_t && !stride_ok(BT, V, us.ld, es))) return LX_ERR_INVALID_ARG;
+  if (!zs.p || !target || !ce || !lse_s) return LX_ERR_INVALID_ARG;
+  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(zs.p, es) || (has_t && !aligned(us.p, es)) || !aligned(target, 8) || !aligned(ce, 4) ||
+      !aligned(lse_s, 4))
     return LX_ERR_INVALID_ARG;
+  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
 
-  const int64_t lb = BT * V * es, fb = BT * 4;
-  const Span g = span(grad, lb);
-  const Span ins[7] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(lse_s, fb),
-                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb), span(g_scale, 4)};
-  // in place (grad == student) is allowed; any other overlap is not
-  if (grad != student && overlaps(g, ins[0])) return LX_ERR_ALIAS;
-  for (int i = 1; i < 7; ++i)
-    if (overlaps(g, ins[i])) return LX_ERR_ALIAS;
+  const int64_t fb = BT * 4;
+  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
+  Span sp[9] = {span(zs.p, strided_bytes(BT, V, zs.ld, es)),
+                span(us.p, has_t ? strided_bytes(BT, V, us.ld, es) : 0),
+                span(target, BT * 8), span(ce, fb), span(lse_s, fb),
+                span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
+                span(has_t ? sigma : nullptr, fb), span(plan.workspace_bytes ? workspace : nullptr,
+                                                         (int64_t)plan.workspace_bytes)};
+  // inputs may overlap each other (e.g. teacher == student); outputs and the
+  // workspace may overlap nothing
+  for (int o = 3; o < 9; ++o)
+    for (int i = 0; i < 9; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  if (plan.workspace_bytes) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
+  }
 
-  lx::BwdArgs a;
-  a.grad = grad;
-  a.student = student;
-  a.teacher = teacher;
+  lx::FwdArgs a;
+  a.student = zs.p;
+  a.teacher = us.p;
   a.target = target;
   a.BT = BT;
   a.V = V;
   a.ignore_index = ignore_index;
+  a.lds = zs.ld;
+  a.ldt = has_t ? us.ld : zs.ld;
+  a.ce = ce;
+  a.tvd = tvd;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.vec = (!has_t || same_mod16(zs.p, zs.ld, us.p, us.ld, BT, es)) ? 1 : 0;
+  a.rows16 = (rows16(zs.p, zs.ld, BT, es) && (!has_t || rows16(us.p, us.ld, BT, es))) ? 1 : 0;
+  a.workspace = workspace;
+  return from_hip(lx::launch_forward(a, plan, dt_of(dt), static_cast<hipStream_t>(stream)));
+}
+
+// The backward over rows of V columns that are columns [v0, v0 + V) of rows of
+// V_total (v0 = 0, V_total = V for whole rows).
+lx_status backward_impl(void* grad, int64_t ldg, Tensor zs, Tensor us, const int64_t* target, int64_t BT,
+                        int64_t V, int64_t v0, int64_t V_total, int64_t ignore_index, const float* lse_s,
+                        const float* lse_t, const float* sigma, float g_ce, float g_tvd, const float* gce_rows,
+                        const float* gtvd_rows, const float* g_scale, lx_dtype dt, void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = us.p != nullptr;
+  if (!stride_ok(BT, V, ldg, es) || !stride_ok(BT, V, zs.ld, es) || (has_t && !stride_ok(BT, V, us.ld, es)))
+    return LX_ERR_INVALID_ARG;
+  if (!grad || !zs.p || !target || !lse_s) return LX_ERR_INVALID_ARG;
+  if (has_t && (!lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(grad, es) || !aligned(zs.p, es) || (has_t && !aligned(us.p, es)) || !aligned(target, 8) ||
+      !aligned(lse_s, 4) || (has_t && (!aligned(lse_t, 4) || !aligned(sigma, 4))) ||
+      (g_scale && !aligned(g_scale, 4)) || !aligned(gce_rows, 4) || !aligned(gtvd_rows, 4))
+    return LX_ERR_INVALID_ARG;
+
+  const int64_t fb = BT * 4;
+  const Span g = span(grad, strided_bytes(BT, V, ldg, es));
+  const Span ins[9] = {span(zs.p, strided_bytes(BT, V, zs.ld, es)),
+                       span(us.p, has_t ? strided_bytes(BT, V, us.ld, es) : 0),
+                       span(target, BT * 8), span(lse_s, fb),
+                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb), span(g_scale, 4),
+                       span(gce_rows, fb), span(has_t ? gtvd_rows : nullptr, fb)};
+  // in place (grad == student with the same row stride) is allowed; any other overlap is not
+  const bool in_place = grad == zs.p && ldg == zs.ld;
+  if (!in_place && overlaps(g, ins[0])) return LX_ERR_ALIAS;
+  for (int i = 1; i < 9; ++i)
+    if (overlaps(g, ins[i])) return LX_ERR_ALIAS;
+
+  lx::BwdArgs a;
+  a.grad = grad;
+  a.student = zs.p;
+  a.teacher = us.p;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.ldg = ldg;
+  a.lds = zs.ld;
+  a.ldt = has_t ? us.ld : zs.ld;
   a.lse_s = lse_s;
   a.lse_t = lse_t;
   a.sigma = sigma;
   a.g_ce = g_ce;
   a.g_tvd = g_tvd;
+  a.gce_rows = gce_rows;
+  a.gtvd_rows = has_t ? gtvd_rows : nullptr;
   a.g_scale = g_scale;
   a.v0 = v0;
   a.V_total = V_total;
-  const uintptr_t m = (uintptr_t)student & 15u;
-  a.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
-  return from_hip(lx::launch_backward(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+  a.vec = (same_mod16(grad, ldg, zs.p, zs.ld, BT, es) && (!has_t || same_mod16(us.p, us.ld, zs.p, zs.ld, BT, es)))
+              ? 1 : 0;
+  return from_hip(lx::launch_backward(a, dt_of(dt), static_cast<hipStream_t>(stream)));
+}
+
+lx_status forward_backward_impl(Tensor zs, Tensor us, const int64_t* target, int64_t BT, int64_t V,
+                                int64_t ignore_index, float* ce, float* tvd, float* lse_s, float* lse_t,
+                                float* sigma, void* grad, int64_t ldg, float g_ce, float g_tvd,
+                                const float* gce_rows, const float* gtvd_rows, const float* g_scale, lx_dtype dt,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const int es = esize_of(dt);
+  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
+  if (lx_status s = check_shape(BT, V, es)) return s;
+  if (BT == 0) return LX_OK;
+  const bool has_t = us.p != nullptr;
+  if (!stride_ok(BT, V, ldg, es) || !stride_ok(BT, V, zs.ld, es) || (has_t && !stride_ok(BT, V, us.ld, es)))
+    return LX_ERR_INVALID_ARG;
+  if (!zs.p || !target || !ce || !lse_s || !grad) return LX_ERR_INVALID_ARG;
+  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
+  if (!aligned(zs.p, es) || (has_t && !aligned(us.p, es)) || !aligned(grad, es) || !aligned(target, 8) ||
+      !aligned(ce, 4) || !aligned(lse_s, 4) || (g_scale && !aligned(g_scale, 4)) || !aligned(gce_rows, 4) ||
+      !aligned(gtvd_rows, 4))
+    return LX_ERR_INVALID_ARG;
+  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
+
+  const int64_t fb = BT * 4;
+  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
+  const lx::ClusterPlan fused = lx::plan_fused(BT, V, es, has_t);
+  const size_t need = plan.workspace_bytes > fused.workspace_bytes ? plan.workspace_bytes : fused.workspace_bytes;
+  // 0..2 inputs (may overlap each other), 3..8 outputs and workspace, 9..11 inputs
+  Span sp[12] = {span(zs.p, strided_bytes(BT, V, zs.ld, es)),
+                 span(us.p, has_t ? strided_bytes(BT, V, us.ld, es) : 0),
+                 span(target, BT * 8), span(ce, fb), span(lse_s, fb),
+                 span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
+                 span(has_t ? sigma : nullptr, fb), span(need ? workspace : nullptr, (int64_t)need),
+                 span(g_scale, 4), span(gce_rows, fb), span(has_t ? gtvd_rows : nullptr, fb)};
+  for (int o = 3; o < 9; ++o)
+    for (int i = 0; i < 12; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  // the gradient may be the student logits themselves (in place, same row
+  // stride); any other overlap is an error
+  const Span g = span(grad, strided_bytes(BT, V, ldg, es));
+  const bool in_place = grad == zs.p && ldg == zs.ld;
+  if (!in_place && overlaps(g, sp[0])) return LX_ERR_ALIAS;
+  for (int i = 1; i < 12; ++i)
+    if (overlaps(g, sp[i])) return LX_ERR_ALIAS;
+  if (need) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
+  }
+
+  lx::FwdArgs a;
+  a.student = zs.p;
+  a.teacher = us.p;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.lds = zs.ld;
+  a.ldt = has_t ? us.ld : zs.ld;
+  a.ce = ce;
+  a.tvd = tvd;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.vec = (!has_t || same_mod16(zs.p, zs.ld, us.p, us.ld, BT, es)) ? 1 : 0;
+  a.rows16 = (rows16(zs.p, zs.ld, BT, es) && (!has_t || rows16(us.p, us.ld, BT, es))) ? 1 : 0;
+  a.workspace = workspace;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused.K > 0 && a.rows16 && rows16(grad, ldg, BT, es)) {
+    const lx::FusedGrad fg{grad, ldg, g_ce, g_tvd, gce_rows, has_t ? gtvd_rows : nullptr, g_scale};
+    return from_hip(lx::launch_fused_cluster(a, fg, fused, dt_of(dt), st));
+  }
+  // no fused kernel for this shape or layout: the forward, then the backward, on the same stream
+  if (lx_status s = from_hip(lx::launch_forward(a, plan, dt_of(dt), st))) return s;
+  lx::BwdArgs b;
+  b.grad = grad;
+  b.student = zs.p;
+  b.teacher = us.p;
+  b.target = target;
+  b.BT = BT;
+  b.V = V;
+  b.ignore_index = ignore_index;
+  b.ldg = ldg;
+  b.lds = a.lds;
+  b.ldt = a.ldt;
+  b.lse_s = lse_s;
+  b.lse_t = lse_t;
+  b.sigma = sigma;
+  b.g_ce = g_ce;
+  b.g_tvd = g_tvd;
+  b.gce_rows = gce_rows;
+  b.gtvd_rows = has_t ? gtvd_rows : nullptr;
+  b.g_scale = g_scale;
+  b.v0 = 0;
+  b.V_total = V;
+  b.vec = (same_mod16(grad, ldg, zs.p, zs.ld, BT, es) && (!has_t || same_mod16(us.p, us.ld, zs.p, zs.ld, BT, es)))
+              ? 1 : 0;
+  return from_hip(lx::launch_backward(b, dt_of(dt), st));
 }
 
 }  // namespace
@@ -125,56 +316,34 @@ size_t lx_ce_tvd_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_tea
 lx_status lx_ce_tvd_forward(const void* student, const void* teacher, const int64_t* target, int64_t BT,
                             int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s, float* lse_t,
                             float* sigma, lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
-  const int es = esize_of(dt);
-  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
-  if (lx_status s = check_shape(BT, V, es)) return s;
-  if (BT == 0) return LX_OK;
-  const bool has_t = teacher != nullptr;
-  if (!student || !target || !ce || !lse_s) return LX_ERR_INVALID_ARG;
-  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
-  if (!aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(target, 8) || !aligned(ce, 4) ||
-      !aligned(lse_s, 4))
-    return LX_ERR_INVALID_ARG;
-  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
+  return forward_impl(Tensor{student, V}, Tensor{teacher, V}, target, BT, V, ignore_index, ce, tvd, lse_s, lse_t,
+                      sigma, dt, workspace, workspace_bytes, stream);
+}
 
-  const int64_t lb = BT * V * es, fb = BT * 4;
-  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
-  Span sp[9] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(ce, fb), span(lse_s, fb),
-                span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
-                span(has_t ? sigma : nullptr, fb), span(plan.workspace_bytes ? workspace : nullptr,
-                                                         (int64_t)plan.workspace_bytes)};
-  // inputs may overlap each other (e.g. teacher == student); outputs and the
-  // workspace may overlap nothing
-  for (int o = 3; o < 9; ++o)
-    for (int i = 0; i < 9; ++i)
-      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
-  if (plan.workspace_bytes) {
-    if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
-  }
-
-  lx::FwdArgs a;
-  a.student = student;
-  a.teacher = teacher;
-  a.target = target;
-  a.BT = BT;
-  a.V = V;
-  a.ignore_index = ignore_index;
-  a.ce = ce;
-  a.tvd = tvd;
-  a.lse_s = lse_s;
-  a.lse_t = lse_t;
-  a.sigma = sigma;
-  a.vec = (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0;
-  a.workspace = workspace;
-  return from_hip(lx::launch_forward(a, plan, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+lx_status lx_ce_tvd_forward_ex(const void* student, int64_t ld_student, const void* teacher, int64_t ld_teacher,
+                               const int64_t* target, int64_t BT, int64_t V, int64_t ignore_index, float* ce,
+                               float* tvd, float* lse_s, float* lse_t, float* sigma, lx_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return forward_impl(Tensor{student, ld_student}, Tensor{teacher, ld_teacher}, target, BT, V, ignore_index, ce,
+                      tvd, lse_s, lse_t, sigma, dt, workspace, workspace_bytes, stream);
 }
 
 lx_status lx_ce_tvd_backward(void* grad, const void* student, const void* teacher, const int64_t* target,
                              int64_t BT, int64_t V, int64_t ignore_index, const float* lse_s, const float* lse_t,
                              const float* sigma, float g_ce, float g_tvd, const float* g_scale, lx_dtype dt,
                              void* stream) {
-  return backward_impl(grad, student, teacher, target, BT, V, 0, V, ignore_index, lse_s, lse_t, sigma, g_ce, g_tvd,
-                       g_scale, dt, stream);
+  return backward_impl(grad, V, Tensor{student, V}, Tensor{teacher, V}, target, BT, V, 0, V, ignore_index, lse_s,
+                       lse_t, sigma, g_ce, g_tvd, nullptr, nullptr, g_scale, dt, stream);
+}
+
+lx_status lx_ce_tvd_backward_ex(void* grad, int64_t ld_grad, const void* student, int64_t ld_student,
+                                const void* teacher, int64_t ld_teacher, const int64_t* target, int64_t BT,
+                                int64_t V, int64_t ignore_index, const float* lse_s, const float* lse_t,
+                                const float* sigma, float g_ce, float g_tvd, const float* grad_ce_rows,
+                                const float* grad_tvd_rows, const float* g_scale, lx_dtype dt, void* stream) {
+  return backward_impl(grad, ld_grad, Tensor{student, ld_student}, Tensor{teacher, ld_teacher}, target, BT, V, 0, V,
+                       ignore_index, lse_s, lse_t, sigma, g_ce, g_tvd, grad_ce_rows, grad_tvd_rows, g_scale, dt,
+                       stream);
 }
 
 lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* teacher, const int64_t* target,
@@ -182,8 +351,8 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
                                    const float* lse_s, const float* lse_t, const float* sigma, float g_ce,
                                    float g_tvd, const float* g_scale, lx_dtype dt, void* stream) {
   if (v0 < 0 || V_shard < 1 || V < 1 || v0 > V - V_shard) return LX_ERR_INVALID_ARG;
-  return backward_impl(grad, student, teacher, target, BT, V_shard, v0, V, ignore_index, lse_s, lse_t, sigma, g_ce,
-                       g_tvd, g_scale, dt, stream);
+  return backward_impl(grad, V_shard, Tensor{student, V_shard}, Tensor{teacher, V_shard}, target, BT, V_shard, v0, V,
+                       ignore_index, lse_s, lse_t, sigma, g_ce, g_tvd, nullptr, nullptr, g_scale, dt, stream);
 }
 
 size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher) {
@@ -199,79 +368,20 @@ lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, c
                                      float* lse_t, float* sigma, void* grad, float g_ce, float g_tvd,
                                      const float* g_scale, lx_dtype dt, void* workspace, size_t workspace_bytes,
                                      void* stream) {
-  const int es = esize_of(dt);
-  if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
-  if (lx_status s = check_shape(BT, V, es)) return s;
-  if (BT == 0) return LX_OK;
-  const bool has_t = teacher != nullptr;
-  if (!student || !target || !ce || !lse_s || !grad) return LX_ERR_INVALID_ARG;
-  if (has_t && (!tvd || !lse_t || !sigma)) return LX_ERR_INVALID_ARG;
-  if (!aligned(student, es) || (has_t && !aligned(teacher, es)) || !aligned(grad, es) || !aligned(target, 8) ||
-      !aligned(ce, 4) || !aligned(lse_s, 4) || (g_scale && !aligned(g_scale, 4)))
-    return LX_ERR_INVALID_ARG;
-  if (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))) return LX_ERR_INVALID_ARG;
+  return forward_backward_impl(Tensor{student, V}, Tensor{teacher, V}, target, BT, V, ignore_index, ce, tvd, lse_s,
+                               lse_t, sigma, grad, V, g_ce, g_tvd, nullptr, nullptr, g_scale, dt, workspace,
+                               workspace_bytes, stream);
+}
 
-  const int64_t lb = BT * V * es, fb = BT * 4;
-  const lx::FwdPlan plan = lx::plan_forward(BT, V, es, has_t);
-  const lx::ClusterPlan fused = lx::plan_fused(BT, V, es, has_t);
-  const size_t need = plan.workspace_bytes > fused.workspace_bytes ? plan.workspace_bytes : fused.workspace_bytes;
-  // 0..2 inputs (may overlap each other), 3..8 outputs and workspace, 9 g_scale (input)
-  Span sp[10] = {span(student, lb), span(teacher, lb), span(target, BT * 8), span(ce, fb), span(lse_s, fb),
-                 span(has_t ? tvd : nullptr, fb), span(has_t ? lse_t : nullptr, fb),
-                 span(has_t ? sigma : nullptr, fb), span(need ? workspace : nullptr, (int64_t)need),
-                 span(g_scale, 4)};
-  for (int o = 3; o < 9; ++o)
-    for (int i = 0; i < 10; ++i)
-      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
-  // the gradient may be the student logits themselves (in place); any other overlap is an error
-  const Span g = span(grad, lb);
-  if (grad != student && overlaps(g, sp[0])) return LX_ERR_ALIAS;
-  for (int i = 1; i < 10; ++i)
-    if (overlaps(g, sp[i])) return LX_ERR_ALIAS;
-  if (need) {
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
-  }
-
-  lx::FwdArgs a;
-  a.student = student;
-  a.teacher = teacher;
-  a.target = target;
-  a.BT = BT;
-  a.V = V;
-  a.ignore_index = ignore_index;
-  a.ce = ce;
-  a.tvd = tvd;
-  a.lse_s = lse_s;
-  a.lse_t = lse_t;
-  a.sigma = sigma;
-  a.vec = (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0;
-  a.workspace = workspace;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fused.K > 0 && ((((uintptr_t)student) | ((uintptr_t)teacher) | ((uintptr_t)grad)) & 15u) == 0) {
-    const lx::FusedGrad fg{grad, g_ce, g_tvd, g_scale};
-    return from_hip(lx::launch_fused_cluster(a, fg, fused, st));
-  }
-  // no fused kernel for this shape or layout: the forward, then the backward, on the same stream
-  if (lx_status s = from_hip(lx::launch_forward(a, plan, dt == LX_BF16, st))) return s;
-  lx::BwdArgs b;
-  b.grad = grad;
-  b.student = student;
-  b.teacher = teacher;
-  b.target = target;
-  b.BT = BT;
-  b.V = V;
-  b.ignore_index = ignore_index;
-  b.lse_s = lse_s;
-  b.lse_t = lse_t;
-  b.sigma = sigma;
-  b.g_ce = g_ce;
-  b.g_tvd = g_tvd;
-  b.g_scale = g_scale;
-  b.v0 = 0;
-  b.V_total = V;
-  const uintptr_t m = (uintptr_t)student & 15u;
-  b.vec = (((uintptr_t)grad & 15u) == m && (!has_t || ((uintptr_t)teacher & 15u) == m)) ? 1 : 0;
-  return from_hip(lx::launch_backward(b, dt == LX_BF16, st));
+lx_status lx_ce_tvd_forward_backward_ex(const void* student, int64_t ld_student, const void* teacher,
+                                        int64_t ld_teacher, const int64_t* target, int64_t BT, int64_t V,
+                                        int64_t ignore_index, float* ce, float* tvd, float* lse_s, float* lse_t,
+                                        float* sigma, void* grad, int64_t ld_grad, float g_ce, float g_tvd,
+                                        const float* grad_ce_rows, const float* grad_tvd_rows, const float* g_scale,
+                                        lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_backward_impl(Tensor{student, ld_student}, Tensor{teacher, ld_teacher}, target, BT, V,
+                               ignore_index, ce, tvd, lse_s, lse_t, sigma, grad, ld_grad, g_ce, g_tvd, grad_ce_rows,
+                               grad_tvd_rows, g_scale, dt, workspace, workspace_bytes, stream);
 }
 
 lx_status lx_ce_tvd_count_valid(const int64_t* target, int64_t BT, int64_t ignore_index, int64_t* n_valid,
@@ -323,7 +433,7 @@ lx_status lx_ce_tvd_vp_stats(const void* student, const void* teacher, const int
     if (overlaps(out, ins[i])) return LX_ERR_ALIAS;
   lx::VpArgs a{student, teacher, target, BT, V_shard, v0, ignore_index, nullptr, nullptr, stats,
                (!has_t || ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u)) ? 1 : 0};
-  return from_hip(lx::launch_vp_stats(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+  return from_hip(lx::launch_vp_stats(a, dt_of(dt), static_cast<hipStream_t>(stream)));
 }
 
 lx_status lx_ce_tvd_vp_merge_stats(const float* stats, int64_t n_shards, const int64_t* target, int64_t BT,
@@ -365,7 +475,7 @@ lx_status lx_ce_tvd_vp_tv(const void* student, const void* teacher, const int64_
     if (overlaps(out, ins[i])) return LX_ERR_ALIAS;
   lx::VpArgs a{student, teacher, target, BT, V_shard, 0, ignore_index, lse_s, lse_t, tv,
                ((uintptr_t)student & 15u) == ((uintptr_t)teacher & 15u) ? 1 : 0};
-  return from_hip(lx::launch_vp_tv(a, dt == LX_BF16, static_cast<hipStream_t>(stream)));
+  return from_hip(lx::launch_vp_tv(a, dt_of(dt), static_cast<hipStream_t>(stream)));
 }
 
 lx_status lx_ce_tvd_vp_merge_tv(const float* tv, int64_t n_shards, const int64_t* target, int64_t BT,

@@ -8,6 +8,8 @@
 //   s_v = sign(p_v - q_v), sign(0) = 0,
 //
 // is written, with the target element's -g_ce added by the lane that owns it.
+// g_ce and g_tvd may carry per-row factors (the upstream gradient of an
+// unreduced, per-row loss), read once per (row, chunk).
 // Per row this is p_v * (alpha + beta * s_v) with alpha = k * (g_ce - 0.5 *
 // g_tvd * sigma) and beta = 0.5 * k * g_tvd.  The sign is read off the
 // exponent arguments of p and q (common.hpp), so q itself is never formed:
@@ -38,9 +40,11 @@ constexpr int kMaxGrid = 1 << 20;
 template <typename T, bool TEACHER, int NT, int UNR>
 __global__ __launch_bounds__(NT) void bwd_kernel(
     T* grad, const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
-    int64_t BT, int V, int64_t v0, int64_t V_total, int64_t ignore_index, int vec, int chunks_per_row,
+    int64_t BT, int V, int64_t ldg, int64_t lds, int64_t ldt, int64_t v0, int64_t V_total,
+    int64_t ignore_index, int vec, int chunks_per_row,
     const float* __restrict__ lse_s, const float* __restrict__ lse_t, const float* __restrict__ sigma,
-    float g_ce, float g_tvd, const float* __restrict__ g_scale) {
+    float g_ce, float g_tvd, const float* __restrict__ gce_rows, const float* __restrict__ gtvd_rows,
+    const float* __restrict__ g_scale) {
   const int tid = threadIdx.x;
   const float k = g_scale ? *g_scale : 1.0f;
   const int64_t tiles = BT * (int64_t)chunks_per_row;
@@ -48,9 +52,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const int64_t r = tile / chunks_per_row;
     const int c = (int)(tile - r * chunks_per_row);
     const int64_t t = target[r];
-    T* gr = grad + r * (int64_t)V;
-    const T* z = student + r * (int64_t)V;
-    const T* u = TEACHER ? teacher + r * (int64_t)V : nullptr;
+    T* gr = grad + r * ldg;
+    const T* z = student + r * lds;
+    const T* u = TEACHER ? teacher + r * ldt : nullptr;
     const RowLayout L = row_layout(z, V, vec);
     const int nsc = L.head + L.tail;
     // this chunk's groups and scalar elements
@@ -77,8 +81,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const int tc = (t >= v0 && t - v0 < V) ? (int)(t - v0) : -1;
     const float nbs = TEACHER ? pq_bias(lse_s[r]) : neg_scaled(lse_s[r]);
     const float nbt = TEACHER ? pq_bias(lse_t[r]) : 0.0f;
-    const float kce = k * g_ce;
-    const float beta = TEACHER ? 0.5f * k * g_tvd : 0.0f;
+    const float kce = k * g_ce * (gce_rows ? gce_rows[r] : 1.0f);
+    const float beta = TEACHER ? 0.5f * k * g_tvd * (gtvd_rows ? gtvd_rows[r] : 1.0f) : 0.0f;
     const float alpha = TEACHER ? kce - beta * sigma[r] : kce;
     const float a1 = TEACHER ? alpha * 0x1p-15f : alpha;
     const float b1 = beta * kTvScale;
@@ -137,17 +141,22 @@ static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
   const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
   hipLaunchKernelGGL((bwd_kernel<T, TEACHER, kBwdThreads, kBwdUnroll>), dim3(grid), dim3(kBwdThreads), 0, st,
                      static_cast<T*>(a.grad), static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
-                     a.target, a.BT, V, a.v0, a.V_total, a.ignore_index, a.vec, chunks, a.lse_s, a.lse_t, a.sigma, a.g_ce,
-                     a.g_tvd, a.g_scale);
+                     a.target, a.BT, V, a.ldg, a.lds, a.ldt, a.v0, a.V_total, a.ignore_index, a.vec, chunks, a.lse_s,
+                     a.lse_t, a.sigma, a.g_ce, a.g_tvd, a.gce_rows, a.gtvd_rows, a.g_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream) {
-  const bool teacher = a.teacher != nullptr;
-  if (bf16) {
-    return teacher ? launch_backward_t<uint16_t, true>(a, stream) : launch_backward_t<uint16_t, false>(a, stream);
+template <typename T>
+static hipError_t launch_backward_dt(const BwdArgs& a, hipStream_t stream) {
+  return a.teacher ? launch_backward_t<T, true>(a, stream) : launch_backward_t<T, false>(a, stream);
+}
+
+hipError_t launch_backward(const BwdArgs& a, Dt dt, hipStream_t stream) {
+  switch (dt) {
+    case Dt::BF16: return launch_backward_dt<uint16_t>(a, stream);
+    case Dt::F16: return launch_backward_dt<_Float16>(a, stream);
+    default: return launch_backward_dt<float>(a, stream);
   }
-  return teacher ? launch_backward_t<float, true>(a, stream) : launch_backward_t<float, false>(a, stream);
 }
 
 }  // namespace lx

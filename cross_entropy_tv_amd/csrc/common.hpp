@@ -2,7 +2,8 @@
 //
 // Numerics (the same helpers serve the forward and the backward, so both
 // passes form p, q and sign(p - q) with the same instruction sequence):
-//   * logits are widened to f32 (bf16 -> f32 is exact), all arithmetic is f32;
+//   * logits are widened to f32 (bf16 and binary16 -> f32 are exact), all
+//     arithmetic is f32;
 //   * exp(x - lse) is evaluated as exp2(fma(x, log2 e, -lse * log2 e)), one
 //     rounding before the hardware v_exp_f32;
 //   * running maxima start at kMFloor, a finite floor, so every rescale factor
@@ -70,6 +71,26 @@ __device__ __forceinline__ void load8_stream(const float* p, float (&x)[8]) {
 __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
+// IEEE binary16 logits: widened to f32 exactly (v_cvt_f32_f16).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack_f16x2(uint32_t w, float& a, float& b) {
+  const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+  a = (float)h.x;
+  b = (float)h.y;
+}
+__device__ __forceinline__ void load8(const _Float16* p, float (&x)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  unpack_f16x2(w.x, x[0], x[1]); unpack_f16x2(w.y, x[2], x[3]);
+  unpack_f16x2(w.z, x[4], x[5]); unpack_f16x2(w.w, x[6], x[7]);
+}
+__device__ __forceinline__ void load8_stream(const _Float16* p, float (&x)[8]) {
+  const u32x4v_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+  const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  unpack_f16x2(w0, x[0], x[1]); unpack_f16x2(w1, x[2], x[3]);
+  unpack_f16x2(w2, x[4], x[5]); unpack_f16x2(w3, x[6], x[7]);
+}
+__device__ __forceinline__ float load1(const _Float16* p) { return (float)*p; }
+
 // ------------------------------------------------------------------ stores
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -103,11 +124,30 @@ __device__ __forceinline__ void store1(uint16_t* p, float g) {
 }
 __device__ __forceinline__ void store1(float* p, float g) { *p = g; }
 
+// binary16 gradients: rounded to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, (f16x2_t){(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ void store8(_Float16* p, const float (&g)[8]) {
+  uint4 w;
+  w.x = pack_f16x2_rne(g[0], g[1]); w.y = pack_f16x2_rne(g[2], g[3]);
+  w.z = pack_f16x2_rne(g[4], g[5]); w.w = pack_f16x2_rne(g[6], g[7]);
+  *reinterpret_cast<uint4*>(p) = w;
+}
+__device__ __forceinline__ void store8_stream(_Float16* p, const float (&g)[8]) {
+  u32x4v_t w;
+  w.x = pack_f16x2_rne(g[0], g[1]); w.y = pack_f16x2_rne(g[2], g[3]);
+  w.z = pack_f16x2_rne(g[4], g[5]); w.w = pack_f16x2_rne(g[6], g[7]);
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4v_t*>(p));
+}
+__device__ __forceinline__ void store1(_Float16* p, float g) { *p = (_Float16)g; }
+
 // Quiet-NaN bit patterns.  The kernels are compiled with NaNs assumed absent
 // from floating-point arithmetic, so a NaN the ABI promises as an output is
 // written as an integer bit pattern and never produced by an FP operation.
 constexpr uint32_t kQNaN32 = 0x7fc00000u;
-constexpr uint16_t kQNaN16 = 0x7fc0u;
+constexpr uint16_t kQNaN16 = 0x7fc0u;      // bf16
+constexpr uint16_t kQNaNHalf = 0x7e00u;    // binary16
 
 __device__ __forceinline__ void store_bits1(uint16_t* p, uint32_t f32bits) { *p = (uint16_t)(f32bits >> 16); }
 __device__ __forceinline__ void store_bits1(float* p, uint32_t f32bits) { *reinterpret_cast<uint32_t*>(p) = f32bits; }
@@ -119,6 +159,15 @@ __device__ __forceinline__ void store_bits8(uint16_t* p, uint32_t f32bits) {
 __device__ __forceinline__ void store_bits8(float* p, uint32_t f32bits) {
   reinterpret_cast<uint4*>(p)[0] = make_uint4(f32bits, f32bits, f32bits, f32bits);
   reinterpret_cast<uint4*>(p)[1] = make_uint4(f32bits, f32bits, f32bits, f32bits);
+}
+// binary16: the fills are +0.0 (f32 bits 0) and a quiet NaN (any other pattern)
+__device__ __forceinline__ uint16_t half_fill(uint32_t f32bits) { return f32bits ? kQNaNHalf : (uint16_t)0; }
+__device__ __forceinline__ void store_bits1(_Float16* p, uint32_t f32bits) {
+  *reinterpret_cast<uint16_t*>(p) = half_fill(f32bits);
+}
+__device__ __forceinline__ void store_bits8(_Float16* p, uint32_t f32bits) {
+  const uint32_t h = half_fill(f32bits), w = h | (h << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w, w, w, w);
 }
 __device__ __forceinline__ void store_nan(float* p) { *reinterpret_cast<uint32_t*>(p) = kQNaN32; }
 

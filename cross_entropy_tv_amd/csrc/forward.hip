@@ -70,7 +70,7 @@ __device__ __forceinline__ void load8_row(const T* p, float (&x)[8]) {
 template <typename T, bool TEACHER, int NT>
 __global__ __launch_bounds__(NT) void fwd_row_kernel(
     const T* __restrict__ student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
-    int64_t BT, int V, int64_t ignore_index, int vec,
+    int64_t BT, int V, int64_t lds, int64_t ldt, int64_t ignore_index, int vec,
     float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
     float* __restrict__ lse_t_out, float* __restrict__ sigma_out) {
   __shared__ Lse red_s[NT / 64];
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
       }
       continue;
     }
-    const T* z = student + r * (int64_t)V;
-    const T* u = TEACHER ? teacher + r * (int64_t)V : nullptr;
+    const T* z = student + r * lds;
+    const T* u = TEACHER ? teacher + r * ldt : nullptr;
     const RowLayout L = row_layout(z, V, vec);
     const int nsc = L.head + L.tail;
     const T* zb = z + L.head;
@@ -192,7 +192,7 @@ __device__ __forceinline__ ChunkRange chunk_range(const RowLayout& L, int c, int
 template <typename T, bool TEACHER, int NT>
 __global__ __launch_bounds__(NT) void fwd_split_stage1(
     const T* __restrict__ student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
-    int64_t BT, int V, int64_t ignore_index, int vec, int S, float* __restrict__ ws1) {
+    int64_t BT, int V, int64_t lds, int64_t ldt, int64_t ignore_index, int vec, int S, float* __restrict__ ws1) {
   __shared__ Lse red_s[NT / 64];
   __shared__ Lse red_t[NT / 64];
   const int tid = threadIdx.x;
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(NT) void fwd_split_stage1(
     const int64_t r = tile / S;
     const int c = (int)(tile - r * S);
     if (target[r] == ignore_index) continue;
-    const T* z = student + r * (int64_t)V;
-    const T* u = TEACHER ? teacher + r * (int64_t)V : nullptr;
+    const T* z = student + r * lds;
+    const T* u = TEACHER ? teacher + r * ldt : nullptr;
     const RowLayout L = row_layout(z, V, vec);
     const ChunkRange R = chunk_range(L, c, S);
     Lse as = lse_init(), at = lse_init();
@@ -236,7 +236,8 @@ __global__ __launch_bounds__(NT) void fwd_split_stage1(
 template <typename T, bool TEACHER, int NT>
 __global__ __launch_bounds__(NT) void fwd_split_stage2(
     const T* __restrict__ student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
-    int64_t BT, int V, int64_t ignore_index, int vec, int S, const float* __restrict__ ws1,
+    int64_t BT, int V, int64_t lds, int64_t ldt, int64_t ignore_index, int vec, int S,
+    const float* __restrict__ ws1,
     float* __restrict__ ws2, float* __restrict__ ce, float* __restrict__ lse_s_out,
     float* __restrict__ lse_t_out) {
   __shared__ float red_f[2][NT / 64];
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(NT) void fwd_split_stage2(
     }
     const float lse_s = lse_value(fs);
     const float lse_t = TEACHER ? lse_value(ft) : 0.0f;
-    const T* z = student + r * (int64_t)V;
+    const T* z = student + r * lds;
     if (c == 0 && tid == 0) {
       store_ce(ce + r, z, t, V, lse_s);
       lse_s_out[r] = lse_s;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(NT) void fwd_split_stage2(
     }
     if (!TEACHER) continue;
 
-    const T* u = teacher + r * (int64_t)V;
+    const T* u = teacher + r * ldt;
     const RowLayout L = row_layout(z, V, vec);
     const ChunkRange R = chunk_range(L, c, S);
     const float nbs = pq_bias(lse_s), nbt = pq_bias(lse_t);
@@ -334,8 +335,8 @@ static hipError_t launch_forward_t(const FwdArgs& a, const FwdPlan& plan, hipStr
   if (plan.split <= 1) {
     const int grid = (int)(a.BT < kMaxGrid ? a.BT : kMaxGrid);
     hipLaunchKernelGGL((fwd_row_kernel<T, TEACHER, kRowThreads>), dim3(grid), dim3(kRowThreads), 0, st,
-                       zs, us, a.target, a.BT, V, a.ignore_index, a.vec, a.ce, a.tvd, a.lse_s, a.lse_t,
-                       a.sigma);
+                       zs, us, a.target, a.BT, V, a.lds, a.ldt, a.ignore_index, a.vec, a.ce, a.tvd, a.lse_s,
+                       a.lse_t, a.sigma);
     return hipGetLastError();
   }
   const int S = plan.split;
@@ -344,11 +345,12 @@ static hipError_t launch_forward_t(const FwdArgs& a, const FwdPlan& plan, hipStr
   const int64_t tiles = a.BT * (int64_t)S;
   const int g1 = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
   hipLaunchKernelGGL((fwd_split_stage1<T, TEACHER, kSplitThreads>), dim3(g1), dim3(kSplitThreads), 0, st,
-                     zs, us, a.target, a.BT, V, a.ignore_index, a.vec, S, ws1);
+                     zs, us, a.target, a.BT, V, a.lds, a.ldt, a.ignore_index, a.vec, S, ws1);
   const int64_t tiles2 = TEACHER ? tiles : a.BT;
   const int g2 = (int)(tiles2 < kMaxGrid ? tiles2 : kMaxGrid);
   hipLaunchKernelGGL((fwd_split_stage2<T, TEACHER, kSplitThreads>), dim3(g2), dim3(kSplitThreads), 0, st,
-                     zs, us, a.target, a.BT, V, a.ignore_index, a.vec, S, ws1, ws2, a.ce, a.lse_s, a.lse_t);
+                     zs, us, a.target, a.BT, V, a.lds, a.ldt, a.ignore_index, a.vec, S, ws1, ws2, a.ce, a.lse_s,
+                     a.lse_t);
   if (TEACHER) {
     const int64_t b3 = (a.BT + 255) / 256;
     const int g3 = (int)(b3 < kMaxGrid ? b3 : kMaxGrid);
@@ -358,16 +360,19 @@ static hipError_t launch_forward_t(const FwdArgs& a, const FwdPlan& plan, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream) {
-  const bool teacher = a.teacher != nullptr;
-  // the read-once path needs both rows on 16-byte boundaries (V % 8 == 0 keeps every row there)
-  if (plan.cluster.K > 0 && ((((uintptr_t)a.student) | ((uintptr_t)a.teacher)) & 15u) == 0)
-    return launch_forward_cluster(a, plan.cluster, stream);
-  if (bf16) {
-    return teacher ? launch_forward_t<uint16_t, true>(a, plan, stream)
-                   : launch_forward_t<uint16_t, false>(a, plan, stream);
+template <typename T>
+static hipError_t launch_forward_dt(const FwdArgs& a, const FwdPlan& plan, hipStream_t stream) {
+  return a.teacher ? launch_forward_t<T, true>(a, plan, stream) : launch_forward_t<T, false>(a, plan, stream);
+}
+
+hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, Dt dt, hipStream_t stream) {
+  // the read-once path needs every student and teacher row on a 16-byte boundary
+  if (plan.cluster.K > 0 && a.rows16) return launch_forward_cluster(a, plan.cluster, dt, stream);
+  switch (dt) {
+    case Dt::BF16: return launch_forward_dt<uint16_t>(a, plan, stream);
+    case Dt::F16: return launch_forward_dt<_Float16>(a, plan, stream);
+    default: return launch_forward_dt<float>(a, plan, stream);
   }
-  return teacher ? launch_forward_t<float, true>(a, plan, stream) : launch_forward_t<float, false>(a, plan, stream);
 }
 
 }  // namespace lx

@@ -54,8 +54,8 @@ constexpr int kStreamPolicy = 2;            // cache policy of the loads: non-te
 // Buffer resource covering `bytes` bytes from p: loads past the end return 0
 // without touching memory, so a thread's loads need no branch around them
 // (which would also keep the compiler from waiting on them one at a time).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint16_t* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, bytes, kRsrcFlags);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kRsrcFlags);
 }
 __device__ __forceinline__ u32x4_t ld_stream(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kStreamPolicy));
@@ -64,11 +64,28 @@ __device__ __forceinline__ void st_stream(__amdgpu_buffer_rsrc_t rs, int byte_of
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, byte_off, 0, kStreamPolicy);
 }
 
+// Two logits packed in a 32-bit word, widened to f32: T = uint16_t holds
+// bf16, T = _Float16 binary16.
+template <typename T>
+__device__ __forceinline__ void unpack2(unsigned w, float& a, float& b);
+template <>
+__device__ __forceinline__ void unpack2<uint16_t>(unsigned w, float& a, float& b) {
+  a = __uint_as_float(w << 16);
+  b = __uint_as_float(w & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void unpack2<_Float16>(unsigned w, float& a, float& b) {
+  unpack_f16x2(w, a, b);
+}
+// (the words are copied out first: a bit cast applied to the element
+// expression w.y itself is compiled as a cast of w.x)
+template <typename T>
 __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
-  x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
-  x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
-  x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
-  x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  unpack2<T>(w0, x[0], x[1]);
+  unpack2<T>(w1, x[2], x[3]);
+  unpack2<T>(w2, x[4], x[5]);
+  unpack2<T>(w3, x[6], x[7]);
 }
 
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
@@ -94,9 +111,10 @@ __device__ __forceinline__ void launder(u32x4_t& w) {
 }
 
 // sum of exp(x - m) over one group, m given as nb = -m * log2(e)
+template <typename T>
 __device__ __forceinline__ void expsum8(const u32x4_t& w, float nb, float& s0, float& s1) {
   float x[8];
-  unpack8(w, x);
+  unpack8<T>(w, x);
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     s0 += exp2_hw(__builtin_fmaf(x[e], kLog2e, nb));
@@ -107,11 +125,12 @@ __device__ __forceinline__ void expsum8(const u32x4_t& w, float nb, float& s0, f
 // step-2 accumulation of one group pair (nbs, nbt from pq_bias): S += p' s'
 // and Q += q' s', so that, times kTvScale, S is sum p * sign(p - q) and
 // S - Q is sum |p - q|
+template <typename T>
 __device__ __forceinline__ void tv8(const u32x4_t& wz, const u32x4_t& wu, float nbs, float nbt, float& Q0,
                                     float& Q1, float& S0, float& S1) {
   float x[8], y[8];
-  unpack8(wz, x);
-  unpack8(wu, y);
+  unpack8<T>(wz, x);
+  unpack8<T>(wu, y);
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     const float ap0 = exparg(x[e], nbs), aq0 = exparg(y[e], nbt);
@@ -129,14 +148,8 @@ __device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, (h2_t){(_Float16)a, (_Float16)b});
 }
 __device__ __forceinline__ h2_t as_h2(unsigned v) { return __builtin_bit_cast(h2_t, v); }
-// (the words are copied out first: a bit cast applied to the element
-// expression w.y itself is compiled as a cast of w.x)
-__device__ __forceinline__ void unpack8_f16(const u32x4_t& w, float (&x)[8]) {
-  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-  const h2_t a = as_h2(w0), b = as_h2(w1), c = as_h2(w2), d = as_h2(w3);
-  x[0] = (float)a.x; x[1] = (float)a.y; x[2] = (float)b.x; x[3] = (float)b.y;
-  x[4] = (float)c.x; x[5] = (float)c.y; x[6] = (float)d.x; x[7] = (float)d.y;
-}
+// the fp16 p' / s' words of the one-pass kernel
+__device__ __forceinline__ void unpack8_f16(const u32x4_t& w, float (&x)[8]) { unpack8<_Float16>(w, x); }
 
 // The one-pass kernel keeps p' = 2^kPqBias * p in fp16 for step 3: normal
 // down to p = 2^-29 and below 32768 for p <= 1.  The signs s' = 2^-24 * sign
@@ -160,10 +173,14 @@ constexpr float kKeepP16Bound = 2.08e-3f;
 // As tv8, and keeps what step 3 needs in place of the two groups' logits:
 // p' in wz and s' in wu, both as fp16, one 32-bit word (two elements) at a
 // time so that few values are live at once.
+template <typename T>
 __device__ __forceinline__ void tv2_signs(unsigned& zw, unsigned& uw, float nbs, float nbt, float& Q0, float& Q1,
                                           float& S0, float& S1) {
-  const float ap0 = exparg(__uint_as_float(zw << 16), nbs), ap1 = exparg(__uint_as_float(zw & 0xffff0000u), nbs);
-  const float aq0 = exparg(__uint_as_float(uw << 16), nbt), aq1 = exparg(__uint_as_float(uw & 0xffff0000u), nbt);
+  float z0, z1, u0, u1;
+  unpack2<T>(zw, z0, z1);
+  unpack2<T>(uw, u0, u1);
+  const float ap0 = exparg(z0, nbs), ap1 = exparg(z1, nbs);
+  const float aq0 = exparg(u0, nbt), aq1 = exparg(u1, nbt);
   const float s0 = sign_eps(ap0, aq0), s1 = sign_eps(ap1, aq1);
   const float p0 = exp2_hw(ap0), p1 = exp2_hw(ap1);
   S0 = __builtin_fmaf(p0, s0, S0);
@@ -173,25 +190,35 @@ __device__ __forceinline__ void tv2_signs(unsigned& zw, unsigned& uw, float nbs,
   zw = pack_f16x2(p0, p1);
   uw = pack_f16x2(s0, s1);
 }
+template <typename T>
 __device__ __forceinline__ void tv8_signs(u32x4_t& wz, u32x4_t& wu, float nbs, float nbt, float& Q0, float& Q1,
                                           float& S0, float& S1) {
   unsigned z0 = wz.x, z1 = wz.y, z2 = wz.z, z3 = wz.w;
   unsigned u0 = wu.x, u1 = wu.y, u2 = wu.z, u3 = wu.w;
-  tv2_signs(z0, u0, nbs, nbt, Q0, Q1, S0, S1);
-  tv2_signs(z1, u1, nbs, nbt, Q0, Q1, S0, S1);
-  tv2_signs(z2, u2, nbs, nbt, Q0, Q1, S0, S1);
-  tv2_signs(z3, u3, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs<T>(z0, u0, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs<T>(z1, u1, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs<T>(z2, u2, nbs, nbt, Q0, Q1, S0, S1);
+  tv2_signs<T>(z3, u3, nbs, nbt, Q0, Q1, S0, S1);
   wz = (u32x4_t){z0, z1, z2, z3};
   wu = (u32x4_t){u0, u1, u2, u3};
 }
 
-// eight gradients rounded to bf16 (nearest even), and eight bf16 quiet NaNs
-__device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
-  return (u32x4_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                   pack_bf16x2(o[6], o[7])};
+// eight gradients rounded to nearest even in the logits' type (bf16 or
+// binary16), and eight quiet NaNs of that type
+template <typename T>
+__device__ __forceinline__ unsigned pack_grad2(float a, float b) {
+  if constexpr (__is_same(T, _Float16)) return pack_f16x2_rne(a, b);
+  else return pack_bf16x2(a, b);
 }
+template <typename T>
+__device__ __forceinline__ u32x4_t pack8(const float (&o)[8]) {
+  return (u32x4_t){pack_grad2<T>(o[0], o[1]), pack_grad2<T>(o[2], o[3]), pack_grad2<T>(o[4], o[5]),
+                   pack_grad2<T>(o[6], o[7])};
+}
+template <typename T>
 __device__ __forceinline__ u32x4_t nan8() {
-  const unsigned h = kQNaN16 | (kQNaN16 << 16);
+  const unsigned q = __is_same(T, _Float16) ? kQNaNHalf : kQNaN16;
+  const unsigned h = q | (q << 16);
   return (u32x4_t){h, h, h, h};
 }
 
@@ -203,6 +230,7 @@ __device__ __forceinline__ u32x4_t nan8() {
 // the optimiser: p * t + zero is the product (a zero product comes out +0)
 // but, unlike p * t, maps to one mixed-precision multiply-add that reads the
 // fp16 half directly.
+template <typename T>
 __device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, float a1, float b1, float zero,
                                         int rel, float pt, float kce) {
   float p[8], sg[8], o[8];
@@ -214,7 +242,7 @@ __device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, f
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], b1, a1) - kce : o[e];
   }
-  return pack8(o);
+  return pack8<T>(o);
 }
 
 // true when one of the eight fp16 values of w exceeds thr
@@ -225,12 +253,13 @@ __device__ __forceinline__ bool any_above(const u32x4_t& w, _Float16 thr) {
   return m.x > thr || m.y > thr;
 }
 
-// As grad8 with p' recomputed in fp32 from the student's bf16 logits wz (nbs
+// As grad8 with p' recomputed in fp32 from the student's logits wz (nbs
 // from pq_bias), so the target element needs only - kce.
+template <typename T>
 __device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t& ws, float nbs, int rel, float a1,
                                               float b1, float kce) {
   float x[8], sg[8], o[8];
-  unpack8(wz, x);
+  unpack8<T>(wz, x);
   unpack8_f16(ws, sg);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = exp2_hw(exparg(x[e], nbs)) * __builtin_fmaf(sg[e], b1, a1);
@@ -238,7 +267,7 @@ __device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t&
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
   }
-  return pack8(o);
+  return pack8<T>(o);
 }
 
 // Lanes [0, n) of wave 0 poll slots sl[0..n) until none is empty (or the
@@ -284,13 +313,14 @@ __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* 
 // Each member has read its whole chunk, and the member holding the target its
 // logit, before any member stores, so the gradient may overwrite the student
 // logits.
-template <int NT, int G, int GL, int WPE, bool FUSED>
+template <typename T, int NT, int G, int GL, int WPE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teacher,
-                    const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int gpm,
+void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target, int V,
+                    int64_t lds, int64_t ldt, int64_t ldg, int64_t ignore_index, int K, int gpm,
                     float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
-                    float* __restrict__ lse_t_out, float* __restrict__ sigma_out, uint16_t* grad, float g_ce,
-                    float g_tvd, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
+                    float* __restrict__ lse_t_out, float* __restrict__ sigma_out, T* grad, float g_ce,
+                    float g_tvd, const float* __restrict__ gce_rows, const float* __restrict__ gtvd_rows,
+                    const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
                     uint64_t* __restrict__ slot2, unsigned* __restrict__ arrived, unsigned* __restrict__ ticket) {
   constexpr int W = NT / 64;
   __shared__ Lse red_z[W], red_u[W];
@@ -313,13 +343,13 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   const int NG = V >> 3;
   const int gb = j * gpm;
   const int ge = min(NG, gb + gpm);
-  const int64_t row = r * (int64_t)V;
+  const int64_t rowz = r * lds, rowu = r * ldt, rowg = r * ldg;
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
       ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
     }
     if (FUSED) {
-      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
 #pragma unroll
       for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
     }
@@ -334,11 +364,10 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   // reads its logit and, in the one-pass kernel, writes the row's outputs
   const int jt = t_ok ? (int)(t >> 3) / gpm : 0;
   float zt = 0.f;
-  if (FUSED && j == jt && tid == 0 && t_ok) zt = load1(student + row + t);
+  if (FUSED && j == jt && tid == 0 && t_ok) zt = load1(student + rowz + t);
 
-
-  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
-  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + rowz + 8 * (int64_t)gb, (ge - gb) * 16);
+  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + rowu + 8 * (int64_t)gb, (ge - gb) * 16);
   u32x4_t rz[G], ru[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -348,9 +377,9 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   if (GL > 0 && cnt > NT * G) {
     // the rest of the chunk goes straight to LDS, 64 groups (1 KB) per load
     const int lcnt = cnt - NT * G;
-    const int64_t lo = row + 8 * (int64_t)(gb + NT * G);
-    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + lo, lcnt * 16);
-    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + lo, lcnt * 16);
+    const int64_t lo = 8 * (int64_t)(gb + NT * G);
+    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + rowz + lo, lcnt * 16);
+    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + rowu + lo, lcnt * 16);
     const int lane = tid & 63;
     for (int b = tid >> 6; b < (lcnt + 63) >> 6; b += NT / 64) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrz, (__attribute__((address_space(3))) void*)&lz[b * 64], 16,
@@ -364,8 +393,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   float mz = kMFloor, mu = kMFloor;
   if (n > 0) {
     float x[8], y[8];
-    unpack8(rz[0], x);
-    unpack8(ru[0], y);
+    unpack8<T>(rz[0], x);
+    unpack8<T>(ru[0], y);
     mz = fmaxf(mz, max8(x));
     mu = fmaxf(mu, max8(y));
   }
@@ -375,8 +404,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       if (i < n) {
-        expsum8(rz[i], nbz, sz0, sz1);
-        expsum8(ru[i], nbu, su0, su1);
+        expsum8<T>(rz[i], nbz, sz0, sz1);
+        expsum8<T>(ru[i], nbu, su0, su1);
       }
     }
     if (GL > 0) {
@@ -384,8 +413,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
 #pragma unroll
       for (int i = 0; i < GL; ++i) {
         if (i < nl) {
-          expsum8(lz[tid + i * NT], nbz, sz0, sz1);
-          expsum8(lu[tid + i * NT], nbu, su0, su1);
+          expsum8<T>(lz[tid + i * NT], nbz, sz0, sz1);
+          expsum8<T>(lu[tid + i * NT], nbu, su0, su1);
         }
       }
     }
@@ -398,16 +427,16 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
         launder(rz[i]);
         launder(ru[i]);
         float x[8], y[8];
-        unpack8(rz[i], x);
-        unpack8(ru[i], y);
+        unpack8<T>(rz[i], x);
+        unpack8<T>(ru[i], y);
         mz = fmaxf(mz, max8(x));
         mu = fmaxf(mu, max8(y));
       }
     }
     for (int i = 0; i < nl; ++i) {
       float x[8], y[8];
-      unpack8(lz[tid + i * NT], x);
-      unpack8(lu[tid + i * NT], y);
+      unpack8<T>(lz[tid + i * NT], x);
+      unpack8<T>(lu[tid + i * NT], y);
       mz = fmaxf(mz, max8(x));
       mu = fmaxf(mu, max8(y));
     }
@@ -418,13 +447,13 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       if (i < n) {
         launder(rz[i]);
         launder(ru[i]);
-        expsum8(rz[i], nbz, sz0, sz1);
-        expsum8(ru[i], nbu, su0, su1);
+        expsum8<T>(rz[i], nbz, sz0, sz1);
+        expsum8<T>(ru[i], nbu, su0, su1);
       }
     }
     for (int i = 0; i < nl; ++i) {
-      expsum8(lz[tid + i * NT], nbz, sz0, sz1);
-      expsum8(lu[tid + i * NT], nbu, su0, su1);
+      expsum8<T>(lz[tid + i * NT], nbz, sz0, sz1);
+      expsum8<T>(lu[tid + i * NT], nbu, su0, su1);
     }
   }
   {
@@ -475,8 +504,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       if (i < n) {
         launder(rz[i]);
         launder(ru[i]);
-        if (FUSED) tv8_signs(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
-        else tv8(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
+        if (FUSED) tv8_signs<T>(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
+        else tv8<T>(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
       }
     }
 #pragma unroll
@@ -484,11 +513,11 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       if (i < nl) {
         u32x4_t wz = lz[tid + i * NT], wu = lu[tid + i * NT];
         if (FUSED) {
-          tv8_signs(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
+          tv8_signs<T>(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
           lz[tid + i * NT] = wz;  // this thread's own slots: read back by it in step 3
           lu[tid + i * NT] = wu;
         } else {
-          tv8(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
+          tv8<T>(wz, wu, nbs, nbt, Q0, Q1, S0, S1);
         }
       }
     }
@@ -518,7 +547,7 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     }
     old = __shfl(old, 0, 64);
     if (old != (unsigned)(K - 1)) return;
-    if (tid == 0 && t_ok) zt = load1(student + row + t);
+    if (tid == 0 && t_ok) zt = load1(student + rowz + t);
     wait_slots(s2, K, got);
     if (tid == 0) {
       float A = lo_f(got[0]), S = hi_f(got[0]);
@@ -567,23 +596,24 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
   // ---- step 3: g = p * (alpha + beta * sign) - k * g_ce * [v == t]
   //             = p' * (a1 + b1 * s') - k * g_ce * [v == t]
   const float k = g_scale ? *g_scale : 1.0f;
-  const float kce = k * g_ce;
-  const float beta = 0.5f * k * g_tvd;
+  const float gce = g_ce * (gce_rows ? gce_rows[r] : 1.0f), gtvd = g_tvd * (gtvd_rows ? gtvd_rows[r] : 1.0f);
+  const float kce = k * gce;
+  const float beta = 0.5f * k * gtvd;
   const float alpha = kce - beta * s_bc[2];
   const float a1 = alpha * kInvPqBias, b1 = beta * kTvScale;
-  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
   // target element relative to the chunk; only the member holding it reads pt
   const int trel = j == jt ? (int)(t - 8 * (int64_t)gb) : -1;
   if (!t_ok) {
     // a target outside [0, V) makes the row's gradient NaN
 #pragma unroll
-    for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, nan8());
+    for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, nan8<T>());
     return;
   }
   const float pt = exp2_hw(exparg(s_zt, nbs));
   float zero = 0.f;
   asm volatile("" : "+v"(zero));
-  const float M = k * (fabsf(g_ce) + fabsf(g_tvd));
+  const float M = k * (fabsf(gce) + fabsf(gtvd));
   if (!(M <= kKeepP16Bound)) {
     // A group holding a p' = 2^kPqBias * p above thr (p > kKeepP16Bound / M, less
     // a margin for the fp16 roundings) is formed from its logits, loaded
@@ -597,8 +627,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       launder(rz[i]);
       launder(ru[i]);
       const u32x4_t o = any_above(rz[i], thr)
-                            ? grad8_exact(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, a1, b1, kce)
-                            : grad8(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce);
+                            ? grad8_exact<T>(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, a1, b1, kce)
+                            : grad8<T>(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce);
       st_stream(rsg, g * 16, o);
     }
 #pragma unroll
@@ -606,8 +636,8 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
       const int g = NT * G + tid + i * NT;
       const u32x4_t wp = lz[tid + i * NT], ws = lu[tid + i * NT];
       const u32x4_t o = any_above(wp, thr)
-                            ? grad8_exact(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, a1, b1, kce)
-                            : grad8(wp, ws, a1, b1, zero, trel - 8 * g, pt, kce);
+                            ? grad8_exact<T>(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, a1, b1, kce)
+                            : grad8<T>(wp, ws, a1, b1, zero, trel - 8 * g, pt, kce);
       st_stream(rsg, g * 16, o);
     }
     return;
@@ -617,12 +647,12 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
     const int g = tid + i * NT;
     launder(rz[i]);
     launder(ru[i]);
-    st_stream(rsg, g * 16, grad8(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce));
+    st_stream(rsg, g * 16, grad8<T>(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce));
   }
 #pragma unroll
   for (int i = 0; i < GL; ++i) {
     const int g = NT * G + tid + i * NT;
-    st_stream(rsg, g * 16, grad8(lz[tid + i * NT], lu[tid + i * NT], a1, b1, zero, trel - 8 * g, pt, kce));
+    st_stream(rsg, g * 16, grad8<T>(lz[tid + i * NT], lu[tid + i * NT], a1, b1, zero, trel - 8 * g, pt, kce));
   }
 }
 
@@ -635,12 +665,12 @@ void cluster_kernel(const uint16_t* student, const uint16_t* __restrict__ teache
 // element and g = k * g_ce * (p - [v == t]).  Member 0 has read the target
 // logit, and every member its whole chunk, before any member stores, so the
 // gradient may overwrite the student logits.
-template <int NT, int G, int WPE>
+template <typename T, int NT, int G, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target, int V, int64_t ignore_index,
-                     int K, int gpm, float* __restrict__ ce, float* __restrict__ lse_s_out, uint16_t* grad,
-                     float g_ce, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
-                     unsigned* __restrict__ ticket) {
+void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V, int64_t lds, int64_t ldg,
+                     int64_t ignore_index, int K, int gpm, float* __restrict__ ce, float* __restrict__ lse_s_out,
+                     T* grad, float g_ce, const float* __restrict__ gce_rows, const float* __restrict__ g_scale,
+                     uint64_t* __restrict__ slot1, unsigned* __restrict__ ticket) {
   constexpr int W = NT / 64;
   __shared__ Lse red_z[W];
   __shared__ uint64_t got[kClusterMaxK];
@@ -658,9 +688,9 @@ void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target
   const int NG = V >> 3;
   const int gb = j * gpm;
   const int ge = min(NG, gb + gpm);
-  const int64_t row = r * (int64_t)V;
+  const int64_t rowz = r * lds, rowg = r * ldg;
   const bool t_ok = t >= 0 && t < V;
-  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 8 * (int64_t)gb, (ge - gb) * 16);
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
       ce[r] = 0.f;
@@ -672,19 +702,19 @@ void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target
   }
   const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
   float zt = 0.f;
-  if (j == 0 && tid == 0 && t_ok) zt = load1(student + row + t);
+  if (j == 0 && tid == 0 && t_ok) zt = load1(student + rowz + t);
 
   // ---- load the chunk; unpack it into the E registers and take this thread's exact maximum
   float ez[G][8];
   float mz = kMFloor;
   {
-    const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 8 * (int64_t)gb, (ge - gb) * 16);
+    const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + rowz + 8 * (int64_t)gb, (ge - gb) * 16);
     u32x4_t rz[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      unpack8(rz[i], ez[i]);
+      unpack8<T>(rz[i], ez[i]);
       if (i < n) mz = fmaxf(mz, max8(ez[i]));
     }
   }
@@ -737,7 +767,7 @@ void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target
   const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(s_lse)));  // p = E * cz
 
   // ---- g = k * g_ce * (p - [v == t])
-  const float kce = (g_scale ? *g_scale : 1.0f) * g_ce;
+  const float kce = (g_scale ? *g_scale : 1.0f) * g_ce * (gce_rows ? gce_rows[r] : 1.0f);
   const float alpha = kce * cz;
   const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
 #pragma unroll
@@ -751,7 +781,7 @@ void fused_ce_kernel(const uint16_t* student, const int64_t* __restrict__ target
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
     }
-    st_stream(rsg, g * 16, t_ok ? pack8(o) : nan8());
+    st_stream(rsg, g * 16, t_ok ? pack8<T>(o) : nan8<T>());
   }
 }
 
@@ -847,34 +877,46 @@ static ClusterWs cluster_ws(void* ws, int64_t BT, int K, hipStream_t st) {
   return w;
 }
 
-hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
+template <typename T>
+static hipError_t launch_forward_cluster_t(const FwdArgs& a, const ClusterPlan& c, hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
   const unsigned tiles = (unsigned)(a.BT * (int64_t)c.K);
-  hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, false>), dim3(tiles), dim3(kClThreads),
-                     0, st, static_cast<const uint16_t*>(a.student), static_cast<const uint16_t*>(a.teacher),
-                     a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
-                     nullptr, 0.f, 0.f, nullptr, w.slot1, w.slot2, w.arrived, w.ticket);
+  hipLaunchKernelGGL((cluster_kernel<T, kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, false>), dim3(tiles),
+                     dim3(kClThreads), 0, st, static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
+                     a.target, (int)a.V, a.lds, a.ldt, (int64_t)0, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s,
+                     a.lse_t, a.sigma, (T*)nullptr, 0.f, 0.f, nullptr, nullptr, nullptr, w.slot1, w.slot2, w.arrived,
+                     w.ticket);
   return hipGetLastError();
 }
 
-hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
+hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, Dt dt, hipStream_t st) {
+  return dt == Dt::F16 ? launch_forward_cluster_t<_Float16>(a, c, st) : launch_forward_cluster_t<uint16_t>(a, c, st);
+}
+
+template <typename T>
+static hipError_t launch_fused_cluster_t(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c,
+                                         hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
   const dim3 grid((unsigned)(a.BT * (int64_t)c.K));
-  const auto* zs = static_cast<const uint16_t*>(a.student);
-  auto* gr = static_cast<uint16_t*>(g.grad);
+  const T* zs = static_cast<const T*>(a.student);
+  T* gr = static_cast<T*>(g.grad);
   if (a.teacher) {
-    hipLaunchKernelGGL((cluster_kernel<kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, true>), grid, dim3(kClThreads), 0,
-                       st, zs, static_cast<const uint16_t*>(a.teacher), a.target, (int)a.V, a.ignore_index, c.K,
-                       c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce, g.g_tvd, g.g_scale, w.slot1,
-                       w.slot2, w.arrived, w.ticket);
+    hipLaunchKernelGGL((cluster_kernel<T, kClThreads, kClGroups, kClLdsGroups, kClWavesPerSimd, true>), grid,
+                       dim3(kClThreads), 0, st, zs, static_cast<const T*>(a.teacher), a.target, (int)a.V, a.lds,
+                       a.ldt, g.ldg, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma, gr, g.g_ce,
+                       g.g_tvd, g.gce_rows, g.gtvd_rows, g.g_scale, w.slot1, w.slot2, w.arrived, w.ticket);
   } else {
-    hipLaunchKernelGGL((fused_ce_kernel<kFusedCeThreads, kFusedCeGroups, kFusedCeWavesPerSimd>), grid,
-                       dim3(kFusedCeThreads), 0, st, zs, a.target, (int)a.V, a.ignore_index, c.K, c.gpm, a.ce,
-                       a.lse_s, gr, g.g_ce, g.g_scale, w.slot1, w.ticket);
+    hipLaunchKernelGGL((fused_ce_kernel<T, kFusedCeThreads, kFusedCeGroups, kFusedCeWavesPerSimd>), grid,
+                       dim3(kFusedCeThreads), 0, st, zs, a.target, (int)a.V, a.lds, g.ldg, a.ignore_index, c.K, c.gpm,
+                       a.ce, a.lse_s, gr, g.g_ce, g.gce_rows, g.g_scale, w.slot1, w.ticket);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, Dt dt, hipStream_t st) {
+  return dt == Dt::F16 ? launch_fused_cluster_t<_Float16>(a, g, c, st) : launch_fused_cluster_t<uint16_t>(a, g, c, st);
 }
 
 }  // namespace lx

@@ -19,6 +19,9 @@ namespace lx {
 //               the forward falls back to the row or split-V path.
 constexpr int kClusterMaxK = 32;
 
+// Logits (and gradient) element type.
+enum class Dt { F32, BF16, F16 };
+
 struct ClusterPlan {
   int K;    // member workgroups per row (0: not applicable)
   int gpm;  // groups of 8 elements per member
@@ -37,13 +40,16 @@ struct FwdPlan {
 
 FwdPlan plan_forward(int64_t BT, int64_t V, int esize, bool teacher);
 
+// Row r of a logits array starts at element r * ld (ld >= V: the row stride).
 struct FwdArgs {
   const void* student;
   const void* teacher;  // nullptr: CE-only
   const int64_t* target;
   int64_t BT, V, ignore_index;
+  int64_t lds, ldt;     // row strides of student and teacher
   float *ce, *tvd, *lse_s, *lse_t, *sigma;
-  int vec;  // 16-byte vector path usable
+  int vec;     // every row of every tensor shares one address modulo 16: 16-byte vector path usable
+  int rows16;  // every row of every tensor starts on a 16-byte boundary (read-once / one-pass paths)
   void* workspace;
 };
 
@@ -53,8 +59,10 @@ struct BwdArgs {
   const void* teacher;  // nullptr: CE-only
   const int64_t* target;
   int64_t BT, V, ignore_index;
+  int64_t ldg, lds, ldt;  // row strides of grad, student and teacher
   const float *lse_s, *lse_t, *sigma;
   float g_ce, g_tvd;
+  const float *gce_rows, *gtvd_rows;  // per-row factors of g_ce and g_tvd, or nullptr
   const float* g_scale;
   int vec;
   // Column shard: these V columns are columns [v0, v0 + V) of rows of V_total
@@ -62,17 +70,20 @@ struct BwdArgs {
   int64_t v0, V_total;
 };
 
-hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, bool bf16, hipStream_t stream);
-hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, hipStream_t stream);
+hipError_t launch_forward(const FwdArgs& a, const FwdPlan& plan, Dt dt, hipStream_t stream);
+hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, Dt dt, hipStream_t stream);
 
 // Gradient arguments of the fused forward + backward.
 struct FusedGrad {
   void* grad;
+  int64_t ldg;
   float g_ce, g_tvd;
+  const float *gce_rows, *gtvd_rows;
   const float* g_scale;
 };
-hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t stream);
-hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, Dt dt,
+                                hipStream_t stream);
+hipError_t launch_backward(const BwdArgs& a, Dt dt, hipStream_t stream);
 // Vocabulary-parallel pieces (vocab_parallel.hip): the shard holds columns
 // [v0, v0 + Vs) of rows of the whole vocabulary.
 struct VpArgs {
@@ -84,8 +95,8 @@ struct VpArgs {
   float* out;                  // stats [BT][5 or 3] or tv [BT][2]
   int vec;
 };
-hipError_t launch_vp_stats(const VpArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_vp_tv(const VpArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_vp_stats(const VpArgs& a, Dt dt, hipStream_t stream);
+hipError_t launch_vp_tv(const VpArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
                                  int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
                                  hipStream_t stream);

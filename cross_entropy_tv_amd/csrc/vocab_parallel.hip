@@ -219,12 +219,20 @@ hipError_t launch_vp_tv_t(const VpArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_vp_stats(const VpArgs& a, bool bf16, hipStream_t st) {
-  return bf16 ? launch_vp_stats_t<uint16_t>(a, st) : launch_vp_stats_t<float>(a, st);
+hipError_t launch_vp_stats(const VpArgs& a, Dt dt, hipStream_t st) {
+  switch (dt) {
+    case Dt::BF16: return launch_vp_stats_t<uint16_t>(a, st);
+    case Dt::F16: return launch_vp_stats_t<_Float16>(a, st);
+    default: return launch_vp_stats_t<float>(a, st);
+  }
 }
 
-hipError_t launch_vp_tv(const VpArgs& a, bool bf16, hipStream_t st) {
-  return bf16 ? launch_vp_tv_t<uint16_t>(a, st) : launch_vp_tv_t<float>(a, st);
+hipError_t launch_vp_tv(const VpArgs& a, Dt dt, hipStream_t st) {
+  switch (dt) {
+    case Dt::BF16: return launch_vp_tv_t<uint16_t>(a, st);
+    case Dt::F16: return launch_vp_tv_t<_Float16>(a, st);
+    default: return launch_vp_tv_t<float>(a, st);
+  }
 }
 
 hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,

@@ -24,8 +24,9 @@
  *
  * Conventions shared by every entry point
  * ----------------------------------------
- * - Logits are row-major, contiguous, shape (BT, V), element type `dt`;
- *   student and teacher share the type.  Row r starts at element r * V.
+ * - Logits are row-major, shape (BT, V), element type `dt`; student and
+ *   teacher share the type.  Row r starts at element r * V (the `_ex` entry
+ *   points take a row stride per tensor instead: row r at element r * ld).
  * - All array pointers are DEVICE pointers owned by the caller.  The library
  *   allocates nothing, keeps no state between calls and is safe to call from
  *   several host threads (on different or on the same stream).
@@ -65,12 +66,12 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 3
+#define LX_CE_TVD_ABI_VERSION 4
 
 typedef enum lx_status {
   LX_OK = 0,
   LX_ERR_INVALID_ARG = 1,       /* NULL / misaligned pointer, bad size */
-  LX_ERR_UNSUPPORTED_DTYPE = 2, /* dt is not LX_F32 or LX_BF16 */
+  LX_ERR_UNSUPPORTED_DTYPE = 2, /* dt is not LX_F32, LX_BF16 or LX_F16 */
   LX_ERR_ALIAS = 3,             /* an output overlaps an input or another output */
   LX_ERR_WORKSPACE = 4,         /* workspace NULL or smaller than required */
   LX_ERR_HIP = 5                /* the HIP runtime rejected a launch */
@@ -78,7 +79,9 @@ typedef enum lx_status {
 
 typedef enum lx_dtype {
   LX_F32 = 0,  /* IEEE binary32 logits (and gradient) */
-  LX_BF16 = 1  /* bfloat16 logits (and gradient); gradients rounded to nearest-even */
+  LX_BF16 = 1, /* bfloat16 logits (and gradient); gradients rounded to nearest-even */
+  LX_F16 = 2   /* IEEE binary16 logits (and gradient); gradients rounded to nearest-even
+                  (values below the binary16 range become subnormal or zero) */
 } lx_dtype;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -156,7 +159,7 @@ size_t lx_ce_tvd_forward_backward_workspace_bytes(int64_t BT, int64_t V, lx_dtyp
  * Computes exactly what lx_ce_tvd_forward followed by lx_ce_tvd_backward
  * computes, combining the "Forward Pass" and "Backward Pass" sections of the
  * PR #1384 analysis page into one pass over the logits where the shape allows:
- * for bf16 logits (with or without a teacher), V % 8 == 0, V >= 2048 and
+ * for bf16 or binary16 logits (with or without a teacher), V % 8 == 0, V >= 2048 and
  * student, teacher and grad 16-byte aligned, each row is read from HBM once and
  * its gradient written once; any other shape runs the two passes back to back
  * on `stream`.
@@ -180,6 +183,56 @@ lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, c
                                      float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
                                      void* grad, float g_ce, float g_tvd, const float* g_scale,
                                      lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Strided rows and per-row upstream gradients.  The page shows contiguous
+ * (BT, V) logits and two scalar upstream gradients, grad_ce and grad_tvd
+ * (section "Backward Pass"), and is silent on row strides and on unreduced
+ * losses.  These entry points extend the three above, with the same
+ * arithmetic per row:
+ *
+ * - ld_student, ld_teacher, ld_grad: elements between the starts of
+ *   consecutive rows of each tensor, >= V (V for a contiguous array), e.g.
+ *   the logits of a vocabulary padded to a wider lm_head output.  Each array
+ *   spans (BT - 1) * ld + V elements for the overlap checks; an in-place
+ *   gradient (grad == student) needs ld_grad == ld_student.  The one-pass and
+ *   read-once kernels need every row on a 16-byte boundary (base and
+ *   ld * element size multiples of 16); other strides run the two-pass
+ *   kernels, with 16-byte vectors when all rows of the tensors share their
+ *   address modulo 16.
+ * - grad_ce_rows, grad_tvd_rows: optional device float[BT] per-row factors of
+ *   g_ce and g_tvd (NULL = 1), the upstream gradient of an unreduced
+ *   (per-row) loss: row r uses g_ce * grad_ce_rows[r] and
+ *   g_tvd * grad_tvd_rows[r], both times *g_scale when given.  Inputs: they
+ *   must not overlap the gradient or an output.
+ *
+ * With ld_* = V and NULL row factors each computes exactly what the
+ * entry point without the suffix computes.  Errors: as those, plus
+ * LX_ERR_INVALID_ARG for a stride below V or one whose last row end is not
+ * addressable.
+ */
+lx_status lx_ce_tvd_forward_ex(const void* student, int64_t ld_student, const void* teacher, int64_t ld_teacher,
+                               const int64_t* target, int64_t BT, int64_t V, int64_t ignore_index,
+                               float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                               lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+lx_status lx_ce_tvd_backward_ex(void* grad, int64_t ld_grad, const void* student, int64_t ld_student,
+                                const void* teacher, int64_t ld_teacher, const int64_t* target,
+                                int64_t BT, int64_t V, int64_t ignore_index,
+                                const float* lse_s, const float* lse_t, const float* sigma,
+                                float g_ce, float g_tvd, const float* grad_ce_rows, const float* grad_tvd_rows,
+                                const float* g_scale, lx_dtype dt, void* stream);
+
+/* Workspace: lx_ce_tvd_forward_backward_workspace_bytes (strides do not change it). */
+lx_status lx_ce_tvd_forward_backward_ex(const void* student, int64_t ld_student, const void* teacher,
+                                        int64_t ld_teacher, const int64_t* target,
+                                        int64_t BT, int64_t V, int64_t ignore_index,
+                                        float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                                        void* grad, int64_t ld_grad, float g_ce, float g_tvd,
+                                        const float* grad_ce_rows, const float* grad_tvd_rows,
+                                        const float* g_scale, lx_dtype dt,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Count of the rows whose target is not ignore_index, the only quantity a

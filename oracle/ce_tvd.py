@@ -48,15 +48,16 @@ import numpy as np
 # ---------------------------------------------------------------- decoding
 
 def decode(raw: np.ndarray) -> np.ndarray:
-    """Logits as float64.  uint16 arrays are bf16 bit patterns; float32/float64 are values.
+    """Logits as float64.  uint16 arrays are bf16 bit patterns; float16/float32/float64 are values.
 
     bf16 is the upper half of an IEEE binary32 word, so widening the bits by 16
-    and reinterpreting gives the exact value.
+    and reinterpreting gives the exact value; binary16 and binary32 values
+    widen to float64 exactly.
     """
     raw = np.asarray(raw)
     if raw.dtype == np.uint16:
         return (raw.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if raw.dtype in (np.float32, np.float64):
+    if raw.dtype in (np.float16, np.float32, np.float64):
         return raw.astype(np.float64)
     raise TypeError(f"unsupported logits dtype {raw.dtype}")
 
@@ -132,14 +133,16 @@ def forward(z_raw, u_raw, target, ignore_index: int = -100) -> dict:
 # ---------------------------------------------------------------- backward
 
 def backward(z_raw, u_raw, target, ignore_index: int = -100,
-             g_ce: float = 1.0, g_tvd: float = 1.0) -> np.ndarray:
-    """d(g_ce * ce + g_tvd * tvd)/dz for every row, float64 [R, V].
+             g_ce=1.0, g_tvd=1.0) -> np.ndarray:
+    """d(sum_r g_ce[r] * ce[r] + g_tvd[r] * tvd[r])/dz for every row, float64 [R, V].
 
     "Backward Pass" of the PR #1384 analysis page: the cross-entropy part is
     p - onehot(t); the total-variation part is the softmax Jacobian applied to
     0.5 * sign(p - q), i.e. 0.5 * p * (sign(p - q) - sigma).  The oracle
     recomputes lse, p, q and sigma itself from the logits.  Ignored rows are
-    all +0.0.  ``u_raw=None`` is CE-only mode.
+    all +0.0.  ``u_raw=None`` is CE-only mode.  g_ce and g_tvd are the
+    upstream gradients of each row's ce and tvd: scalars (the page's case)
+    or arrays of R per-row values (an unreduced loss).
     """
     z = decode(z_raw)
     R, V = z.shape
@@ -147,6 +150,8 @@ def backward(z_raw, u_raw, target, ignore_index: int = -100,
     grad = np.zeros((R, V), dtype=np.float64)
     if not valid.any():
         return grad
+    g_ce = np.broadcast_to(np.asarray(g_ce, dtype=np.float64), (R,))[valid][:, None]
+    g_tvd = np.broadcast_to(np.asarray(g_tvd, dtype=np.float64), (R,))[valid][:, None]
     zv = z[valid]
     _check_rows(zv, "student")
     rows = np.arange(zv.shape[0])

@@ -54,7 +54,7 @@ def grad_to_host(g: torch.Tensor) -> np.ndarray:
 
 
 def grad_bits(g: torch.Tensor) -> np.ndarray:
-    if g.dtype == torch.bfloat16:
+    if g.dtype in (torch.bfloat16, torch.float16):
         return g.view(torch.int16).cpu().numpy().view(np.uint16)
     return g.view(torch.int32).cpu().numpy().view(np.uint32)
 
@@ -93,7 +93,8 @@ def check_forward(out: dict, z_raw, u_raw, target, ignore_index, label=""):
 
 
 def check_grad(g_gpu: np.ndarray, g_bits: np.ndarray, z_raw, u_raw, target, ignore_index, g_ce, g_tvd, label=""):
-    """g_gpu: float64 view of the device gradient; g_bits: its raw bits."""
+    """g_gpu: float64 view of the device gradient; g_bits: its raw bits.  g_ce and
+    g_tvd are scalars or per-row arrays (the upstream gradient of each row)."""
     target = np.asarray(target)
     valid = target != ignore_index
     assert np.all(g_bits[~valid] == 0), f"{label}: ignored gradient rows are not +0.0"
@@ -101,7 +102,8 @@ def check_grad(g_gpu: np.ndarray, g_bits: np.ndarray, z_raw, u_raw, target, igno
     tol = G_REL * np.abs(ref) + G_ABS
     if u_raw is not None and valid.any():
         p, mask, slack = tie_info(z_raw, u_raw, valid)
-        extra = np.abs(g_tvd) * p * (1 + G_REL) * (mask + 0.5 * slack[:, None])
+        gt = np.abs(np.broadcast_to(np.asarray(g_tvd, dtype=np.float64), target.shape))[valid][:, None]
+        extra = gt * p * (1 + G_REL) * (mask + 0.5 * slack[:, None])
         tol[valid] += extra
     err = np.abs(g_gpu - ref)
     bad = err > tol
@@ -109,7 +111,7 @@ def check_grad(g_gpu: np.ndarray, g_bits: np.ndarray, z_raw, u_raw, target, igno
         r, v = np.argwhere(bad)[0]
         raise AssertionError(f"{label}: {bad.sum()} gradient elements out of tolerance; first at row {r} v {v}: "
                              f"gpu {g_gpu[r, v]!r} ref {ref[r, v]!r} tol {tol[r, v]!r}")
-    if u_raw is None and z_raw.shape[1] >= 2 and g_ce > 0:
+    if u_raw is None and z_raw.shape[1] >= 2 and np.ndim(g_ce) == 0 and g_ce > 0:
         # CE-only: exactly one negative entry per valid row, at its target
         neg = g_gpu[valid] < 0
         assert np.all(neg.sum(1) == 1) and np.all(neg[np.arange(neg.shape[0]), target[valid]]), \

@@ -16,7 +16,12 @@ and raises AssertionError when it disagrees with an independent source:
   sums, shift invariance, permutation equivariance, linearity in the upstream
   gradients;
 * ``ignore_rules``: ignored rows all +0.0, precedence of the ignore index,
-  out-of-range targets raise; mean reduction including the all-ignored case.
+  out-of-range targets raise; mean reduction including the all-ignored case;
+* ``row_weights``: per-row upstream gradients (an unreduced loss) against
+  torch float64 autograd of sum_r w_ce[r] * CE_r + w_tvd[r] * TVD_r;
+* ``decoding``: every finite bf16 and binary16 bit pattern decodes to the value
+  its sign, exponent and fraction fields define (IEEE 754 binary16; bf16 as
+  the upper half of binary32), built here with math.ldexp.
 
 The mutation test plants mistakes in copies of the oracle and checks that at
 least one of these fails for each.
@@ -270,4 +275,58 @@ def ignore_rules(orc):
     _close(gi[:, keep], orc.backward(z[:, keep], u[:, keep], remap[tt], -100, 1.0, 1.0), what="-inf classes grad")
 
 
-ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules)
+# ------------------------------------------------------------ per-row upstream gradients
+
+def row_weights(orc):
+    import torch
+
+    rng = np.random.default_rng(13)
+    R, V = 7, 29
+    z = rng.normal(0, 2.5, size=(R, V))
+    u = rng.normal(0, 2.5, size=(R, V))
+    t = rng.integers(0, V, size=R)
+    t[4] = -100
+    valid = t != -100
+    w_ce = rng.normal(0, 1.0, size=R)
+    w_tvd = rng.normal(0, 1.0, size=R)
+    zt = torch.from_numpy(z).requires_grad_(True)
+    tt = torch.from_numpy(t)
+    ce = torch.nn.functional.cross_entropy(zt, tt, reduction="none", ignore_index=-100)
+    tv = 0.5 * (torch.softmax(zt, -1) - torch.softmax(torch.from_numpy(u), -1)).abs().sum(-1)
+    m = torch.from_numpy(valid.astype(np.float64))
+    ((torch.from_numpy(w_ce) * ce + torch.from_numpy(w_tvd) * tv * m).sum()).backward()
+    _close(orc.backward(z, u, t, -100, w_ce, w_tvd), zt.grad.numpy(), what="per-row weights vs autograd")
+    zt2 = torch.from_numpy(z).requires_grad_(True)
+    ce2 = torch.nn.functional.cross_entropy(zt2, tt, reduction="none", ignore_index=-100)
+    (torch.from_numpy(w_ce) * ce2).sum().backward()
+    _close(orc.backward(z, None, t, -100, w_ce, w_tvd), zt2.grad.numpy(), what="CE-only per-row weights")
+    # equal per-row weights are the scalar case
+    _close(orc.backward(z, u, t, -100, np.full(R, 0.3), np.full(R, -1.1)),
+           orc.backward(z, u, t, -100, 0.3, -1.1), what="constant row weights")
+
+
+# ------------------------------------------------------------ logits decoding
+
+def _ieee_value(bits: int, exp_bits: int, frac_bits: int) -> float:
+    """Value of a finite IEEE-style bit pattern from its fields."""
+    sign = -1.0 if bits >> (exp_bits + frac_bits) else 1.0
+    e = (bits >> frac_bits) & ((1 << exp_bits) - 1)
+    f = bits & ((1 << frac_bits) - 1)
+    bias = (1 << (exp_bits - 1)) - 1
+    if e == 0:
+        return sign * math.ldexp(f, 1 - bias - frac_bits)
+    return sign * math.ldexp((1 << frac_bits) + f, e - bias - frac_bits)
+
+
+def decoding(orc):
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    for name, exp_bits, frac_bits, raw in (
+            ("bf16", 8, 7, pats.astype(np.uint16)),
+            ("binary16", 5, 10, pats.astype(np.uint16).view(np.float16))):
+        finite = ((pats >> frac_bits) & ((1 << exp_bits) - 1)) != (1 << exp_bits) - 1
+        got = orc.decode(raw[finite])
+        ref = np.array([_ieee_value(int(b), exp_bits, frac_bits) for b in pats[finite]])
+        assert got.dtype == np.float64 and np.array_equal(got, ref), f"{name} decoding"
+
+
+ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules, row_weights, decoding)

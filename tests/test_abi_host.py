@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 3
+    assert lx.lx_abi_version() == 4
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
                        (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP")):
         assert lx.lx_status_string(code) == name
@@ -199,3 +199,53 @@ def test_vocab_parallel_validation():
     assert bshard(v0=201) == lx.LX_ERR_INVALID_ARG                   # shard runs past the row
     assert bshard(V=50) == lx.LX_ERR_INVALID_ARG
     assert bshard(grad=A + 64) == lx.LX_ERR_ALIAS                    # partial overlap with the student
+
+
+def fwd_ex(student=A, lds=100, teacher=A + (1 << 31), ldt=100, target=A * 3, BT=4, V=100, ce=A * 4,
+           tvd=A * 4 + 64, lse_s=A * 4 + 128, lse_t=A * 4 + 192, sigma=A * 4 + 256, dt=1):
+    return L.lx_ce_tvd_forward_ex(student, lds, teacher, ldt, target, BT, V, -100, ce, tvd, lse_s, lse_t, sigma, dt,
+                                  None, 0, None)
+
+
+def bwd_ex(grad=A * 5, ldg=100, student=A, lds=100, teacher=A + (1 << 31), ldt=100, BT=4, V=100, gce=None,
+           gtvd=None, dt=1):
+    return L.lx_ce_tvd_backward_ex(grad, ldg, student, lds, teacher, ldt, A * 3, BT, V, -100, A * 4 + 128,
+                                   A * 4 + 192, A * 4 + 256, 1.0, 1.0, gce, gtvd, None, dt, None)
+
+
+def fwdbwd_ex(student=A, lds=100, teacher=A + (1 << 31), ldt=100, grad=A * 5, ldg=100, BT=4, V=100, gce=None,
+              gtvd=None, dt=1):
+    return L.lx_ce_tvd_forward_backward_ex(student, lds, teacher, ldt, A * 3, BT, V, -100, A * 4, A * 4 + 64,
+                                           A * 4 + 128, A * 4 + 192, A * 4 + 256, grad, ldg, 1.0, 1.0, gce, gtvd,
+                                           None, dt, None, 0, None)
+
+
+def test_strided_entry_points_validation():
+    for call in (fwd_ex, bwd_ex, fwdbwd_ex):
+        assert call(BT=0) == lx.LX_OK                                  # no-op, strides not inspected
+        assert call(dt=3) == lx.LX_ERR_UNSUPPORTED_DTYPE
+        assert call(lds=99) == lx.LX_ERR_INVALID_ARG                   # row stride below V
+        assert call(ldt=50) == lx.LX_ERR_INVALID_ARG
+        assert call(BT=2**40, lds=2**30) == lx.LX_ERR_INVALID_ARG     # last row end not addressable
+    for call in (bwd_ex, fwdbwd_ex):
+        assert call(ldg=10) == lx.LX_ERR_INVALID_ARG
+        assert call(gce=A * 6 + 2) == lx.LX_ERR_INVALID_ARG            # row factors float aligned
+        assert call(grad=A, ldg=100, lds=120) == lx.LX_ERR_ALIAS        # in place needs the same stride
+        assert call(gce=A * 5 + 64) == lx.LX_ERR_ALIAS                 # row factors inside the gradient
+        assert call(gtvd=A * 5 + 600) == lx.LX_ERR_ALIAS
+        # the strided span of the student covers (BT - 1) * ld + V elements (bf16: 2 bytes)
+        assert call(lds=1000, grad=A + 2 * 2500) == lx.LX_ERR_ALIAS
+    assert fwd_ex(lds=1000, ce=A + 2 * 2500) == lx.LX_ERR_ALIAS        # output inside the strided student
+    assert fwdbwd_ex(gce=A * 4 + 64) == lx.LX_ERR_ALIAS                # row factors over an output
+
+
+def test_binary16_logits_are_accepted():
+    # LX_F16 (2): validation reaches the same checks as for bf16 (same element size)
+    assert fwd(dt=2, tvd=A * 4) == lx.LX_ERR_ALIAS
+    assert fwd(dt=2, student=A + 1) == lx.LX_ERR_INVALID_ARG
+    assert bwd(dt=2, grad=A + 2) == lx.LX_ERR_ALIAS
+    assert fwdbwd(dt=2, grad=A + 2) == lx.LX_ERR_ALIAS
+    # the read-once / one-pass plans apply to 2-byte logits of either kind
+    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 2, 1) == lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1)
+    assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 2, 0) == \
+        lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 0)

@@ -24,6 +24,9 @@ MUTANTS = {
     "p_uses_teacher_lse": ("p = probs_rows(zv, lse_s)", "p = probs_rows(zv, lse_t)"),
     "target_off_by_one": ("onehot[rows, t] = 1.0", "onehot[rows, (t + 1) % V] = 1.0"),
     "tvd_grad_half_dropped": ("g_tvd * 0.5 * p * (s - sigma)", "g_tvd * p * (s - sigma)"),
+    "row_weights_swapped": ("g_ce = np.broadcast_to(np.asarray(g_ce,", "g_ce = np.broadcast_to(np.asarray(g_tvd,"),
+    "row_weights_unmasked": ("(R,))[valid][:, None]\n    g_tvd", "(R,))[:, None][:1]\n    g_tvd"),
+    "binary16_read_as_bf16": ("    if raw.dtype == np.uint16:", "    if raw.dtype in (np.uint16, np.float16):\n        raw = raw.view(np.uint16)"),
     "ignored_rows_not_zeroed": ('valid = _valid_mask(target, V, ignore_index)\n    grad', 'valid = _valid_mask(target, V, ignore_index) | True\n    grad'),
 }
 

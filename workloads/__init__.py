@@ -226,8 +226,9 @@ def custom(BT: int, V: int, dtype: str, seed: int, scale: float = 2.0, teacher_n
     teacher independent with the same law, or student + N(0, teacher_noise^2)
     when ``teacher_noise`` is given.  Rows listed in ``identical_rows`` get a
     bit-identical teacher, rows in ``uniform_rows`` a constant student row, rows
-    in ``ignore_rows`` the ignore index.  Returns (student_raw, teacher_raw,
-    target) with bf16 as uint16 bit patterns.
+    in ``ignore_rows`` the ignore index.  ``dtype`` is "f32", "bf16" or "f16"
+    (binary16, rounded to nearest even from the float32 draws).  Returns
+    (student_raw, teacher_raw, target) with bf16 as uint16 bit patterns.
     """
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ENTROPY, spawn_key=(1000 + seed,))))
     z = g.standard_normal((BT, V), dtype=np.float32) * np.float32(scale)
@@ -244,6 +245,11 @@ def custom(BT: int, V: int, dtype: str, seed: int, scale: float = 2.0, teacher_n
         if teacher_noise is not None:
             u = bf16_bits_to_f32(zr) + g.standard_normal((BT, V), dtype=np.float32) * np.float32(teacher_noise)
         ur = bf16_bits_rne(u)
+    elif dtype == "f16":
+        zr = z.astype(np.float16)  # IEEE binary16, round to nearest even
+        if teacher_noise is not None:
+            u = zr.astype(np.float32) + g.standard_normal((BT, V), dtype=np.float32) * np.float32(teacher_noise)
+        ur = u.astype(np.float16)
     else:
         zr = z
         if teacher_noise is not None:
