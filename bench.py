@@ -227,6 +227,86 @@ def run_vocab_parallel(w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
     return out
 
 
+def _time_call(fn, steps, warmup):
+    """Average HIP-event time (ms) of fn() on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
+    """The one-pass forward + backward of the ABI-breadth entry points on the same batch:
+    binary16 copies of the logits; the logits inside arrays padded to V + pad columns
+    (row strides, e.g. a vocabulary rounded up to a multiple of 256), gradient in
+    place; per-row upstream gradients (an unreduced loss).  Each is timed alone, with
+    its algorithmic bytes those of the one pass (read student and teacher once, write
+    the gradient once)."""
+    import torch
+    import cross_entropy_tv_amd as lx
+
+    BT, V = w.BT, w.V
+    dev = zs.device
+    f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
+    ce, lse_s, tvd, lse_t, sigma = f(), f(), f(), f(), f()
+    stream = torch.cuda.current_stream()
+    n_ign = BT - n_valid
+    alg = n_valid * 3 * V * w.esize + n_ign * V * w.esize + BT * 8 + BT * 4 * 5 + 4
+    inv = torch.empty(1, dtype=torch.float32, device=dev)
+    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
+    nws = lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, lx.LX_BF16, True)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    out = {}
+
+    def record(name, ms, extra=None):
+        out[name] = {"ms": round(ms, 4), "GBs": round(alg / ms / 1e6, 1),
+                     "pct_peak": round(100.0 * alg / ms / 1e6 / HBM_PEAK_GBS, 2), **(extra or {})}
+
+    g = torch.empty_like(zs)
+
+    def plain():
+        lx.lx_ce_tvd_forward_backward(zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, inv, ws, stream)
+
+    # the headline call again, for reference next to the variants (same process, same memory state)
+    record("reference", _time_call(plain, steps, warmup))
+    # binary16 logits: the bf16 batch rounded to binary16
+    z16, u16 = zs.to(torch.float16), us.to(torch.float16)
+    g16 = torch.empty_like(z16)
+    record("f16", _time_call(lambda: lx.lx_ce_tvd_forward_backward(
+        z16, u16, tg, -100, ce, tvd, lse_s, lse_t, sigma, g16, 1.0, 1.0, inv, ws, stream), steps, warmup),
+        {"logits": "f16"})
+    del z16, u16, g16
+    # row strides: views into arrays of V + pad columns, gradient in place over a scratch copy
+    zbig = torch.empty((BT, V + pad), dtype=zs.dtype, device=dev)
+    ubig = torch.empty((BT, V + pad), dtype=us.dtype, device=dev)
+    zbig[:, :V] = zs
+    ubig[:, :V] = us
+    zv, uv = zbig[:, :V], ubig[:, :V]
+    gbig = torch.empty_like(zbig)
+    gv = gbig[:, :V]
+    record("strided", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
+        zv, uv, tg, -100, ce, tvd, lse_s, lse_t, sigma, gv, 1.0, 1.0, g_scale=inv, workspace=ws, stream=stream),
+        steps, warmup), {"row_stride": V + pad})
+    del zbig, ubig, gbig
+    # per-row upstream gradients of an unreduced loss (factors ~ U(0.5, 1.5))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    wce = torch.rand(BT, generator=gen, device=dev) + 0.5
+    wtv = torch.rand(BT, generator=gen, device=dev) + 0.5
+    record("row_factors", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
+        zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, wce, wtv, inv, ws, stream), steps, warmup))
+    record("reference_after", _time_call(plain, steps, warmup))
+    return out
+
+
 def copy_ceiling(dev, nbytes=2 << 30, reps=10):
     """Achieved GB/s of a plain device copy (read + write), the practical streaming ceiling."""
     import torch
@@ -318,6 +398,7 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-vocab-parallel", action="store_true")
+    ap.add_argument("--no-ex", action="store_true", help="skip the binary16 / strided / per-row one-pass legs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
@@ -363,6 +444,8 @@ def main():
         extra["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in fu.items()}
     if teacher and not args.no_vocab_parallel and w.V % 8 == 0:
         extra["vocab_parallel"] = run_vocab_parallel(w, zs, us, tg, n_valid, args.steps, args.warmup)
+    if teacher and not args.no_ex and w.dtype == "bf16":
+        extra["one_pass_ex"] = run_ex(w, zs, us, tg, n_valid, args.steps, args.warmup)
     if not args.no_ceiling:
         extra["copy_ceiling_GBs"] = copy_ceiling(dev)
 

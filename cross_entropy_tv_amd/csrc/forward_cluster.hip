@@ -338,6 +338,13 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   const int64_t r = tile / (unsigned)K;
   const int j = (int)(tile - (unsigned)r * (unsigned)K);
   const int64_t t = target[r];
+  // the row's upstream gradients, read now so that the loads are long done by step 3
+  float k = 1.0f, gce = 0.0f, gtvd = 0.0f;
+  if (FUSED) {
+    k = g_scale ? *g_scale : 1.0f;
+    gce = g_ce * (gce_rows ? gce_rows[r] : 1.0f);
+    gtvd = g_tvd * (gtvd_rows ? gtvd_rows[r] : 1.0f);
+  }
 
   // ---- this member's chunk: groups [gb, ge) of the row; thread tid owns gb + tid + i * NT
   const int NG = V >> 3;
@@ -595,8 +602,6 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
 
   // ---- step 3: g = p * (alpha + beta * sign) - k * g_ce * [v == t]
   //             = p' * (a1 + b1 * s') - k * g_ce * [v == t]
-  const float k = g_scale ? *g_scale : 1.0f;
-  const float gce = g_ce * (gce_rows ? gce_rows[r] : 1.0f), gtvd = g_tvd * (gtvd_rows ? gtvd_rows[r] : 1.0f);
   const float kce = k * gce;
   const float beta = 0.5f * k * gtvd;
   const float alpha = kce - beta * s_bc[2];
@@ -690,6 +695,8 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   const int ge = min(NG, gb + gpm);
   const int64_t rowz = r * lds, rowg = r * ldg;
   const bool t_ok = t >= 0 && t < V;
+  // the row's upstream gradient, read now so that the load is long done after the exchange
+  const float kce = (g_scale ? *g_scale : 1.0f) * g_ce * (gce_rows ? gce_rows[r] : 1.0f);
   const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
@@ -767,7 +774,6 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   const float cz = exp2_hw(__builtin_fmaf(mz, kLog2e, neg_scaled(s_lse)));  // p = E * cz
 
   // ---- g = k * g_ce * (p - [v == t])
-  const float kce = (g_scale ? *g_scale : 1.0f) * g_ce * (gce_rows ? gce_rows[r] : 1.0f);
   const float alpha = kce * cz;
   const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
 #pragma unroll
