@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
 KERNEL_SOURCES = ["common.hpp", "forward.hip", "forward_cluster.hip", "backward.hip", "reduce.hip"]
 
@@ -307,6 +308,57 @@ def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
     return out
 
 
+def run_linear(steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=4096):
+    """The lm_head products + CE + TVD in one call (student and teacher lm_heads of
+    hidden size H over the vocabulary, seeded synthetic hidden states and weights):
+    the whole call, and each bf16 matrix product alone at the call's shapes, timed
+    with HIP events; FLOP/s against the dense bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+    import cross_entropy_tv_amd as lx
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    x_s, w_s, x_t, w_t, t = W.linear_inputs(BT, V, H, H, seed=77)
+
+    def d(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, Wd, Xt, Wt, tg = d(x_s), d(w_s), d(x_t), d(w_t), torch.from_numpy(t).to(dev)
+    del x_s, w_s, x_t, w_t
+    f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
+    ce, tvd, lse_s, lse_t, sigma = f(), f(), f(), f(), f()
+    gx = torch.empty((BT, H), dtype=torch.float32, device=dev)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    inv = torch.empty(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
+    ws = torch.empty(lx.lx_ce_tvd_linear_workspace_bytes(BT, V, True, chunk_rows), dtype=torch.uint8, device=dev)
+    ms = _time_call(lambda: lx.lx_ce_tvd_linear_forward_backward(
+        X, Wd, Xt, Wt, tg, -100, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, inv, chunk_rows, ws, stream),
+        steps, warmup)
+    flops = 2.0 * BT * V * H * 4  # student and teacher logits, grad of x, grad of w
+    out = {"shape": f"BT={BT} V={V} H_s=H_t={H} chunk_rows={chunk_rows}", "ms": round(ms, 3),
+           "tokens_per_s": round(BT / ms * 1e3, 1), "TFLOPs": round(flops / ms / 1e9, 1),
+           "pct_mfma_peak": round(100.0 * flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+    # each product alone, at the shapes of one chunk
+    R = chunk_rows
+    z = torch.empty((R, V), dtype=torch.float32, device=dev)
+    G = torch.zeros((R, V), dtype=torch.bfloat16, device=dev)
+    gemms = {
+        "logits_XWt": (lambda: lx.lx_gemm_bf16(X[:R], True, Wd, True, z, R, V, H, False, stream), R, V, H),
+        "grad_x_GW": (lambda: lx.lx_gemm_bf16(G, True, Wd, False, gx[:R], R, H, V, False, stream), R, H, V),
+        "grad_w_GtX": (lambda: lx.lx_gemm_bf16(G, False, X[:R], False, gw, V, H, R, True, stream), V, H, R),
+    }
+    for name, (fn, M, N, K) in gemms.items():
+        t_ms = _time_call(fn, steps, warmup)
+        fl = 2.0 * M * N * K
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(t_ms, 4), "TFLOPs": round(fl / t_ms / 1e9, 1),
+                     "pct_mfma_peak": round(100.0 * fl / t_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+    del z, G, ws, gx, gw
+    return out
+
+
 def copy_ceiling(dev, nbytes=2 << 30, reps=10):
     """Achieved GB/s of a plain device copy (read + write), the practical streaming ceiling."""
     import torch
@@ -399,6 +451,7 @@ def main():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-vocab-parallel", action="store_true")
     ap.add_argument("--no-ex", action="store_true", help="skip the binary16 / strided / per-row one-pass legs")
+    ap.add_argument("--no-linear", action="store_true", help="skip the lm_head product + loss leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
@@ -446,6 +499,8 @@ def main():
         extra["vocab_parallel"] = run_vocab_parallel(w, zs, us, tg, n_valid, args.steps, args.warmup)
     if teacher and not args.no_ex and w.dtype == "bf16":
         extra["one_pass_ex"] = run_ex(w, zs, us, tg, n_valid, args.steps, args.warmup)
+    if teacher and not args.no_linear:
+        extra["linear"] = run_linear(args.steps, args.warmup)
     if not args.no_ceiling:
         extra["copy_ceiling_GBs"] = copy_ceiling(dev)
 

@@ -84,6 +84,13 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_forward_backward_ex.argtypes = [p, i64, p, i64, p, i64, i64, i64, p, p, p, p, p, p, i64, f32, f32,
                                                 p, p, p, i32, p, sz, p]
     L.lx_ce_tvd_forward_backward_ex.restype = i32
+    L.lx_gemm_bf16.argtypes = [p, i64, i32, p, i64, i32, p, i64, i64, i64, i64, i32, p]
+    L.lx_gemm_bf16.restype = i32
+    L.lx_ce_tvd_linear_workspace_bytes.argtypes = [i64, i64, i32, i64]
+    L.lx_ce_tvd_linear_workspace_bytes.restype = sz
+    L.lx_ce_tvd_linear_forward_backward.argtypes = [p, p, i64, p, p, i64, p, i64, i64, i64, p, p, p, p, p, p, p,
+                                                    f32, f32, p, i64, p, sz, p]
+    L.lx_ce_tvd_linear_forward_backward.restype = i32
     return L
 
 
@@ -340,6 +347,50 @@ def lx_ce_tvd_forward_backward_ex(student, teacher, target, ignore_index, ce, tv
            "lx_ce_tvd_forward_backward_ex")
 
 
+def lx_gemm_bf16(A, a_k_contiguous: bool, B, b_k_contiguous: bool, C, M: int, N: int, K: int,
+                 accumulate: bool = False, stream=None) -> None:
+    """C[m][n] (+)= sum_k A(m, k) B(n, k) on bf16 device tensors A, B (2-D, rows contiguous)
+    and a float32 2-D C.  A(m, k) is A[m, k] when a_k_contiguous else A[k, m]; likewise B."""
+    import torch
+    for t, name in ((A, "A"), (B, "B")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D bfloat16 tensor with contiguous rows")
+    if C.dtype != torch.float32 or C.dim() != 2 or C.stride(1) != 1:
+        raise ValueError("C must be a 2-D float32 tensor with contiguous rows")
+    _check(lib.lx_gemm_bf16(_ptr(A), A.stride(0), int(bool(a_k_contiguous)), _ptr(B), B.stride(0),
+                            int(bool(b_k_contiguous)), _ptr(C), C.stride(0), int(M), int(N), int(K),
+                            int(bool(accumulate)), _stream(stream)), "lx_gemm_bf16")
+
+
+def lx_ce_tvd_linear_workspace_bytes(BT: int, V: int, has_teacher: bool, chunk_rows: int) -> int:
+    return lib.lx_ce_tvd_linear_workspace_bytes(BT, V, int(bool(has_teacher)), chunk_rows)
+
+
+def lx_ce_tvd_linear_forward_backward(x_s, w_s, x_t, w_t, target, ignore_index, ce, tvd, lse_s, lse_t, sigma,
+                                      grad_x_s, grad_w_s, g_ce: float, g_tvd: float, g_scale=None,
+                                      chunk_rows: int | None = None, workspace=None, stream=None) -> None:
+    """lm_head products and the CE + TVD loss: x_s (BT, H_s), w_s (V, H_s), x_t / w_t (or None)
+    contiguous bfloat16; grad_x_s (BT, H_s) / grad_w_s (V, H_s) float32 or None.  The workspace
+    (uint8 device tensor) is allocated here with torch when not given."""
+    import torch
+    BT, H_s = x_s.shape
+    V = w_s.shape[0]
+    H_t = 0 if x_t is None else x_t.shape[1]
+    for t, name in ((x_s, "x_s"), (w_s, "w_s"), (x_t, "x_t"), (w_t, "w_t")):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    chunk = BT if chunk_rows is None else int(chunk_rows)
+    need = lx_ce_tvd_linear_workspace_bytes(BT, V, x_t is not None, chunk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_s.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.lx_ce_tvd_linear_forward_backward(_ptr(x_s), _ptr(w_s), H_s, _ptr(x_t), _ptr(w_t), H_t, _ptr(target),
+                                                 BT, V, int(ignore_index), _ptr(ce), _ptr(tvd), _ptr(lse_s),
+                                                 _ptr(lse_t), _ptr(sigma), _ptr(grad_x_s), _ptr(grad_w_s),
+                                                 float(g_ce), float(g_tvd), _ptr(g_scale), chunk, _ptr(workspace),
+                                                 wbytes, _stream(stream)), "lx_ce_tvd_linear_forward_backward")
+
+
 __all__ = [
     "LxError", "lib", "LIB_PATH", "LX_OK", "LX_ERR_INVALID_ARG", "LX_ERR_UNSUPPORTED_DTYPE", "LX_ERR_ALIAS",
     "LX_ERR_WORKSPACE", "LX_ERR_HIP", "LX_F32", "LX_BF16", "LX_F16", "lx_status_string", "lx_abi_version",
@@ -347,4 +398,5 @@ __all__ = [
     "lx_ce_tvd_forward_backward_workspace_bytes", "lx_ce_tvd_forward_backward", "lx_ce_tvd_count_valid",
     "lx_vp_stats_floats", "lx_ce_tvd_vp_stats", "lx_ce_tvd_vp_merge_stats", "lx_ce_tvd_vp_tv", "lx_ce_tvd_vp_merge_tv",
     "lx_ce_tvd_backward_shard", "lx_ce_tvd_forward_ex", "lx_ce_tvd_backward_ex", "lx_ce_tvd_forward_backward_ex",
+    "lx_gemm_bf16", "lx_ce_tvd_linear_workspace_bytes", "lx_ce_tvd_linear_forward_backward",
 ]

@@ -4,7 +4,9 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include "gemm.hpp"
 #include "launch.hpp"
+#include "linear.hpp"
 #include "lx_ce_tvd.h"
 
 namespace {
@@ -492,6 +494,97 @@ lx_status lx_ce_tvd_vp_merge_tv(const float* tv, int64_t n_shards, const int64_t
       if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
   return from_hip(lx::launch_vp_merge_tv(tv, n_shards, target, BT, ignore_index, tvd, sigma,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ lm_head product + loss
+
+lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const void* B, int64_t ldb,
+                       int b_k_contiguous, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int accumulate,
+                       void* stream) {
+  if (M < 1 || N < 1 || K < 1 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return LX_ERR_INVALID_ARG;
+  if (!A || !B || !C) return LX_ERR_INVALID_ARG;
+  const int64_t ca = a_k_contiguous ? K : M, cb = b_k_contiguous ? K : N;  // contiguous dimensions
+  const int64_t ra = a_k_contiguous ? M : K, rb = b_k_contiguous ? N : K;  // rows of the stored arrays
+  if (ca % 8 || cb % 8 || lda < ca || ldb < cb || lda % 8 || ldb % 8 || ldc < N) return LX_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 4)) return LX_ERR_INVALID_ARG;
+  if (ra - 1 > (INT64_MAX / 2 - ca) / lda || rb - 1 > (INT64_MAX / 2 - cb) / ldb ||
+      M - 1 > (INT64_MAX / 4 - N) / ldc)
+    return LX_ERR_INVALID_ARG;
+  if ((M + 255) / 256 * ((N + 255) / 256) > INT_MAX / 8) return LX_ERR_INVALID_ARG;
+  const Span sa = span(A, ((ra - 1) * lda + ca) * 2), sb = span(B, ((rb - 1) * ldb + cb) * 2);
+  const Span sc = span(C, ((M - 1) * ldc + N) * 4);
+  if (overlaps(sc, sa) || overlaps(sc, sb)) return LX_ERR_ALIAS;
+  lx::GemmArgs g{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc, M, N, K,
+                 a_k_contiguous != 0, b_k_contiguous != 0, accumulate != 0};
+  return from_hip(lx::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)));
+}
+
+size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, int64_t chunk_rows) {
+  if (BT < 1 || V < 1 || V > (int64_t)INT_MAX || chunk_rows < 1) return 0;
+  const int64_t rows = chunk_rows < BT ? chunk_rows : BT;
+  if (rows > INT64_MAX / V / 16) return 0;
+  return lx::linear_workspace_bytes(BT, chunk_rows, V, has_teacher != 0);
+}
+
+lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, int64_t H_s, const void* x_t,
+                                            const void* w_t, int64_t H_t, const int64_t* target, int64_t BT,
+                                            int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s,
+                                            float* lse_t, float* sigma, float* grad_x_s, float* grad_w_s,
+                                            float g_ce, float g_tvd, const float* g_scale, int64_t chunk_rows,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (BT < 0 || V < 8 || V > (int64_t)INT_MAX || V % 8 || chunk_rows < 1) return LX_ERR_INVALID_ARG;
+  if (BT == 0) return LX_OK;
+  const bool has_t = x_t != nullptr || w_t != nullptr;
+  if (!x_s || !w_s || !target || !ce || !lse_s || (has_t && (!x_t || !w_t || !tvd || !lse_t || !sigma)))
+    return LX_ERR_INVALID_ARG;
+  if (H_s < 8 || H_s % 8 || H_s > (int64_t)INT_MAX || (has_t && (H_t < 8 || H_t % 8 || H_t > (int64_t)INT_MAX)))
+    return LX_ERR_INVALID_ARG;
+  if (BT > (int64_t)INT_MAX || V > INT64_MAX / 4 / (H_s > H_t ? H_s : H_t) || BT > INT64_MAX / 4 / H_s ||
+      (has_t && BT > INT64_MAX / 4 / H_t))
+    return LX_ERR_INVALID_ARG;
+  if (!aligned(x_s, 16) || !aligned(w_s, 16) || (has_t && (!aligned(x_t, 16) || !aligned(w_t, 16))) ||
+      !aligned(target, 8) || !aligned(ce, 4) || !aligned(lse_s, 4) || !aligned(g_scale, 4) ||
+      !aligned(grad_x_s, 4) || !aligned(grad_w_s, 4) ||
+      (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))))
+    return LX_ERR_INVALID_ARG;
+  const size_t need = lx_ce_tvd_linear_workspace_bytes(BT, V, has_t, chunk_rows);
+  if (!need) return LX_ERR_INVALID_ARG;
+  const int64_t fb = BT * 4;
+  // 0..5 inputs (may overlap each other), 6..13 outputs and the workspace
+  const Span sp[14] = {span(x_s, BT * H_s * 2), span(w_s, V * H_s * 2), span(has_t ? x_t : nullptr, BT * H_t * 2),
+                       span(has_t ? w_t : nullptr, V * H_t * 2), span(target, BT * 8), span(g_scale, 4),
+                       span(ce, fb), span(lse_s, fb), span(has_t ? tvd : nullptr, fb),
+                       span(has_t ? lse_t : nullptr, fb), span(has_t ? sigma : nullptr, fb),
+                       span(grad_x_s, BT * H_s * 4), span(grad_w_s, V * H_s * 4),
+                       span(workspace, (int64_t)need)};
+  for (int o = 6; o < 14; ++o)
+    for (int i = 0; i < 14; ++i)
+      if (i != o && overlaps(sp[o], sp[i])) return LX_ERR_ALIAS;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
+  lx::LinearArgs a{};
+  a.x_s = static_cast<const uint16_t*>(x_s);
+  a.w_s = static_cast<const uint16_t*>(w_s);
+  a.x_t = has_t ? static_cast<const uint16_t*>(x_t) : nullptr;
+  a.w_t = has_t ? static_cast<const uint16_t*>(w_t) : nullptr;
+  a.H_s = H_s;
+  a.H_t = has_t ? H_t : 0;
+  a.target = target;
+  a.BT = BT;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.ce = ce;
+  a.tvd = tvd;
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.sigma = sigma;
+  a.grad_x_s = grad_x_s;
+  a.grad_w_s = grad_w_s;
+  a.g_ce = g_ce;
+  a.g_tvd = g_tvd;
+  a.g_scale = g_scale;
+  a.chunk_rows = chunk_rows;
+  a.workspace = workspace;
+  return from_hip(lx::run_linear(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

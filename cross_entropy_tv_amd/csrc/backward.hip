@@ -37,9 +37,11 @@ constexpr int kBwdUnroll = 2;  // groups of 8 elements per lane per chunk
 constexpr int kBwdGroupsPerChunk = kBwdThreads * kBwdUnroll;
 constexpr int kMaxGrid = 1 << 20;
 
-template <typename T, bool TEACHER, int NT, int UNR>
+// TG: the gradient's element type (T, or bf16 for the fp32 logits of the
+// linear path, whose gradient feeds bf16 matrix products).
+template <typename T, bool TEACHER, int NT, int UNR, typename TG = T>
 __global__ __launch_bounds__(NT) void bwd_kernel(
-    T* grad, const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
+    TG* grad, const T* student, const T* __restrict__ teacher, const int64_t* __restrict__ target,
     int64_t BT, int V, int64_t ldg, int64_t lds, int64_t ldt, int64_t v0, int64_t V_total,
     int64_t ignore_index, int vec, int chunks_per_row,
     const float* __restrict__ lse_s, const float* __restrict__ lse_t, const float* __restrict__ sigma,
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const int64_t r = tile / chunks_per_row;
     const int c = (int)(tile - r * chunks_per_row);
     const int64_t t = target[r];
-    T* gr = grad + r * ldg;
+    TG* gr = grad + r * ldg;
     const T* z = student + r * lds;
     const T* u = TEACHER ? teacher + r * ldt : nullptr;
     const RowLayout L = row_layout(z, V, vec);
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const int g1 = min(L.groups, g0 + NT * UNR);
     const int s0 = c * (NT * UNR * 8);
     const int s1 = min(nsc, s0 + NT * UNR * 8);
-    T* gb = gr + L.head;
+    TG* gb = gr + L.head;
     const T* zb = z + L.head;
     const T* ub = TEACHER ? u + L.head : nullptr;
 
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
   }
 }
 
-template <typename T, bool TEACHER>
+template <typename T, bool TEACHER, typename TG = T>
 static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated call
   const int V = (int)a.V;
@@ -139,8 +141,8 @@ static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
   const int chunks = (int)(cpr < 1 ? 1 : cpr);
   const int64_t tiles = a.BT * (int64_t)chunks;
   const int grid = (int)(tiles < kMaxGrid ? tiles : kMaxGrid);
-  hipLaunchKernelGGL((bwd_kernel<T, TEACHER, kBwdThreads, kBwdUnroll>), dim3(grid), dim3(kBwdThreads), 0, st,
-                     static_cast<T*>(a.grad), static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
+  hipLaunchKernelGGL((bwd_kernel<T, TEACHER, kBwdThreads, kBwdUnroll, TG>), dim3(grid), dim3(kBwdThreads), 0, st,
+                     static_cast<TG*>(a.grad), static_cast<const T*>(a.student), static_cast<const T*>(a.teacher),
                      a.target, a.BT, V, a.ldg, a.lds, a.ldt, a.v0, a.V_total, a.ignore_index, a.vec, chunks, a.lse_s,
                      a.lse_t, a.sigma, a.g_ce, a.g_tvd, a.gce_rows, a.gtvd_rows, a.g_scale);
   return hipGetLastError();
@@ -149,6 +151,11 @@ static hipError_t launch_backward_t(const BwdArgs& a, hipStream_t st) {
 template <typename T>
 static hipError_t launch_backward_dt(const BwdArgs& a, hipStream_t stream) {
   return a.teacher ? launch_backward_t<T, true>(a, stream) : launch_backward_t<T, false>(a, stream);
+}
+
+hipError_t launch_backward_f32_to_bf16(const BwdArgs& a, hipStream_t stream) {
+  return a.teacher ? launch_backward_t<float, true, uint16_t>(a, stream)
+                   : launch_backward_t<float, false, uint16_t>(a, stream);
 }
 
 hipError_t launch_backward(const BwdArgs& a, Dt dt, hipStream_t stream) {

@@ -1,0 +1,27 @@
+// Host interface of the bf16 MFMA matrix product (gemm.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lx {
+
+// C[m][n] (+)= sum_k A(m, k) * B(n, k), bf16 A and B, fp32 C (row stride ldc).
+// A(m, k) = A[m * lda + k] when a_kc, else A[k * lda + m]; likewise B(n, k).
+// Preconditions (checked by the caller): 1 <= M, N, K < 2^31; the contiguous
+// dimension of A and B a multiple of 8; A, B 16-byte aligned, lda and ldb
+// multiples of 8; C 4-byte aligned.
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+  int64_t M, N, K;
+  bool a_kc, b_kc, accumulate;
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace lx

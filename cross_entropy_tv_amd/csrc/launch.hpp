@@ -84,6 +84,10 @@ struct FusedGrad {
 hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, Dt dt,
                                 hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, Dt dt, hipStream_t stream);
+// fp32 logits, bf16 gradient (rounded to nearest even); vec must be 0 unless
+// every logits row and gradient row share one address modulo 16 in elements
+// of their own size, i.e. pass vec = 0 when in doubt.
+hipError_t launch_backward_f32_to_bf16(const BwdArgs& a, hipStream_t stream);
 // Vocabulary-parallel pieces (vocab_parallel.hip): the shard holds columns
 // [v0, v0 + Vs) of rows of the whole vocabulary.
 struct VpArgs {

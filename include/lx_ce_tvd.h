@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 4
+#define LX_CE_TVD_ABI_VERSION 5
 
 typedef enum lx_status {
   LX_OK = 0,
@@ -353,6 +353,71 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
                                    const float* lse_s, const float* lse_t, const float* sigma,
                                    float g_ce, float g_tvd, const float* g_scale,
                                    lx_dtype dt, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * The lm_head product and the loss together.  The aibars.net Liger-Kernel
+ * project page lists a fused linear cross-entropy (the lm_head projection and
+ * the loss in one operation, so the full logits are never kept); the PR #1384
+ * analysis page's CE + TVD loss ("Forward Pass", "Backward Pass") runs here on
+ * the logits of student and teacher lm_heads:
+ *
+ *   z = x_s w_s^T,  u = x_t w_t^T                       (logits, fp32)
+ *   ce, tvd, lse_s, lse_t, sigma per row               (as lx_ce_tvd_forward)
+ *   G = k * (g_ce * d ce/dz + g_tvd * d tvd/dz)        (as lx_ce_tvd_backward)
+ *   grad_x_s = G w_s,  grad_w_s = G^T x_s
+ *
+ * Rows are processed in chunks of chunk_rows; a chunk's logits and G live in
+ * the workspace only while it is processed.  The matrix products run on the
+ * matrix cores (bf16 inputs, fp32 accumulation); the logits are kept in fp32
+ * and G is rounded to bf16 (nearest even) before the two gradient products.
+ */
+
+/*
+ * Matrix product on the matrix cores, the contraction step of the path above:
+ *
+ *   C[m][n] = (accumulate ? C[m][n] : 0) + sum_k A(m, k) * B(n, k)
+ *
+ * Inputs : A, B bf16 (device), C fp32 (device, row stride ldc >= N).
+ *          A(m, k) = A[m * lda + k] when a_k_contiguous, else A[k * lda + m];
+ *          B(n, k) = B[n * ldb + k] when b_k_contiguous, else B[k * ldb + n].
+ *          The contiguous dimension of A and of B (K, or M for A and N for B)
+ *          must be a multiple of 8, lda and ldb multiples of 8 no smaller than
+ *          that dimension, A and B 16-byte aligned, C 4-byte aligned;
+ *          1 <= M, N, K <= 2^31 - 1.  C must not overlap A or B.
+ * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS, LX_ERR_HIP.
+ */
+lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const void* B, int64_t ldb,
+                       int b_k_contiguous, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                       int accumulate, void* stream);
+
+/* Bytes of workspace lx_ce_tvd_linear_forward_backward needs (0 when BT == 0). */
+size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, int64_t chunk_rows);
+
+/*
+ * Inputs : x_s bf16 (BT, H_s) and w_s bf16 (V, H_s), row-major; x_t bf16
+ *          (BT, H_t) and w_t bf16 (V, H_t), or both NULL for CE-only mode;
+ *          target int64[BT]; H_s, H_t and V multiples of 8, V <= 2^31 - 1;
+ *          all four arrays 16-byte aligned.
+ * Outputs: ce, lse_s float[BT]; tvd, lse_t, sigma float[BT] with a teacher
+ *          (may be NULL without); grad_x_s float (BT, H_s) and grad_w_s float
+ *          (V, H_s), each optional (NULL: not computed), both OVERWRITTEN.
+ *          g_ce, g_tvd, g_scale as lx_ce_tvd_backward.  No output may overlap
+ *          an input, another output or the workspace.
+ * Workspace: at least lx_ce_tvd_linear_workspace_bytes(BT, V, teacher != NULL,
+ *          chunk_rows) bytes, 256-byte aligned: about chunk_rows * V * 10
+ *          bytes with a teacher (fp32 logits of both, bf16 G), 6 without.
+ * Errors : LX_ERR_INVALID_ARG (shapes, alignment, chunk_rows < 1),
+ *          LX_ERR_ALIAS, LX_ERR_WORKSPACE, LX_ERR_HIP.
+ */
+lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, int64_t H_s,
+                                            const void* x_t, const void* w_t, int64_t H_t,
+                                            const int64_t* target, int64_t BT, int64_t V, int64_t ignore_index,
+                                            float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                                            float* grad_x_s, float* grad_w_s,
+                                            float g_ce, float g_tvd, const float* g_scale,
+                                            int64_t chunk_rows, void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -182,3 +182,30 @@ def reduce_mean(ce, tvd, target, ignore_index: int = -100):
         mce = np.float64(np.sum(np.asarray(ce, dtype=np.float64)[valid])) / np.float64(n)
         mtv = None if tvd is None else np.float64(np.sum(np.asarray(tvd, dtype=np.float64)[valid])) / np.float64(n)
     return mce, mtv, n
+
+
+# ---------------------------------------------------------------- lm_head product + loss
+
+def linear_forward_backward(x_s_raw, w_s_raw, x_t_raw, w_t_raw, target, ignore_index: int = -100,
+                            g_ce=1.0, g_tvd=1.0) -> dict:
+    """The loss over the logits of student and teacher lm_heads, with the gradients
+    of the student's hidden states and weight.
+
+    The aibars.net Liger-Kernel page's fused linear cross-entropy: the logits are
+    the lm_head product z = x_s w_s^T (u = x_t w_t^T for the teacher), computed
+    here exactly in float64 (a matrix product of the decoded inputs); the loss
+    and G = d(g_ce ce + g_tvd tvd)/dz are ``forward`` and ``backward`` above;
+    by the chain rule through z = x w^T, dL/dx_s = G w_s and dL/dw_s = G^T x_s.
+    ``x_t_raw=None`` is CE-only mode.  Returns the forward dict plus ``grad``
+    (G), ``grad_x_s`` and ``grad_w_s``.
+    """
+    xs, ws = decode(x_s_raw), decode(w_s_raw)
+    z = xs @ ws.T
+    u = None if x_t_raw is None else decode(x_t_raw) @ decode(w_t_raw).T
+    out = forward(z, u, target, ignore_index)
+    g = backward(z, u, target, ignore_index, g_ce, g_tvd)
+    out["grad"] = g
+    out["grad_x_s"] = g @ ws
+    out["grad_w_s"] = g.T @ xs
+    out["z"], out["u"] = z, u
+    return out

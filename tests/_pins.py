@@ -19,6 +19,8 @@ and raises AssertionError when it disagrees with an independent source:
   out-of-range targets raise; mean reduction including the all-ignored case;
 * ``row_weights``: per-row upstream gradients (an unreduced loss) against
   torch float64 autograd of sum_r w_ce[r] * CE_r + w_tvd[r] * TVD_r;
+* ``linear_chain_rule``: the lm_head variant against torch float64 autograd
+  through x @ w.T and central differences on single entries of x and w;
 * ``decoding``: every finite bf16 and binary16 bit pattern decodes to the value
   its sign, exponent and fraction fields define (IEEE 754 binary16; bf16 as
   the upper half of binary32), built here with math.ldexp.
@@ -329,4 +331,61 @@ def decoding(orc):
         assert got.dtype == np.float64 and np.array_equal(got, ref), f"{name} decoding"
 
 
-ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules, row_weights, decoding)
+# ------------------------------------------------------------ lm_head product + loss
+
+def linear_chain_rule(orc):
+    """The loss over lm_head logits and its gradients w.r.t. the student's hidden
+    states and weight, against torch float64 autograd through x @ w.T, and
+    central differences of the float64 loss on single entries."""
+    import torch
+
+    rng = np.random.default_rng(21)
+    BT, Hs, Ht, V = 6, 5, 7, 11
+    xs, ws = rng.normal(0, 1.5, (BT, Hs)), rng.normal(0, 1.0, (V, Hs))
+    xt, wt = rng.normal(0, 1.5, (BT, Ht)), rng.normal(0, 1.0, (V, Ht))
+    t = rng.integers(0, V, BT)
+    t[2] = -100
+    valid = torch.from_numpy((t != -100).astype(np.float64))
+    tt = torch.from_numpy(t)
+    for teacher in (True, False):
+        g_ce, g_tvd = 0.7, -1.3
+        out = orc.linear_forward_backward(xs, ws, xt if teacher else None, wt if teacher else None, t, -100,
+                                          g_ce, g_tvd)
+        X = torch.from_numpy(xs).requires_grad_(True)
+        W = torch.from_numpy(ws).requires_grad_(True)
+        z = X @ W.T
+        ce = torch.nn.functional.cross_entropy(z, tt, reduction="none", ignore_index=-100)
+        loss = g_ce * ce.sum()
+        if teacher:
+            u = torch.from_numpy(xt) @ torch.from_numpy(wt).T
+            tv = 0.5 * (torch.softmax(z, -1) - torch.softmax(u, -1)).abs().sum(-1) * valid
+            loss = loss + g_tvd * tv.sum()
+            _close(out["tvd"], tv.detach().numpy(), what="linear tvd vs autograd forward")
+        loss.backward()
+        _close(out["ce"], ce.detach().numpy(), what="linear ce vs torch")
+        _close(out["grad_x_s"], X.grad.numpy(), what=f"grad_x_s vs autograd (teacher {teacher})")
+        _close(out["grad_w_s"], W.grad.numpy(), what=f"grad_w_s vs autograd (teacher {teacher})")
+
+    # central differences of the loss on a few single entries of x_s and w_s
+    def loss_of(xs_, ws_):
+        fw = orc.forward(xs_ @ ws_.T, xt @ wt.T, t, -100)
+        return 0.7 * fw["ce"].sum() + 1.1 * fw["tvd"].sum()
+
+    out = orc.linear_forward_backward(xs, ws, xt, wt, t, -100, 0.7, 1.1)
+    h = 1e-6
+    for (b, k) in ((0, 0), (3, 4), (5, 2)):
+        xp, xm = xs.copy(), xs.copy()
+        xp[b, k] += h
+        xm[b, k] -= h
+        _close(out["grad_x_s"][b, k], (loss_of(xp, ws) - loss_of(xm, ws)) / (2 * h), tol=1e-6,
+               what=f"grad_x_s[{b},{k}] central difference")
+    for (v, k) in ((0, 1), (7, 3), (10, 4)):
+        wp, wm = ws.copy(), ws.copy()
+        wp[v, k] += h
+        wm[v, k] -= h
+        _close(out["grad_w_s"][v, k], (loss_of(xs, wp) - loss_of(xs, wm)) / (2 * h), tol=1e-6,
+               what=f"grad_w_s[{v},{k}] central difference")
+
+
+ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules, row_weights, decoding,
+            linear_chain_rule)

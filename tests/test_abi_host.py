@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 4
+    assert lx.lx_abi_version() == 5
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
                        (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP")):
         assert lx.lx_status_string(code) == name
@@ -249,3 +249,55 @@ def test_binary16_logits_are_accepted():
     assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 2, 1) == lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1)
     assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 2, 0) == \
         lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 0)
+
+
+def test_gemm_validation():
+    g = L.lx_gemm_bf16
+
+    def call(A=A, lda=64, akc=1, B=A * 2, ldb=64, bkc=1, C=A * 3, ldc=32, M=16, N=32, K=64, acc=0):
+        return g(A, lda, akc, B, ldb, bkc, C, ldc, M, N, K, acc, None)
+
+    assert call(M=0) == lx.LX_ERR_INVALID_ARG
+    assert call(K=2**31) == lx.LX_ERR_INVALID_ARG
+    assert call(A=None) == lx.LX_ERR_INVALID_ARG
+    assert call(K=60, lda=64, ldb=64) == lx.LX_ERR_INVALID_ARG          # K-contiguous operands need K % 8 == 0
+    assert call(akc=0, M=12, lda=16) == lx.LX_ERR_INVALID_ARG           # M-contiguous A needs M % 8 == 0
+    assert call(bkc=0, N=36, ldb=40, ldc=36) == lx.LX_ERR_INVALID_ARG   # N-contiguous B needs N % 8 == 0
+    assert call(lda=60) == lx.LX_ERR_INVALID_ARG                         # row stride below the row
+    assert call(lda=68) == lx.LX_ERR_INVALID_ARG                         # row stride not a multiple of 8
+    assert call(ldc=31) == lx.LX_ERR_INVALID_ARG
+    assert call(A=A + 8) == lx.LX_ERR_INVALID_ARG                        # 16-byte alignment
+    assert call(C=A * 3 + 2) == lx.LX_ERR_INVALID_ARG
+    assert call(C=A + 64) == lx.LX_ERR_ALIAS                             # C over A
+    assert call(C=A * 2 + 1024) == lx.LX_ERR_ALIAS                       # C over B
+
+
+def test_linear_validation():
+    f = L.lx_ce_tvd_linear_forward_backward
+    ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 1, 128)
+    # fp32 logits of both lm_heads (2 x 4 B) and bf16 G per element of a 128-row chunk, plus the forward's share
+    assert ws_need >= 128 * 8200 * 10
+    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 0, 128) < ws_need
+    assert lx.lx_ce_tvd_linear_workspace_bytes(0, 8200, 1, 128) == 0
+    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 1, 0) == 0
+
+    def call(xs=A, ws=A * 2, Hs=64, xt=A * 3, wt=A * 4, Ht=64, t=A * 5, BT=300, V=8200, ce=A * 6,
+             tvd=A * 6 + 4096, lse_s=A * 6 + 8192, lse_t=A * 6 + 12288, sigma=A * 6 + 16384, gx=A * 7, gw=A * 8,
+             chunk=128, wsp=A * 16, wsb=ws_need):
+        return f(xs, ws, Hs, xt, wt, Ht, t, BT, V, -100, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, None, chunk,
+                 wsp, wsb, None)
+
+    assert call(BT=0) == lx.LX_OK
+    assert call(V=8196) == lx.LX_ERR_INVALID_ARG          # V % 8
+    assert call(Hs=60) == lx.LX_ERR_INVALID_ARG           # H % 8
+    assert call(Ht=0) == lx.LX_ERR_INVALID_ARG
+    assert call(chunk=0) == lx.LX_ERR_INVALID_ARG
+    assert call(wt=None) == lx.LX_ERR_INVALID_ARG         # teacher needs both x_t and w_t
+    assert call(sigma=None) == lx.LX_ERR_INVALID_ARG
+    assert call(xs=A + 8) == lx.LX_ERR_INVALID_ARG        # 16-byte alignment
+    assert call(gx=A * 6 + 64) == lx.LX_ERR_ALIAS         # gradient over an output
+    assert call(gw=A * 2 + 64) == lx.LX_ERR_ALIAS         # gradient over the weight
+    assert call(ce=A * 16 + 64) == lx.LX_ERR_ALIAS        # output inside the workspace
+    assert call(wsp=None) == lx.LX_ERR_WORKSPACE
+    assert call(wsb=ws_need - 1) == lx.LX_ERR_WORKSPACE
+    assert call(wsp=A * 16 + 128) == lx.LX_ERR_WORKSPACE  # 256-byte alignment

@@ -27,6 +27,9 @@ MUTANTS = {
     "row_weights_swapped": ("g_ce = np.broadcast_to(np.asarray(g_ce,", "g_ce = np.broadcast_to(np.asarray(g_tvd,"),
     "row_weights_unmasked": ("(R,))[valid][:, None]\n    g_tvd", "(R,))[:, None][:1]\n    g_tvd"),
     "binary16_read_as_bf16": ("    if raw.dtype == np.uint16:", "    if raw.dtype in (np.uint16, np.float16):\n        raw = raw.view(np.uint16)"),
+    "linear_grad_x_sign": ('out["grad_x_s"] = g @ ws', 'out["grad_x_s"] = -g @ ws'),
+    "linear_grad_w_from_teacher_hidden": ('out["grad_w_s"] = g.T @ xs', 'out["grad_w_s"] = g.T @ (xs if x_t_raw is None else decode(x_t_raw)[:, :xs.shape[1]])'),
+    "linear_teacher_logits_transposed": ("decode(x_t_raw) @ decode(w_t_raw).T", "(decode(w_t_raw) @ decode(x_t_raw).T).T[:, ::-1]"),
     "ignored_rows_not_zeroed": ('valid = _valid_mask(target, V, ignore_index)\n    grad', 'valid = _valid_mask(target, V, ignore_index) | True\n    grad'),
 }
 

@@ -261,3 +261,26 @@ def custom(BT: int, V: int, dtype: str, seed: int, scale: float = 2.0, teacher_n
     for r in ignore_rows:
         t[r] = IGNORE_INDEX
     return np.ascontiguousarray(zr), np.ascontiguousarray(ur), t
+
+
+def linear_inputs(BT: int, V: int, H_s: int, H_t: int | None, seed: int, logit_scale: float = 2.5,
+                  ignore_frac: float = 0.05):
+    """Seeded inputs of the lm_head variant: hidden states x ~ N(0, 1) and weights
+    w ~ N(0, (logit_scale / sqrt(H))^2), so the logits x w^T have standard deviation
+    about ``logit_scale``; teacher drawn independently (``H_t=None``: no teacher);
+    targets uniform, round(ignore_frac * BT) rows ignored.  bf16 bit patterns
+    (uint16), rounded to nearest even.  Returns (x_s, w_s, x_t, w_t, target)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ENTROPY, spawn_key=(2000 + seed,))))
+
+    def draw(shape, std):
+        return bf16_bits_rne(g.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+    x_s = draw((BT, H_s), 1.0)
+    w_s = draw((V, H_s), logit_scale / np.sqrt(H_s))
+    x_t = w_t = None
+    if H_t:
+        x_t = draw((BT, H_t), 1.0)
+        w_t = draw((V, H_t), logit_scale / np.sqrt(H_t))
+    t = g.integers(0, V, size=BT, dtype=np.int64)
+    t[g.permutation(BT)[: int(round(ignore_frac * BT))]] = IGNORE_INDEX
+    return x_s, w_s, x_t, w_t, t
