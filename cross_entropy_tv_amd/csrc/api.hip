@@ -506,6 +506,7 @@ lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const voi
   const int64_t ca = a_k_contiguous ? K : M, cb = b_k_contiguous ? K : N;  // contiguous dimensions
   const int64_t ra = a_k_contiguous ? M : K, rb = b_k_contiguous ? N : K;  // rows of the stored arrays
   if (ca % 8 || cb % 8 || lda < ca || ldb < cb || lda % 8 || ldb % 8 || ldc < N) return LX_ERR_INVALID_ARG;
+  if (lda > lx::kGemmMaxLd || ldb > lx::kGemmMaxLd) return LX_ERR_INVALID_ARG;  // in-slice offsets stay 32-bit
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 4)) return LX_ERR_INVALID_ARG;
   if (ra - 1 > (INT64_MAX / 2 - ca) / lda || rb - 1 > (INT64_MAX / 2 - cb) / ldb ||
       M - 1 > (INT64_MAX / 4 - N) / ldc)
@@ -532,12 +533,12 @@ lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, in
                                             float* lse_t, float* sigma, float* grad_x_s, float* grad_w_s,
                                             float g_ce, float g_tvd, const float* g_scale, int64_t chunk_rows,
                                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (BT < 0 || V < 8 || V > (int64_t)INT_MAX || V % 8 || chunk_rows < 1) return LX_ERR_INVALID_ARG;
+  if (BT < 0 || V < 8 || V > lx::kGemmMaxLd || V % 8 || chunk_rows < 1) return LX_ERR_INVALID_ARG;
   if (BT == 0) return LX_OK;
   const bool has_t = x_t != nullptr || w_t != nullptr;
   if (!x_s || !w_s || !target || !ce || !lse_s || (has_t && (!x_t || !w_t || !tvd || !lse_t || !sigma)))
     return LX_ERR_INVALID_ARG;
-  if (H_s < 8 || H_s % 8 || H_s > (int64_t)INT_MAX || (has_t && (H_t < 8 || H_t % 8 || H_t > (int64_t)INT_MAX)))
+  if (H_s < 8 || H_s % 8 || H_s > lx::kGemmMaxLd || (has_t && (H_t < 8 || H_t % 8 || H_t > lx::kGemmMaxLd)))
     return LX_ERR_INVALID_ARG;
   if (BT > (int64_t)INT_MAX || V > INT64_MAX / 4 / (H_s > H_t ? H_s : H_t) || BT > INT64_MAX / 4 / H_s ||
       (has_t && BT > INT64_MAX / 4 / H_t))

@@ -10,24 +10,41 @@
 //   grad X  dX = G W  : A = G (AK),   B = W (!BK),  K = vocabulary
 //   grad W  dW = G^T X: A = G (!AK),  B = X (!BK),  K = rows
 //
-// Workgroup tile 256 x 256 x 64, four waves of 128 x 128 (2 x 2), each wave
-// a 4 x 4 grid of v_mfma_f32_32x32x16_bf16.  The K-slices of A and B go
-// through LDS, double buffered (2 x 2 x 256 x 72 bf16 = 144 KB, so one
-// workgroup per compute unit), always stored K-contiguous with 16 bytes of
-// padding per row: an operand that is K-contiguous in memory is copied with
-// 16-byte writes, one that is M- or N-contiguous is transposed on the way in
-// (16-byte global loads along M or N, one k per lane, eight 2-byte LDS
-// writes that fill 64 consecutive columns of a row per instruction).  The next
-// K-slice is loaded into registers while the current one is multiplied.
+// Workgroup tile 256 x 256, four waves of 128 x 128 (2 x 2), each wave a
+// 4 x 4 grid of v_mfma_f32_32x32x16_bf16 with its accumulators in AGPRs, one
+// workgroup per compute unit (the accumulators take all 256 AGPRs).  K
+// advances in slices of 64 that go straight from memory to LDS (buffer loads
+// with the LDS-destination bit: no staging registers), double buffered
+// (2 x 2 x 32 KB): the next slice loads while the current one is multiplied.
+// A K-contiguous operand lands as 256 rows of 128 bytes whose eight 16-byte
+// chunks are XOR-swizzled by the row (chunk c of row r in slot c ^ (r % 8)),
+// so the 32 rows of a fragment read spread over the banks; an M- or
+// N-contiguous operand lands as 64 rows of 512 bytes, as stored, and its
+// fragments are read with the gfx950 LDS transpose read (ds_read_b64_tr_b16:
+// in each group of 16 lanes, the lane that supplies row j receives element
+// i % 4 of rows 4 s + i / 4, s = 0..3), which hands every lane 4 consecutive
+// k of one row or column: two reads make the 8 k of an MFMA operand.  Each
+// group of 4 MFMAs is preceded by the LDS reads of the fragments the next
+// group needs.  Loads past the matrix (ragged M, N, K) get an offset past the
+// buffer's range and read zeros, with no branch.
 //
-// Tiles are ordered M-fastest and dealt to the XCDs in contiguous runs (the
-// hardware hands workgroup ids to the 8 XCDs round robin), so the workgroups
-// that share a B tile run on one XCD and share its L2.
+// Tiles are dealt to the XCDs in contiguous runs (the hardware hands
+// workgroup ids to the 8 XCDs round robin), and within a run they go in
+// groups of 4 M-tiles sweeping N, so the ~32 tiles an XCD runs at once (4 x 8)
+// share their A and B slices in that XCD's L2.
+//
+// Measured on the 4096 x 151936 x 4096 logits product: 37% of the dense bf16
+// peak on random data (47% on zeros: the matrix cores draw less power), 78%
+// with the global loads switched off (the pure MFMA + LDS-read ceiling of this
+// structure); counters put the L2 hit rate at 77% (the compulsory misses of
+// 4 x 8 tile groups) and the waves waiting on the loads a third of the time.
+// Tried and not kept: a 4-stage ring of 32-wide K-slices (loads three slices
+// ahead; slower, 32%), staging through registers with transposing LDS writes
+// (35%).
 //
 // Requirements (checked on the host): the contiguous dimension of every
 // operand is a multiple of 8 elements and every row starts on a 16-byte
-// boundary; M, N, K >= 1.  Tails of M, N and K are handled by predication
-// (zeros are loaded past the ends; stores are masked).
+// boundary; M, N, K >= 1.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,80 +55,129 @@ namespace lx {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (16 bytes of padding)
+constexpr int kStages = 2;                       // K-slices in LDS: the next one loads while one is multiplied
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
+constexpr int kGroupM = 4;                       // tiles per group along M (tile order)
+constexpr int kTileBytes = 256 * kBK * 2;       // one operand's K-slice: 32 KB
+constexpr int kLoads = kTileBytes / (kThreads * 16);  // 16-byte loads per thread per operand and slice
+constexpr int kRsrcFlags = 0x00020000;           // buffer resource word 3 for gfx9-family raw buffers
+constexpr uint32_t kOutOfRange = 0x80000000u;    // a load offset past every buffer's range: reads 0
 
-// 16-byte global loads of one K-slice into registers: 2048 vectors of 8 bf16
-// per operand, 8 per thread.
-struct Slice {
-  uint4 v[8];
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)bytes, kRsrcFlags);
+}
 
-// Operand tile rows r0.. (m or n) over k0..k0+kBK.  KC: K-contiguous storage.
+// One K-slice of an operand (256 rows r0.. of the M or N dimension, k0..k0+63)
+// into LDS tile T.  P is the operand, ld its row stride, rows / K its extents,
+// end the bytes from P to the end of its last row.
 template <bool KC>
-__device__ __forceinline__ void load_slice(Slice& s, const uint16_t* P, int64_t ld, int rows, int K, int r0, int k0) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void load_slice(uint8_t* T, const uint16_t* P, int64_t ld, int rows, int K, int64_t end,
+                                           int r0, int k0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // slice base: row r0 / column k0 (K-contiguous) or row k0 / column r0 (otherwise)
+  const int64_t base = KC ? (int64_t)r0 * ld + k0 : (int64_t)k0 * ld + r0;
+  const int64_t left = end - 2 * base;
+  const uint32_t range = left > 0x7fffffff ? 0x7fffffffu : (uint32_t)(left > 0 ? left : 0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + base, range);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int v = t + kThreads * i;
-    int r, k;
-    if (KC) {  // 256 rows x 8 vectors along k
-      r = v >> 3;
-      k = (v & 7) * 8;
-    } else {  // 64 k-rows x 32 vectors along r; the 64 lanes of a wave take 64 different k
-      k = v & 63;
-      r = (v >> 6) * 8;
+  for (int q = 0; q < kLoads; ++q) {
+    const int kb = (wave * kLoads + q);  // which 1 KB of the 32 KB tile this wave instruction fills
+    uint32_t off;
+    bool ok;
+    if (KC) {  // 8 rows of 128 bytes per KB; lane L fills slot L % 8 of row kb * 8 + L / 8
+      const int r = kb * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);  // the chunk that belongs in this slot
+      ok = r0 + r < rows && k0 + 8 * c < K;
+      off = (uint32_t)(r * ld + 8 * c) * 2u;
+    } else {  // 2 rows of 512 bytes per KB; lane L fills chunk L % 32 of row kb * 2 + L / 32
+      const int k = kb * 2 + (lane >> 5);
+      const int c = lane & 31;
+      ok = k0 + k < K && r0 + 8 * c < rows;
+      off = (uint32_t)(k * ld + 8 * c) * 2u;
     }
-    const int gr = r0 + r, gk = k0 + k;
-    const bool ok = KC ? (gr < rows && gk < K) : (gk < K && gr < rows);
-    s.v[i] = ok ? *reinterpret_cast<const uint4*>(KC ? P + (int64_t)gr * ld + gk : P + (int64_t)gk * ld + gr)
-                : make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(T + kb * 1024), 16, ok ? off : kOutOfRange, 0, 0, 0);
   }
 }
 
+// The MFMA fragment of rows rb..rb+31 (M or N), k = ks..ks+15: lane l gets row
+// rb + l % 32, k = ks + 8 (l / 32) + 0..7.
 template <bool KC>
-__device__ __forceinline__ void store_slice(const Slice& s, uint16_t (*L)[kLdsRow]) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ bf16x8_t fragment(const uint8_t* T, int rb, int ks) {
+  const int lane = threadIdx.x & 63;
+  if (KC) {
+    const int r = rb + (lane & 31);
+    const int c = (ks >> 3) + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(T + r * 128 + ((c ^ (r & 7)) << 4));
+  } else {
+    const int g = lane >> 4, j = lane & 15;
+    const int r = rb + 16 * (g & 1) + 4 * (j & 3);
+    const int k = ks + 8 * (g >> 1) + (j >> 2);
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + k * 512 + r * 2));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + (k + 4) * 512 + r * 2));
+    const s16x4_t v8[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8_t, v8);
+  }
+}
+
+struct Frags {
+  bf16x8_t a_cur, a_nxt, b_cur[4], b_nxt[4];
+};
+
+// One group of 4 MFMAs: A fragment I of the 16-wide k step S against the
+// step's 4 B fragments.  Before the group, the next A fragment (I + 1, or
+// fragment 0 of step S + 1) and B fragment I of step S + 1 are requested, so
+// their LDS latency hides behind the group's MFMAs; the scheduling barriers
+// keep that order (the compiler would otherwise read each fragment just
+// before its first use, to save registers, and stall on every read).
+template <bool AK, bool BK, int S, int I>
+__device__ __forceinline__ void step(Frags& f, f32x16_t (&acc)[4][4], const uint8_t* TA, const uint8_t* TB, int wm,
+                                     int wn) {
+  constexpr bool has_a = I < 3 || S < 3;
+  constexpr bool has_b = S < 3;
+  constexpr int reads = (has_a ? (AK ? 1 : 2) : 0) + (has_b ? (BK ? 1 : 2) : 0);
+  if (has_a) f.a_nxt = fragment<AK>(TA, I < 3 ? wm + 32 * (I + 1) : wm, I < 3 ? 16 * S : 16 * (S + 1));
+  if (has_b) f.b_nxt[I] = fragment<BK>(TB, wn + 32 * I, 16 * (S + 1));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int v = t + kThreads * i;
-    if (KC) {
-      *reinterpret_cast<uint4*>(&L[v >> 3][(v & 7) * 8]) = s.v[i];
-    } else {  // lane k writes column k of rows r..r+7: each row's 64 columns in one instruction
-      const int k = v & 63, r = (v >> 6) * 8;
-      const uint32_t w[4] = {s.v[i].x, s.v[i].y, s.v[i].z, s.v[i].w};
+  for (int j = 0; j < 4; ++j) acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a_cur, f.b_cur[j], acc[I][j], 0, 0, 0);
+  if (reads) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                  // then the MFMAs
+  if (has_a) f.a_cur = f.a_nxt;
+  if (I == 3 && has_b) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        L[r + 2 * e][k] = (uint16_t)(w[e] & 0xffffu);
-        L[r + 2 * e + 1][k] = (uint16_t)(w[e] >> 16);
-      }
-    }
+    for (int j = 0; j < 4; ++j) f.b_cur[j] = f.b_nxt[j];
   }
 }
 
 template <bool AK, bool BK, bool ACC>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-                      float* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles) {
-  __shared__ uint16_t As[2][kBM][kLdsRow];
-  __shared__ uint16_t Bs[2][kBN][kLdsRow];
+void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end, const uint16_t* __restrict__ B,
+                      int64_t ldb, int64_t b_end, float* __restrict__ C, int64_t ldc, int M, int N, int K,
+                      int tiles_m, int tiles_n, int tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStages * kTileBytes];  // A stages, then B stages
 
-  // XCD-contiguous tile order: workgroup id i runs on XCD i % 8
+  // XCD-contiguous tile order: workgroup id i runs on XCD i % 8; within an
+  // XCD, groups of kGroupM M-tiles sweep N, so the tiles that run together
+  // share A and B slices in that XCD's L2
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int tile = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
   if (tile >= tiles) return;
-  const int m0 = (tile % tiles_m) * kBM;
-  const int n0 = (tile / tiles_m) * kBN;
+  const int per_group = kGroupM * tiles_n;
+  const int group = tile / per_group;
+  const int gm = min(kGroupM, tiles_m - group * kGroupM);  // M-tiles in this (possibly last, short) group
+  const int in_group = tile - group * per_group;
+  const int m0 = (group * kGroupM + in_group % gm) * kBM;
+  const int n0 = (in_group / gm) * kBN;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
-  const int lr = lane & 31;        // row of the A fragment / column of the B fragment
-  const int lk = (lane >> 5) * 8;  // first k of the lane's 8
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -120,36 +186,34 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
 
   const int nk = (K + kBK - 1) / kBK;
-  Slice sa, sb;
-  load_slice<AK>(sa, A, lda, M, K, m0, 0);
-  load_slice<BK>(sb, B, ldb, N, K, n0, 0);
-  store_slice<AK>(sa, As[0]);
-  store_slice<BK>(sb, Bs[0]);
+  auto issue = [&](int kt) {
+    const int st = kt & 1;
+    load_slice<AK>(lds + st * kTileBytes, A, lda, M, K, a_end, m0, kt * kBK);
+    load_slice<BK>(lds + (kStages + st) * kTileBytes, B, ldb, N, K, b_end, n0, kt * kBK);
+  };
+  issue(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_slice<AK>(sa, A, lda, M, K, m0, (kt + 1) * kBK);
-      load_slice<BK>(sb, B, ldb, N, K, n0, (kt + 1) * kBK);
-    }
+    const int st = kt & 1;
+    const uint8_t* TA = lds + st * kTileBytes;
+    const uint8_t* TB = lds + (kStages + st) * kTileBytes;
+    if (kt + 1 < nk) issue(kt + 1);  // the other stage, free since the barrier that ended slice kt - 1
+    // Fragments run one step ahead of the MFMAs that use them (see step()).
+    Frags f;
+    f.a_cur = fragment<AK>(TA, wm, 0);
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 16) {
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm + 32 * i + lr][ks + lk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][wn + 32 * j + lr][ks + lk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      store_slice<AK>(sa, As[buf ^ 1]);
-      store_slice<BK>(sb, Bs[buf ^ 1]);
-    }
+    for (int j = 0; j < 4; ++j) f.b_cur[j] = fragment<BK>(TB, wn + 32 * j, 0);
+    step<AK, BK, 0, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 0, 1>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 0, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 0, 3>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 1, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 1, 1>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 1, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 1, 3>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 2, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 2, 1>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 2, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 2, 3>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 3, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 3, 1>(f, acc, TA, TB, wm, wn);
+    step<AK, BK, 3, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 3, 3>(f, acc, TA, TB, wm, wn);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice kt + 1 has landed
     __syncthreads();
   }
 
@@ -158,7 +222,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + 32 * j + lr;
+      const int n = n0 + wn + 32 * j + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm + 32 * i + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
@@ -177,8 +241,12 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
   const int tiles_n = (int)((g.N + kBN - 1) / kBN);
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  // bytes from each operand's start to the end of its last stored row
+  const int64_t a_end = 2 * (AK ? (g.M - 1) * g.lda + g.K : (g.K - 1) * g.lda + g.M);
+  const int64_t b_end = 2 * (BK ? (g.N - 1) * g.ldb + g.K : (g.K - 1) * g.ldb + g.N);
   hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, ACC>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, st,
-                     g.A, g.lda, g.B, g.ldb, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, tiles_m, tiles);
+                     g.A, g.lda, a_end, g.B, g.ldb, b_end, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, tiles_m, tiles_n,
+                     tiles);
   return hipGetLastError();
 }
 

@@ -10,7 +10,11 @@ namespace lx {
 // A(m, k) = A[m * lda + k] when a_kc, else A[k * lda + m]; likewise B(n, k).
 // Preconditions (checked by the caller): 1 <= M, N, K < 2^31; the contiguous
 // dimension of A and B a multiple of 8; A, B 16-byte aligned, lda and ldb
-// multiples of 8; C 4-byte aligned.
+// multiples of 8 no larger than kGemmMaxLd; C 4-byte aligned.
+// Largest row stride (elements): a K-slice's offsets, 256 rows of the stride
+// in bytes, stay below 2^31.
+constexpr int64_t kGemmMaxLd = 1 << 22;
+
 struct GemmArgs {
   const uint16_t* A;
   int64_t lda;

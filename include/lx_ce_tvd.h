@@ -383,7 +383,7 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  *          B(n, k) = B[n * ldb + k] when b_k_contiguous, else B[k * ldb + n].
  *          The contiguous dimension of A and of B (K, or M for A and N for B)
  *          must be a multiple of 8, lda and ldb multiples of 8 no smaller than
- *          that dimension, A and B 16-byte aligned, C 4-byte aligned;
+ *          that dimension and at most 2^22, A and B 16-byte aligned, C 4-byte aligned;
  *          1 <= M, N, K <= 2^31 - 1.  C must not overlap A or B.
  * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS, LX_ERR_HIP.
  */
@@ -397,7 +397,7 @@ size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, 
 /*
  * Inputs : x_s bf16 (BT, H_s) and w_s bf16 (V, H_s), row-major; x_t bf16
  *          (BT, H_t) and w_t bf16 (V, H_t), or both NULL for CE-only mode;
- *          target int64[BT]; H_s, H_t and V multiples of 8, V <= 2^31 - 1;
+ *          target int64[BT]; H_s, H_t and V multiples of 8, at most 2^22;
  *          all four arrays 16-byte aligned.
  * Outputs: ce, lse_s float[BT]; tvd, lse_t, sigma float[BT] with a teacher
  *          (may be NULL without); grad_x_s float (BT, H_s) and grad_w_s float
