@@ -218,18 +218,25 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   }
 
   // register r of lane l holds row (r % 4) + 4 * (l / 32) + 8 * (r / 4), column l % 32 of each 32 x 32 tile
+  // (accumulating: the 16 values of a 32 x 32 tile are all read before any is
+  // written back, so the reads are in flight together)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + wn + 32 * j + (lane & 31);
+      float old[16];
+      if (ACC) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm + 32 * i + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+          old[r] = (m < M && n < N) ? C[(int64_t)m * ldc + n] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm + 32 * i + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        if (m < M && n < N) {
-          float* c = C + (int64_t)m * ldc + n;
-          *c = ACC ? *c + acc[i][j][r] : acc[i][j][r];
-        }
+        if (m < M && n < N) C[(int64_t)m * ldc + n] = ACC ? old[r] + acc[i][j][r] : acc[i][j][r];
       }
     }
   }
