@@ -39,8 +39,9 @@
 // structure); counters put the L2 hit rate at 77% (the compulsory misses of
 // 4 x 8 tile groups) and the waves waiting on the loads a third of the time.
 // Tried and not kept: a 4-stage ring of 32-wide K-slices (loads three slices
-// ahead; slower, 32%), staging through registers with transposing LDS writes
-// (35%).
+// ahead; 32%) and a 3-stage ring of 48-wide K-slices (30%): deeper rings of
+// narrower slices lose, so the loads' latency is not what limits this kernel;
+// staging through registers with transposing LDS writes (35%).
 //
 // Requirements (checked on the host): the contiguous dimension of every
 // operand is a multiple of 8 elements and every row starts on a 16-byte
