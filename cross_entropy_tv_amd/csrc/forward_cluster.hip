@@ -650,8 +650,6 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int g = tid + i * NT;
-    launder(rz[i]);
-    launder(ru[i]);
     st_stream(rsg, g * 16, grad8<T>(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce));
   }
 #pragma unroll
