@@ -17,9 +17,9 @@
 // with the LDS-destination bit: no staging registers), double buffered
 // (2 x 2 x 32 KB): the next slice loads while the current one is multiplied.
 // A K-contiguous operand lands as 256 rows of 128 bytes whose eight 16-byte
-// chunks are XOR-swizzled by the row (chunk c of row r in slot c ^ (r % 8)),
-// so the 32 rows of a fragment read spread over the banks; an M- or
-// N-contiguous operand lands as 64 rows of 512 bytes, as stored, and its
+// chunks are XOR-swizzled by the row (kc_swizzle), so a fragment read
+// spreads over the banks; an M- or N-contiguous operand lands as 64 rows of
+// 512 bytes, its chunks XOR-swizzled by k (tr_swizzle), and its
 // fragments are read with the gfx950 LDS transpose read (ds_read_b64_tr_b16:
 // in each group of 16 lanes, the lane that supplies row j receives element
 // i % 4 of rows 4 s + i / 4, s = 0..3), which hands every lane 4 consecutive
@@ -74,6 +74,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* p, u
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
+// LDS placement of 16-byte chunks.  K-contiguous tiles (rows of 128 bytes):
+// chunk c of row r sits in slot c ^ (r % 8), so 8 consecutive rows of a
+// fragment read (same chunk) land on distinct banks (c ^ ((r / 2) % 8), which
+// spreads 16 rows, measured the same within run-to-run variation).  M/N-contiguous
+// tiles (rows of 512 bytes, one per k): chunk c of row k sits in slot
+// c ^ (2 (k % 4)), so the four k rows a 16-lane transpose read touches (two
+// neighbouring chunks each) land on distinct banks instead of the same ones
+// (the grad-w product, both operands transposed: 8.54 -> 8.14 ms).
+__device__ __forceinline__ int kc_swizzle(int r) { return r & 7; }
+__device__ __forceinline__ int tr_swizzle(int k) { return (k & 3) << 1; }
+
 // One K-slice of an operand (256 rows r0.. of the M or N dimension, k0..k0+63)
 // into LDS tile T.  P is the operand, ld its row stride, rows / K its extents,
 // end the bytes from P to the end of its last row.
@@ -93,12 +104,12 @@ __device__ __forceinline__ void load_slice(uint8_t* T, const uint16_t* P, int64_
     bool ok;
     if (KC) {  // 8 rows of 128 bytes per KB; lane L fills slot L % 8 of row kb * 8 + L / 8
       const int r = kb * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);  // the chunk that belongs in this slot
+      const int c = (lane & 7) ^ kc_swizzle(r);  // the chunk that belongs in this slot
       ok = r0 + r < rows && k0 + 8 * c < K;
       off = (uint32_t)(r * ld + 8 * c) * 2u;
-    } else {  // 2 rows of 512 bytes per KB; lane L fills chunk L % 32 of row kb * 2 + L / 32
+    } else {  // 2 rows of 512 bytes per KB; lane L fills slot L % 32 of row kb * 2 + L / 32
       const int k = kb * 2 + (lane >> 5);
-      const int c = lane & 31;
+      const int c = (lane & 31) ^ tr_swizzle(k);
       ok = k0 + k < K && r0 + 8 * c < rows;
       off = (uint32_t)(k * ld + 8 * c) * 2u;
     }
@@ -114,14 +125,16 @@ __device__ __forceinline__ bf16x8_t fragment(const uint8_t* T, int rb, int ks) {
   if (KC) {
     const int r = rb + (lane & 31);
     const int c = (ks >> 3) + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(T + r * 128 + ((c ^ (r & 7)) << 4));
+    return *reinterpret_cast<const bf16x8_t*>(T + r * 128 + ((c ^ kc_swizzle(r)) << 4));
   } else {
     const int g = lane >> 4, j = lane & 15;
     const int r = rb + 16 * (g & 1) + 4 * (j & 3);
     const int k = ks + 8 * (g >> 1) + (j >> 2);
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + k * 512 + r * 2));
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + (k + 4) * 512 + r * 2));
+    // 4 elements r..r+3 (r % 4 == 0) lie in one chunk; k and k + 4 share k % 4
+    const int in_row = (((r >> 3) ^ tr_swizzle(k)) << 4) + (r & 7) * 2;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + k * 512 + in_row));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(T + (k + 4) * 512 + in_row));
     const s16x4_t v8[2] = {lo, hi};
     return __builtin_bit_cast(bf16x8_t, v8);
   }
