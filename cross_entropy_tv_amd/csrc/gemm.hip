@@ -25,7 +25,12 @@
 // i % 4 of rows 4 s + i / 4, s = 0..3), which hands every lane 4 consecutive
 // k of one row or column: two reads make the 8 k of an MFMA operand.  Each
 // group of 4 MFMAs is preceded by the LDS reads of the fragments the next
-// group needs.  Loads past the matrix (ragged M, N, K) get an offset past the
+// group needs.  The loads' addresses are computed once per tile (only the
+// slice base and the K bound change per slice); the next slice's loads go out
+// with the first four MFMA groups when both operands are K-contiguous (38-40%
+// instead of 37%), and all before the first group when one is transposed
+// (spreading them over the slice drops those products to 12-24%: the strided
+// rows miss L2 more, and late loads stall the end-of-slice wait).  Loads past the matrix (ragged M, N, K) get an offset past the
 // buffer's range and read zeros, with no branch.
 //
 // Tiles are dealt to the XCDs in contiguous runs (the hardware hands
@@ -85,37 +90,62 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* p, u
 __device__ __forceinline__ int kc_swizzle(int r) { return r & 7; }
 __device__ __forceinline__ int tr_swizzle(int k) { return (k & 3) << 1; }
 
-// One K-slice of an operand (256 rows r0.. of the M or N dimension, k0..k0+63)
-// into LDS tile T.  P is the operand, ld its row stride, rows / K its extents,
-// end the bytes from P to the end of its last row.
+// One operand's share of a K-slice load (256 rows r0.. of the M or N
+// dimension, k0..k0+63, into an LDS tile), split so that everything that does
+// not change from slice to slice is computed once per tile: lane L of wave w
+// fills 16 bytes of each of the 1 KB pieces w * 8 + q of the 32 KB tile.
+//   K-contiguous: 8 rows of 128 bytes per KB, lane L fills slot L % 8 of row
+//   kb * 8 + L / 8 (the chunk that belongs there, kc_swizzle);
+//   otherwise: 2 rows of 512 bytes per KB, lane L fills slot L % 32 of row
+//   kb * 2 + L / 32 (tr_swizzle).
+// Rows past the matrix get an out-of-range offset (zeros, no access) once;
+// the K bound is checked per slice, so the slice past the last one loads
+// nothing at all.
 template <bool KC>
-__device__ __forceinline__ void load_slice(uint8_t* T, const uint16_t* P, int64_t ld, int rows, int K, int64_t end,
-                                           int r0, int k0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // slice base: row r0 / column k0 (K-contiguous) or row k0 / column r0 (otherwise)
-  const int64_t base = KC ? (int64_t)r0 * ld + k0 : (int64_t)k0 * ld + r0;
-  const int64_t left = end - 2 * base;
-  const uint32_t range = left > 0x7fffffff ? 0x7fffffffu : (uint32_t)(left > 0 ? left : 0);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + base, range);
+struct SliceLoader {
+  uint32_t off[kLoads];  // byte offset from the slice base, or kOutOfRange
+  int kk[kLoads];        // k of this lane's 16 bytes within the slice
+  const uint16_t* P;
+  int64_t ld, end;
+  int K, r0;
+
+  __device__ __forceinline__ void init(const uint16_t* P_, int64_t ld_, int64_t end_, int rows, int K_, int r0_,
+                                       int wave) {
+    P = P_;
+    ld = ld_;
+    end = end_;
+    K = K_;
+    r0 = r0_;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int q = 0; q < kLoads; ++q) {
-    const int kb = (wave * kLoads + q);  // which 1 KB of the 32 KB tile this wave instruction fills
-    uint32_t off;
-    bool ok;
-    if (KC) {  // 8 rows of 128 bytes per KB; lane L fills slot L % 8 of row kb * 8 + L / 8
-      const int r = kb * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ kc_swizzle(r);  // the chunk that belongs in this slot
-      ok = r0 + r < rows && k0 + 8 * c < K;
-      off = (uint32_t)(r * ld + 8 * c) * 2u;
-    } else {  // 2 rows of 512 bytes per KB; lane L fills slot L % 32 of row kb * 2 + L / 32
-      const int k = kb * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ tr_swizzle(k);
-      ok = k0 + k < K && r0 + 8 * c < rows;
-      off = (uint32_t)(k * ld + 8 * c) * 2u;
+    for (int q = 0; q < kLoads; ++q) {
+      const int kb = wave * kLoads + q;
+      int r, k;
+      if (KC) {
+        r = kb * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ kc_swizzle(r);
+        k = 8 * c;
+        off[q] = r0 + r < rows ? (uint32_t)(r * ld + k) * 2u : kOutOfRange;
+      } else {
+        k = kb * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ tr_swizzle(k);
+        r = 8 * c;
+        off[q] = r0 + r < rows ? (uint32_t)(k * ld + r) * 2u : kOutOfRange;
+      }
+      kk[q] = k;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(T + kb * 1024), 16, ok ? off : kOutOfRange, 0, 0, 0);
   }
-}
+
+  // load q of slice k0 into tile T (T and the 1 KB piece are wave-uniform)
+  __device__ __forceinline__ void issue(int q, uint8_t* T, int k0, int wave) const {
+    const int64_t base = KC ? (int64_t)r0 * ld + k0 : (int64_t)k0 * ld + r0;
+    const int64_t left = end - 2 * base;
+    const uint32_t range = left > 0x7fffffff ? 0x7fffffffu : (uint32_t)(left > 0 ? left : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + base, range);
+    const uint32_t o = k0 + kk[q] < K ? off[q] : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(T + (wave * kLoads + q) * 1024), 16, o, 0, 0, 0);
+  }
+};
 
 // The MFMA fragment of rows rb..rb+31 (M or N), k = ks..ks+15: lane l gets row
 // rb + l % 32, k = ks + 8 (l / 32) + 0..7.
@@ -152,15 +182,27 @@ struct Frags {
 // before its first use, to save registers, and stall on every read).
 template <bool AK, bool BK, int S, int I>
 __device__ __forceinline__ void step(Frags& f, f32x16_t (&acc)[4][4], const uint8_t* TA, const uint8_t* TB, int wm,
-                                     int wn) {
+                                     int wn, const SliceLoader<AK>& la, const SliceLoader<BK>& lb, uint8_t* NA,
+                                     uint8_t* NB, int k0n, int wave) {
   constexpr bool has_a = I < 3 || S < 3;
   constexpr bool has_b = S < 3;
   constexpr int reads = (has_a ? (AK ? 1 : 2) : 0) + (has_b ? (BK ? 1 : 2) : 0);
   if (has_a) f.a_nxt = fragment<AK>(TA, I < 3 ? wm + 32 * (I + 1) : wm, I < 3 ? 16 * S : 16 * (S + 1));
   if (has_b) f.b_nxt[I] = fragment<BK>(TB, wn + 32 * I, 16 * (S + 1));
+  // both operands K-contiguous: the next slice's 16 loads go out with the
+  // first 4 groups (4 each: 2 of A, 2 of B), early enough to land before the
+  // slice ends; otherwise they all went out before the first group (loop body)
+  constexpr bool spread = AK && BK;
+  if (spread && S == 0) {
+    la.issue(2 * I, NA, k0n, wave);
+    lb.issue(2 * I, NB, k0n, wave);
+    la.issue(2 * I + 1, NA, k0n, wave);
+    lb.issue(2 * I + 1, NB, k0n, wave);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a_cur, f.b_cur[j], acc[I][j], 0, 0, 0);
   if (reads) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  // DS reads
+  if (spread && S == 0) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // the loads
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                  // then the MFMAs
   if (has_a) f.a_cur = f.a_nxt;
   if (I == 3 && has_b) {
@@ -190,7 +232,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   const int n0 = (in_group / gm) * kBN;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
 
   f32x16_t acc[4][4];
@@ -199,13 +241,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
 
+  SliceLoader<AK> la;
+  SliceLoader<BK> lb;
+  la.init(A, lda, a_end, M, K, m0, wave);
+  lb.init(B, ldb, b_end, N, K, n0, wave);
   const int nk = (K + kBK - 1) / kBK;
-  auto issue = [&](int kt) {
-    const int st = kt & 1;
-    load_slice<AK>(lds + st * kTileBytes, A, lda, M, K, a_end, m0, kt * kBK);
-    load_slice<BK>(lds + (kStages + st) * kTileBytes, B, ldb, N, K, b_end, n0, kt * kBK);
-  };
-  issue(0);
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q) {
+    la.issue(q, lds, 0, wave);
+    lb.issue(q, lds + kStages * kTileBytes, 0, wave);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -213,20 +258,30 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
     const int st = kt & 1;
     const uint8_t* TA = lds + st * kTileBytes;
     const uint8_t* TB = lds + (kStages + st) * kTileBytes;
-    if (kt + 1 < nk) issue(kt + 1);  // the other stage, free since the barrier that ended slice kt - 1
-    // Fragments run one step ahead of the MFMAs that use them (see step()).
+    // the next slice goes to the other stage, free since the barrier that
+    // ended slice kt - 1; past the last slice every load is out of range
+    uint8_t* NA = lds + (st ^ 1) * kTileBytes;
+    uint8_t* NB = lds + (kStages + (st ^ 1)) * kTileBytes;
+    const int k0n = (kt + 1) * kBK;
+    if (!(AK && BK)) {  // a transposed operand: the whole next slice is requested before any MFMA
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        la.issue(q, NA, k0n, wave);
+        lb.issue(q, NB, k0n, wave);
+      }
+    }
+    // Fragments run one step ahead of the MFMAs that use them, and the next
+    // slice's 16 loads go out with the first groups of MFMAs (see step()).
     Frags f;
     f.a_cur = fragment<AK>(TA, wm, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.b_cur[j] = fragment<BK>(TB, wn + 32 * j, 0);
-    step<AK, BK, 0, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 0, 1>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 0, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 0, 3>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 1, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 1, 1>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 1, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 1, 3>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 2, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 2, 1>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 2, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 2, 3>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 3, 0>(f, acc, TA, TB, wm, wn); step<AK, BK, 3, 1>(f, acc, TA, TB, wm, wn);
-    step<AK, BK, 3, 2>(f, acc, TA, TB, wm, wn); step<AK, BK, 3, 3>(f, acc, TA, TB, wm, wn);
+#define LX_STEP(S, I) step<AK, BK, S, I>(f, acc, TA, TB, wm, wn, la, lb, NA, NB, k0n, wave)
+    LX_STEP(0, 0); LX_STEP(0, 1); LX_STEP(0, 2); LX_STEP(0, 3);
+    LX_STEP(1, 0); LX_STEP(1, 1); LX_STEP(1, 2); LX_STEP(1, 3);
+    LX_STEP(2, 0); LX_STEP(2, 1); LX_STEP(2, 2); LX_STEP(2, 3);
+    LX_STEP(3, 0); LX_STEP(3, 1); LX_STEP(3, 2); LX_STEP(3, 3);
+#undef LX_STEP
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice kt + 1 has landed
     __syncthreads();
   }
