@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
-KERNEL_SOURCES = ["common.hpp", "forward.hip", "forward_cluster.hip", "backward.hip", "reduce.hip"]
+# sources of the kernels whose HBM counters are committed (profiles/pmc_traffic.json)
+KERNEL_SOURCES = ["common.hpp", "launch.hpp", "forward.hip", "forward_cluster.hip", "backward.hip"]
 
 
 def kernel_source_hash() -> str:
