@@ -28,11 +28,11 @@
 
 namespace lx {
 
-// 128 threads x 2 groups of 8 elements per lane: chunks of 2048 elements, so a
+// 256 threads x 2 groups of 8 elements per lane: chunks of 4096 elements, so a
 // launch has hundreds of thousands of short workgroups.  On the 8192 x 151936
-// training batch (CE+TVD): 128 x 2 1.17 ms, 512 x 2 1.19, 256 x 2 1.20,
-// 256 x 1 1.28, 256 x 4 1.34, 512 x 4 1.31, 256 x 8 1.36, 1024 x 1 1.37.
-constexpr int kBwdThreads = 128;
+// training batch (CE+TVD, one device): 256 x 2 1.196 ms, 128 x 2 1.21,
+// 512 x 1 1.22, 256 x 1 1.23, 512 x 2 1.27, 64 x 4 1.30, 128 x 1 1.48.
+constexpr int kBwdThreads = 256;
 constexpr int kBwdUnroll = 2;  // groups of 8 elements per lane per chunk
 constexpr int kBwdGroupsPerChunk = kBwdThreads * kBwdUnroll;
 constexpr int kMaxGrid = 1 << 20;
@@ -47,10 +47,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
     const float* __restrict__ lse_s, const float* __restrict__ lse_t, const float* __restrict__ sigma,
     float g_ce, float g_tvd, const float* __restrict__ gce_rows, const float* __restrict__ gtvd_rows,
     const float* __restrict__ g_scale) {
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const float k = g_scale ? *g_scale : 1.0f;
   const int64_t tiles = BT * (int64_t)chunks_per_row;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  for (int64_t tile = bid_x(); tile < tiles; tile += nblocks_x()) {
     const int64_t r = tile / chunks_per_row;
     const int c = (int)(tile - r * chunks_per_row);
     const int64_t t = target[r];

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ids.hpp"
+
 namespace lx {
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -259,7 +261,7 @@ template <int NT>
 __device__ __forceinline__ Lse block_lse(Lse a, Lse* red) {
   constexpr int W = NT / 64;
   a = wave_lse(a);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  if ((tid_x() & 63) == 0) red[tid_x() >> 6] = a;
   __syncthreads();
   Lse f = red[0];
 #pragma unroll
@@ -271,10 +273,10 @@ template <int NT>
 __device__ __forceinline__ float block_sum_t0(float v, float* red) {
   constexpr int W = NT / 64;
   v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((tid_x() & 63) == 0) red[tid_x() >> 6] = v;
   __syncthreads();
   float f = 0.0f;
-  if (threadIdx.x == 0) {
+  if (tid_x() == 0) {
     f = red[0];
 #pragma unroll
     for (int w = 1; w < W; ++w) f += red[w];

@@ -76,9 +76,9 @@ __global__ __launch_bounds__(NT) void fwd_row_kernel(
   __shared__ Lse red_s[NT / 64];
   __shared__ Lse red_t[NT / 64];
   __shared__ float red_f[2][NT / 64];
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
 
-  for (int64_t r = blockIdx.x; r < BT; r += gridDim.x) {
+  for (int64_t r = bid_x(); r < BT; r += nblocks_x()) {
     const int64_t t = target[r];
     if (t == ignore_index) {
       if (tid == 0) {
@@ -195,9 +195,9 @@ __global__ __launch_bounds__(NT) void fwd_split_stage1(
     int64_t BT, int V, int64_t lds, int64_t ldt, int64_t ignore_index, int vec, int S, float* __restrict__ ws1) {
   __shared__ Lse red_s[NT / 64];
   __shared__ Lse red_t[NT / 64];
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int64_t tiles = BT * (int64_t)S;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  for (int64_t tile = bid_x(); tile < tiles; tile += nblocks_x()) {
     const int64_t r = tile / S;
     const int c = (int)(tile - r * S);
     if (target[r] == ignore_index) continue;
@@ -241,10 +241,10 @@ __global__ __launch_bounds__(NT) void fwd_split_stage2(
     float* __restrict__ ws2, float* __restrict__ ce, float* __restrict__ lse_s_out,
     float* __restrict__ lse_t_out) {
   __shared__ float red_f[2][NT / 64];
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int per = TEACHER ? S : 1;  // CE-only: one workgroup per row merges and stores
   const int64_t tiles = BT * (int64_t)per;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  for (int64_t tile = bid_x(); tile < tiles; tile += nblocks_x()) {
     const int64_t r = tile / per;
     const int c = (int)(tile - r * per);
     const int64_t t = target[r];
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void fwd_split_stage3(const int64_t* __restric
                                                         int64_t ignore_index, int S,
                                                         const float* __restrict__ ws2,
                                                         float* __restrict__ tvd, float* __restrict__ sigma) {
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < BT; r += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t r = bid_x() * (int64_t)bdim_x() + tid_x(); r < BT; r += (int64_t)nblocks_x() * bdim_x()) {
     if (target[r] == ignore_index) {
       tvd[r] = 0.0f;
       sigma[r] = 0.0f;

@@ -274,7 +274,7 @@ __device__ __forceinline__ u32x4_t grad8_exact(const u32x4_t& wz, const u32x4_t&
 // bounded wait gives up) and store what they read in got[]; n <= 64.
 // Returns true, in wave 0, when the wait gave up.
 __device__ __forceinline__ bool wait_slots(const uint64_t* sl, int n, uint64_t* got) {
-  const int lane = threadIdx.x;
+  const int lane = tid_x();
   const bool mine = lane < n;
   uint64_t v = kEmpty;
   unsigned spins = 0;
@@ -331,7 +331,7 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   __shared__ float s_zt;
   __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
 
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -681,7 +681,7 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   __shared__ float s_lse;
   __shared__ float s_zt;
 
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -792,8 +792,8 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
 // Presets the exchange slots to kEmpty and the arrival counters and the ticket to 0.
 __global__ __launch_bounds__(256) void cluster_ws_init_kernel(uint64_t* __restrict__ slots, int64_t nslots,
                                                               unsigned* __restrict__ zeros, int64_t nzeros) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)nblocks_x() * bdim_x();
+  const int64_t i0 = bid_x() * (int64_t)bdim_x() + tid_x();
   for (int64_t i = i0; i < nslots; i += stride) slots[i] = kEmpty;
   for (int64_t i = i0; i < nzeros; i += stride) zeros[i] = 0u;
 }

@@ -55,6 +55,7 @@
 #include <stdint.h>
 
 #include "gemm.hpp"
+#include "ids.hpp"
 
 namespace lx {
 
@@ -116,7 +117,7 @@ struct SliceLoader {
     end = end_;
     K = K_;
     r0 = r0_;
-    const int lane = threadIdx.x & 63;
+    const int lane = tid_x() & 63;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
       const int kb = wave * kLoads + q;
@@ -151,7 +152,7 @@ struct SliceLoader {
 // rb + l % 32, k = ks + 8 (l / 32) + 0..7.
 template <bool KC>
 __device__ __forceinline__ bf16x8_t fragment(const uint8_t* T, int rb, int ks) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_x() & 63;
   if (KC) {
     const int r = rb + (lane & 31);
     const int c = (ks >> 3) + (lane >> 5);
@@ -222,7 +223,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   // XCD, groups of kGroupM M-tiles sweep N, so the tiles that run together
   // share A and B slices in that XCD's L2
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  const int tile = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  const int tile = (int)(bid_x() % kXcds) * per_xcd + (int)(bid_x() / kXcds);
   if (tile >= tiles) return;
   const int per_group = kGroupM * tiles_n;
   const int group = tile / per_group;
@@ -231,8 +232,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   const int m0 = (group * kGroupM + in_group % gm) * kBM;
   const int n0 = (in_group / gm) * kBN;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = tid_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
 
   f32x16_t acc[4][4];

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_mean_kernel(
   __shared__ double sc[kRedThreads];
   __shared__ double st[kRedThreads];
   __shared__ long long sn[kRedThreads];
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   double a = 0.0, b = 0.0;
   long long n = 0;
   for (int64_t i = tid; i < BT; i += kRedThreads) {

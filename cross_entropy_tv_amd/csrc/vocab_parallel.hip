@@ -44,8 +44,8 @@ __global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ stud
   __shared__ Lse red_s[NT / 64];
   __shared__ Lse red_t[NT / 64];
   constexpr int P = TEACHER ? 5 : 3;
-  const int tid = threadIdx.x;
-  for (int64_t r = blockIdx.x; r < BT; r += gridDim.x) {
+  const int tid = tid_x();
+  for (int64_t r = bid_x(); r < BT; r += nblocks_x()) {
     const int64_t t = target[r];
     float* o = stats + r * P;
     if (t == ignore_index) {
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
     const float* __restrict__ stats, int N, int64_t BT, const int64_t* __restrict__ target, int64_t V,
     int64_t ignore_index, float* __restrict__ ce, float* __restrict__ lse_s, float* __restrict__ lse_t) {
   constexpr int P = TEACHER ? 5 : 3;
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < BT; r += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t r = bid_x() * (int64_t)bdim_x() + tid_x(); r < BT; r += (int64_t)nblocks_x() * bdim_x()) {
     const int64_t t = target[r];
     if (t == ignore_index) {
       ce[r] = 0.0f;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(NT) void vp_tv_kernel(const T* __restrict__ student
                                                    int64_t ignore_index, int vec, const float* __restrict__ lse_s,
                                                    const float* __restrict__ lse_t, float* __restrict__ tv) {
   __shared__ float red_f[2][NT / 64];
-  const int tid = threadIdx.x;
-  for (int64_t r = blockIdx.x; r < BT; r += gridDim.x) {
+  const int tid = tid_x();
+  for (int64_t r = bid_x(); r < BT; r += nblocks_x()) {
     const int64_t t = target[r];
     if (t == ignore_index) {
       if (tid < 2) tv[2 * r + tid] = 0.0f;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NT) void vp_tv_kernel(const T* __restrict__ student
 __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_tv_kernel(
     const float* __restrict__ tv, int N, int64_t BT, const int64_t* __restrict__ target, int64_t ignore_index,
     float* __restrict__ tvd, float* __restrict__ sigma) {
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < BT; r += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t r = bid_x() * (int64_t)bdim_x() + tid_x(); r < BT; r += (int64_t)nblocks_x() * bdim_x()) {
     if (target[r] == ignore_index) {
       tvd[r] = 0.0f;
       sigma[r] = 0.0f;
