@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
 # sources of the kernels whose HBM counters are committed (profiles/pmc_traffic.json)
-KERNEL_SOURCES = ["common.hpp", "launch.hpp", "forward.hip", "forward_cluster.hip", "backward.hip"]
+KERNEL_SOURCES = ["common.hpp", "ids.hpp", "launch.hpp", "forward.hip", "forward_cluster.hip", "backward.hip"]
 
 
 def kernel_source_hash() -> str:
