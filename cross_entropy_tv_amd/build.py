@@ -64,7 +64,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lhipblaslt"]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

@@ -1,4 +1,4 @@
-// Host interface of the bf16 MFMA matrix product (gemm.hip).
+// Host interface of the bf16 matrix product (gemm.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,8 +11,7 @@ namespace lx {
 // Preconditions (checked by the caller): 1 <= M, N, K < 2^31; the contiguous
 // dimension of A and B a multiple of 8; A, B 16-byte aligned, lda and ldb
 // multiples of 8 no larger than kGemmMaxLd; C 4-byte aligned.
-// Largest row stride (elements): a K-slice's offsets, 256 rows of the stride
-// in bytes, stay below 2^31.
+// Largest operand row stride (elements) the entry points accept.
 constexpr int64_t kGemmMaxLd = 1 << 22;
 
 struct GemmArgs {
