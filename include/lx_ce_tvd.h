@@ -369,8 +369,10 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  *
  * Rows are processed in chunks of chunk_rows; a chunk's logits and G live in
  * the workspace only while it is processed.  The matrix products run on the
- * matrix cores (bf16 inputs, fp32 accumulation); the logits are kept in fp32
- * and G is rounded to bf16 (nearest even) before the two gradient products.
+ * matrix cores through lx_gemm_bf16 (bf16 inputs, fp32 accumulation; its
+ * first call on a device allocates hipBLASLt's handle and workspace); the
+ * logits are kept in fp32 and G is rounded to bf16 (nearest even) before the
+ * two gradient products.
  */
 
 /*
@@ -385,6 +387,10 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  *          must be a multiple of 8, lda and ldb multiples of 8 no smaller than
  *          that dimension and at most 2^22, A and B 16-byte aligned, C 4-byte aligned;
  *          1 <= M, N, K <= 2^31 - 1.  C must not overlap A or B.
+ * Runs as one hipBLASLt matmul.  The first call on a device creates that
+ * device's hipBLASLt handle and allocates a 64 MiB workspace for it (device
+ * memory, kept until the process ends); the algorithm chosen for a shape is
+ * cached.  Calls from several host threads are serialised per device.
  * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS, LX_ERR_HIP.
  */
 lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const void* B, int64_t ldb,
