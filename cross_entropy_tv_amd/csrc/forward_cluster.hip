@@ -659,6 +659,383 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   }
 }
 
+// ---------------------------------------------------------------- one pass over fp32 logits (lm_head path)
+//
+// The lm_head path's logits are fp32 (the matrix products' output) and its
+// student gradient G is bf16, in a buffer of its own.  cluster_f32_kernel is
+// cluster_kernel<..., FUSED = true> for that case, with groups of 4 fp32
+// logits (16 bytes) where the bf16 kernel has 8: half the logits per
+// register, so a 151936-logit row takes K = 8 member workgroups.  Step 2
+// keeps the quad's p' and s' (fp16, 8 bytes each) in the registers of its
+// student logits, and step 3 writes 4 bf16 gradients (8 bytes) per quad.
+// Rows are contiguous (row stride V), V a multiple of 4, every row of the
+// logits on a 16-byte boundary.  Per element the arithmetic is that of
+// cluster_kernel<..., true>, and with a gradient scale beyond kKeepP16Bound
+// the quads that hold a large p are formed from their logits, loaded again.
+
+namespace {
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack4f(const u32x4_t& w, float (&x)[4]) {
+  x[0] = __uint_as_float(w.x);
+  x[1] = __uint_as_float(w.y);
+  x[2] = __uint_as_float(w.z);
+  x[3] = __uint_as_float(w.w);
+}
+__device__ __forceinline__ float max4f(const u32x4_t& w) {
+  float x[4];
+  unpack4f(w, x);
+  return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+}
+__device__ __forceinline__ void expsum4f(const u32x4_t& w, float nb, float& s0, float& s1) {
+  float x[4];
+  unpack4f(w, x);
+  s0 += exp2_hw(__builtin_fmaf(x[0], kLog2e, nb));
+  s1 += exp2_hw(__builtin_fmaf(x[1], kLog2e, nb));
+  s0 += exp2_hw(__builtin_fmaf(x[2], kLog2e, nb));
+  s1 += exp2_hw(__builtin_fmaf(x[3], kLog2e, nb));
+}
+// step 2 of a quad pair: S += p' s', Q += q' s'; wz becomes {p'01, p'23, s'01, s'23} (fp16 pairs)
+__device__ __forceinline__ void tv4f_signs(u32x4_t& wz, const u32x4_t& wu, float nbs, float nbt, float& Q0,
+                                           float& Q1, float& S0, float& S1) {
+  float x[4], y[4], p[4], s[4];
+  unpack4f(wz, x);
+  unpack4f(wu, y);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float ap = exparg(x[e], nbs), aq = exparg(y[e], nbt);
+    s[e] = sign_eps(ap, aq);
+    p[e] = exp2_hw(ap);
+    if (e & 1) {
+      S1 = __builtin_fmaf(p[e], s[e], S1);
+      Q1 = __builtin_fmaf(exp2_hw(aq), s[e], Q1);
+    } else {
+      S0 = __builtin_fmaf(p[e], s[e], S0);
+      Q0 = __builtin_fmaf(exp2_hw(aq), s[e], Q0);
+    }
+  }
+  wz = (u32x4_t){pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(s[0], s[1]), pack_f16x2(s[2], s[3])};
+}
+// step 3 of a quad from its p' and s' (the target element, rel in [0, 4), from pt in fp32)
+__device__ __forceinline__ u32x2_t grad4f(const u32x4_t& w, float a1, float b1, float zero, int rel, float pt,
+                                          float kce) {
+  float p[4], sg[4], o[4];
+  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  unpack_f16x2(w0, p[0], p[1]);
+  unpack_f16x2(w1, p[2], p[3]);
+  unpack_f16x2(w2, sg[0], sg[1]);
+  unpack_f16x2(w3, sg[2], sg[3]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(p[e], __builtin_fmaf(sg[e], b1, a1), zero);
+  if ((unsigned)rel < 4u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], b1, a1) - kce : o[e];
+  }
+  return (u32x2_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+// as grad4f with p' recomputed in fp32 from the quad's student logits wz
+__device__ __forceinline__ u32x2_t grad4f_exact(const u32x4_t& wz, const u32x4_t& w, float nbs, int rel, float a1,
+                                                float b1, float kce) {
+  float x[4], sg[4], o[4];
+  unpack4f(wz, x);
+  const unsigned w2 = w.z, w3 = w.w;
+  unpack_f16x2(w2, sg[0], sg[1]);
+  unpack_f16x2(w3, sg[2], sg[3]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = exp2_hw(exparg(x[e], nbs)) * __builtin_fmaf(sg[e], b1, a1);
+  if ((unsigned)rel < 4u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
+  }
+  return (u32x2_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+// true when one of the quad's four fp16 p' (words x, y) exceeds thr
+__device__ __forceinline__ bool any_above4(const u32x4_t& w, _Float16 thr) {
+  const unsigned w0 = w.x, w1 = w.y;
+  const h2_t m = __builtin_elementwise_max(as_h2(w0), as_h2(w1));
+  return m.x > thr || m.y > thr;
+}
+__device__ __forceinline__ void st8_stream(__amdgpu_buffer_rsrc_t rs, int byte_off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, byte_off, 0, kStreamPolicy);
+}
+
+}  // namespace
+
+template <int NT, int G, int GL, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
+void cluster_f32_kernel(const float* __restrict__ student, const float* __restrict__ teacher,
+                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int qpm,
+                        float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
+                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out, uint16_t* __restrict__ grad,
+                        float g_ce, float g_tvd, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
+                        uint64_t* __restrict__ slot2, unsigned* __restrict__ ticket) {
+  constexpr int W = NT / 64;
+  __shared__ Lse red_z[W], red_u[W];
+  __shared__ float red_a[W], red_s[W];
+  __shared__ uint64_t got[2 * kClusterMaxK];
+  __shared__ unsigned s_tile;
+  __shared__ float s_bc[4];
+  __shared__ float s_zt;
+  __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
+
+  const int tid = tid_x();
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned tile = s_tile;
+  const int64_t r = tile / (unsigned)K;
+  const int j = (int)(tile - (unsigned)r * (unsigned)K);
+  const int64_t t = target[r];
+  const float k = g_scale ? *g_scale : 1.0f;
+
+  // ---- this member's chunk: quads [qb, qe) of the row; thread tid owns qb + tid + i * NT
+  const int NQ = V >> 2;
+  const int qb = j * qpm;
+  const int qe = min(NQ, qb + qpm);
+  const int cnt = qe - qb;
+  const int64_t row = r * (int64_t)V;
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 4 * (int64_t)qb, cnt * 8);
+  if (t == ignore_index) {
+    if (j == 0 && tid == 0) {
+      ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < G + GL; ++i) st8_stream(rsg, (tid + i * NT) * 8, (u32x2_t){0u, 0u});
+    return;
+  }
+  const int n = tid < cnt ? min(G, (cnt - tid - 1) / NT + 1) : 0;
+  const int nl = NT * G + tid < cnt ? min(GL, (cnt - NT * G - tid - 1) / NT + 1) : 0;
+  const bool t_ok = t >= 0 && t < V;
+  const int jt = t_ok ? (int)(t >> 2) / qpm : 0;  // the member whose chunk holds the target
+  float zt = 0.f;
+  if (j == jt && tid == 0 && t_ok) zt = student[row + t];
+
+  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 4 * (int64_t)qb, cnt * 16);
+  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 4 * (int64_t)qb, cnt * 16);
+  u32x4_t rz[G], ru[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+    ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+  }
+  if (GL > 0 && cnt > NT * G) {
+    // the rest of the chunk goes straight to LDS, 64 quads (1 KB) per load
+    const int lcnt = cnt - NT * G;
+    const int64_t lo = 4 * (int64_t)(qb + NT * G);
+    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + row + lo, lcnt * 16);
+    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + row + lo, lcnt * 16);
+    const int lane = tid & 63;
+    for (int b = tid >> 6; b < (lcnt + 63) >> 6; b += W) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrz, (__attribute__((address_space(3))) void*)&lz[b * 64], 16,
+                                               (b * 64 + lane) * 16, 0, 0, kStreamPolicy);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lru, (__attribute__((address_space(3))) void*)&lu[b * 64], 16,
+                                               (b * 64 + lane) * 16, 0, 0, kStreamPolicy);
+    }
+  }
+
+  // ---- step 1: sums of exponentials against this thread's reference maxima
+  float mz = kMFloor, mu = kMFloor;
+  if (n > 0) {
+    mz = fmaxf(mz, max4f(rz[0]));
+    mu = fmaxf(mu, max4f(ru[0]));
+  }
+  float sz0 = 0.f, sz1 = 0.f, su0 = 0.f, su1 = 0.f;
+  {
+    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        expsum4f(rz[i], nbz, sz0, sz1);
+        expsum4f(ru[i], nbu, su0, su1);
+      }
+    }
+    if (GL > 0) {
+      __syncthreads();  // every wave's loads into LDS have landed
+#pragma unroll
+      for (int i = 0; i < GL; ++i) {
+        if (i < nl) {
+          expsum4f(lz[tid + i * NT], nbz, sz0, sz1);
+          expsum4f(lu[tid + i * NT], nbu, su0, su1);
+        }
+      }
+    }
+  }
+  if (!(sz0 + sz1 < 3.0e38f) || !(su0 + su1 < 3.0e38f)) {
+    // a logit far above the first quad's maximum: redo against the true maxima
+#pragma unroll
+    for (int i = 1; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        mz = fmaxf(mz, max4f(rz[i]));
+        mu = fmaxf(mu, max4f(ru[i]));
+      }
+    }
+    for (int i = 0; i < nl; ++i) {
+      mz = fmaxf(mz, max4f(lz[tid + i * NT]));
+      mu = fmaxf(mu, max4f(lu[tid + i * NT]));
+    }
+    const float nbz = -(mz * kLog2e), nbu = -(mu * kLog2e);
+    sz0 = sz1 = su0 = su1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        expsum4f(rz[i], nbz, sz0, sz1);
+        expsum4f(ru[i], nbu, su0, su1);
+      }
+    }
+    for (int i = 0; i < nl; ++i) {
+      expsum4f(lz[tid + i * NT], nbz, sz0, sz1);
+      expsum4f(lu[tid + i * NT], nbu, su0, su1);
+    }
+  }
+  {
+    Lse pz = wave_lse(Lse{mz, sz0 + sz1});
+    Lse pu = wave_lse(Lse{mu, su0 + su1});
+    if ((tid & 63) == 0) {
+      red_z[tid >> 6] = pz;
+      red_u[tid >> 6] = pu;
+    }
+    if (tid == 0) s_zt = zt;
+  }
+  __syncthreads();
+  uint64_t* s1 = slot1 + r * (int64_t)K * 2;
+  if (tid == 0) {
+    Lse fz = red_z[0], fu = red_u[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      lse_merge(fz, red_z[w]);
+      lse_merge(fu, red_u[w]);
+    }
+    publish(s1 + 2 * j, pack2(fz.m, fz.s));
+    publish(s1 + 2 * j + 1, pack2(fu.m, fu.s));
+  }
+
+  // ---- exchange 1: the row's K (max, sum-exp) pairs, merged in member order
+  if (tid < 64) wait_slots(s1, 2 * K, got);
+  __syncthreads();
+  if (tid == 0) {
+    Lse fz{lo_f(got[0]), hi_f(got[0])}, fu{lo_f(got[1]), hi_f(got[1])};
+    for (int m = 1; m < K; ++m) {
+      lse_merge(fz, Lse{lo_f(got[2 * m]), hi_f(got[2 * m])});
+      lse_merge(fu, Lse{lo_f(got[2 * m + 1]), hi_f(got[2 * m + 1])});
+    }
+    s_bc[0] = lse_value(fz);
+    s_bc[1] = lse_value(fu);
+  }
+  __syncthreads();
+  const float lse_s = s_bc[0], lse_t = s_bc[1];
+
+  // ---- step 2 over the kept chunk: p' and s' replace the student's logits
+  const float nbs = pq_bias(lse_s), nbt = pq_bias(lse_t);
+  {
+    float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (i < n) {
+        launder(rz[i]);
+        launder(ru[i]);
+        tv4f_signs(rz[i], ru[i], nbs, nbt, Q0, Q1, S0, S1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      if (i < nl) {
+        u32x4_t wz = lz[tid + i * NT];
+        tv4f_signs(wz, lu[tid + i * NT], nbs, nbt, Q0, Q1, S0, S1);
+        lz[tid + i * NT] = wz;  // this thread's own slot: read back by it in step 3
+      }
+    }
+    const float Q = wave_sum(Q0 + Q1), S = wave_sum(S0 + S1);
+    if ((tid & 63) == 0) {
+      red_a[tid >> 6] = (S - Q) * kTvScale;
+      red_s[tid >> 6] = S * kTvScale;
+    }
+  }
+  __syncthreads();
+
+  // ---- exchange 2: every member sums the K pairs in member order (identical sigma)
+  uint64_t* s2 = slot2 + r * (int64_t)K;
+  if (tid == 0) {
+    float A = red_a[0], S = red_s[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      A += red_a[w];
+      S += red_s[w];
+    }
+    publish(s2 + j, pack2(A, S));
+  }
+  if (tid < 64) wait_slots(s2, K, got);
+  __syncthreads();
+  if (tid == 0) {
+    float A = lo_f(got[0]), S = hi_f(got[0]);
+    for (int m = 1; m < K; ++m) {
+      A += lo_f(got[m]);
+      S += hi_f(got[m]);
+    }
+    s_bc[2] = S;
+    if (j == jt) {
+      if (t_ok) ce[r] = lse_s - s_zt; else store_nan(ce + r);
+      tvd[r] = 0.5f * A;
+      lse_s_out[r] = lse_s;
+      lse_t_out[r] = lse_t;
+      sigma_out[r] = S;
+    }
+  }
+  __syncthreads();
+
+  // ---- step 3: G = p' * (a1 + b1 * s') - k * g_ce * [v == t], in bf16
+  const float kce = k * g_ce;
+  const float beta = 0.5f * k * g_tvd;
+  const float alpha = kce - beta * s_bc[2];
+  const float a1 = alpha * kInvPqBias, b1 = beta * kTvScale;
+  const int trel = j == jt ? (int)(t - 4 * (int64_t)qb) : -1;
+  if (!t_ok) {
+    // a target outside [0, V) makes the row's gradient NaN
+    const unsigned h = kQNaN16 | ((unsigned)kQNaN16 << 16);
+#pragma unroll
+    for (int i = 0; i < G + GL; ++i) st8_stream(rsg, (tid + i * NT) * 8, (u32x2_t){h, h});
+    return;
+  }
+  const float pt = exp2_hw(exparg(s_zt, nbs));
+  float zero = 0.f;
+  asm volatile("" : "+v"(zero));
+  const float M = k * (fabsf(g_ce) + fabsf(g_tvd));
+  if (!(M <= kKeepP16Bound)) {
+    // a quad holding a p' above thr is formed from its student logits, loaded again
+    const _Float16 thr = (_Float16)(0x1p15f * kKeepP16Bound * (1.0f - 0x1p-9f) / M);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int q = tid + i * NT;
+      launder(rz[i]);
+      const u32x2_t o = any_above4(rz[i], thr) ? grad4f_exact(ld_stream(rsz, q * 16), rz[i], nbs, trel - 4 * q, a1, b1, kce)
+                                               : grad4f(rz[i], a1, b1, zero, trel - 4 * q, pt, kce);
+      st8_stream(rsg, q * 8, o);
+    }
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      const int q = NT * G + tid + i * NT;
+      const u32x4_t w = lz[tid + i * NT];
+      const u32x2_t o = any_above4(w, thr) ? grad4f_exact(ld_stream(rsz, q * 16), w, nbs, trel - 4 * q, a1, b1, kce)
+                                           : grad4f(w, a1, b1, zero, trel - 4 * q, pt, kce);
+      st8_stream(rsg, q * 8, o);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int q = tid + i * NT;
+    st8_stream(rsg, q * 8, grad4f(rz[i], a1, b1, zero, trel - 4 * q, pt, kce));
+  }
+#pragma unroll
+  for (int i = 0; i < GL; ++i) {
+    const int q = NT * G + tid + i * NT;
+    st8_stream(rsg, q * 8, grad4f(lz[tid + i * NT], a1, b1, zero, trel - 4 * q, pt, kce));
+  }
+}
+
 // ---------------------------------------------------------------- one-pass CE-only forward + backward
 //
 // With no teacher the one pass needs a single exchange (the student lse).
@@ -829,10 +1206,11 @@ constexpr int kFusedCeWavesPerSimd = 3;
 // 1024 (K = 16) 44 / 59 us, 2048 (K = 32) 59 / 81 us, 256 (K = 7) 38 / 44 us.
 constexpr int64_t kClTargetTiles = 512;
 
-static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups) {
+// Members per row and units (16-byte groups) per member for BT rows of NG
+// units, nt threads holding `groups` units each.
+static ClusterPlan plan_units(int64_t BT, int64_t NG, int nt, int groups) {
   ClusterPlan c{0, 0, 0};
-  if (esize != 2 || V % 8 != 0 || BT <= 0) return c;
-  const int64_t NG = V / 8;
+  if (BT <= 0) return c;
   if (NG < nt) return c;  // short rows: the one-workgroup-per-row path is as good
   const int64_t cap = (int64_t)nt * groups;
   const int64_t k_fit = (NG + cap - 1) / cap;        // fewest members whose chunks fit in registers
@@ -850,6 +1228,21 @@ static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups
   const size_t counters = ((size_t)BT + 1) * sizeof(unsigned);
   c.workspace_bytes = (slots + counters + 255) & ~(size_t)255;
   return c;
+}
+
+static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups) {
+  if (esize != 2 || V % 8 != 0 || BT <= 0) return ClusterPlan{0, 0, 0};
+  return plan_units(BT, V / 8, nt, groups);
+}
+
+// fp32 one pass of the lm_head path: quads of 4 logits, 15 in registers and
+// 4 in LDS per thread and tensor (the bf16 kernel's budget)
+constexpr int kF32Groups = 15;
+constexpr int kF32LdsGroups = 4;
+
+ClusterPlan plan_linear_onepass(int64_t BT, int64_t V) {
+  if (V % 4 != 0 || BT <= 0) return ClusterPlan{0, 0, 0};
+  return plan_units(BT, V / 4, kClThreads, kF32Groups + kF32LdsGroups);
 }
 
 ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
@@ -916,6 +1309,17 @@ static hipError_t launch_fused_cluster_t(const FwdArgs& a, const FusedGrad& g, c
                        dim3(kFusedCeThreads), 0, st, zs, a.target, (int)a.V, a.lds, g.ldg, a.ignore_index, c.K, c.gpm,
                        a.ce, a.lse_s, gr, g.g_ce, g.gce_rows, g.g_scale, w.slot1, w.ticket);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_onepass(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
+  (void)hipGetLastError();
+  const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
+  hipLaunchKernelGGL((cluster_f32_kernel<kClThreads, kF32Groups, kF32LdsGroups, kClWavesPerSimd>),
+                     dim3((unsigned)(a.BT * (int64_t)c.K)), dim3(kClThreads), 0, st,
+                     static_cast<const float*>(a.student), static_cast<const float*>(a.teacher), a.target, (int)a.V,
+                     a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
+                     static_cast<uint16_t*>(g.grad), g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.ticket);
   return hipGetLastError();
 }
 

@@ -9,7 +9,9 @@
 // optionally teacher X_t, W_t:
 //
 //   z = X_s W_s^T, u = X_t W_t^T                  (bf16 MFMA products, fp32 logits)
-//   ce, tvd, lse_s, lse_t, sigma, G = dL/dz       (the loss kernels; G in bf16)
+//   ce, tvd, lse_s, lse_t, sigma, G = dL/dz       (the loss kernels; G in bf16;
+//                                                  with a teacher one pass over
+//                                                  the logits, cluster_f32_kernel)
 //   dX_s = G W_s,  dW_s = G^T X_s                 (bf16 MFMA products, fp32)
 //
 // The rows run in chunks of `chunk_rows`: the chunk's logits (fp32) and G
@@ -41,10 +43,16 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t rows, int64_t V, bool teacher
   LinearWs w{};
   const size_t zl = align256((size_t)rows * (size_t)V * 4);
   const size_t gl = align256((size_t)rows * (size_t)V * 2);
-  size_t fl = plan_forward(rows, V, 4, teacher).workspace_bytes;
+  // the loss's workspace: the forward's, or the one pass's (with a teacher)
+  auto loss_ws = [&](int64_t n) {
+    const size_t f = plan_forward(n, V, 4, teacher).workspace_bytes;
+    const size_t o = teacher ? plan_linear_onepass(n, V).workspace_bytes : 0;
+    return f > o ? f : o;
+  };
+  size_t fl = loss_ws(rows);
   const int64_t tail = BT % rows;
   if (tail) {
-    const size_t ft = plan_forward(tail, V, 4, teacher).workspace_bytes;
+    const size_t ft = loss_ws(tail);
     fl = ft > fl ? ft : fl;
   }
   fl = align256(fl);
@@ -78,7 +86,7 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
       GemmArgs gu{a.x_t + r0 * a.H_t, a.H_t, a.w_t, a.H_t, w.u, V, rows, V, a.H_t, true, true, false};
       if (hipError_t e = launch_gemm_bf16(gu, st)) return e;
     }
-    // the loss over the chunk's fp32 logits
+    // the loss over the chunk's fp32 logits (and G = dL/dz in bf16)
     FwdArgs f{};
     f.student = w.z;
     f.teacher = w.u;
@@ -96,30 +104,40 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     f.vec = 1;
     f.rows16 = 1;
     f.workspace = w.fwd;
-    if (hipError_t e = launch_forward(f, plan_forward(rows, V, 4, teacher), Dt::F32, st)) return e;
-    if (!a.grad_x_s && !a.grad_w_s) continue;
-    // G = dL/dz in bf16
-    BwdArgs b{};
-    b.grad = w.g;
-    b.student = w.z;
-    b.teacher = w.u;
-    b.target = a.target + r0;
-    b.BT = rows;
-    b.V = V;
-    b.ignore_index = a.ignore_index;
-    b.ldg = V;
-    b.lds = V;
-    b.ldt = V;
-    b.lse_s = f.lse_s;
-    b.lse_t = f.lse_t;
-    b.sigma = f.sigma;
-    b.g_ce = a.g_ce;
-    b.g_tvd = a.g_tvd;
-    b.g_scale = a.g_scale;
-    b.vec = 1;  // V % 8 == 0 and 256-byte aligned chunks: every fp32 and bf16 row on a 16-byte boundary
-    b.v0 = 0;
-    b.V_total = V;
-    if (hipError_t e = launch_backward_f32_to_bf16(b, st)) return e;
+    const bool grads = a.grad_x_s || a.grad_w_s;
+    const ClusterPlan op = (teacher && grads) ? plan_linear_onepass(rows, V) : ClusterPlan{0, 0, 0};
+    if (op.K > 0) {
+      // forward and G in one pass over the logits
+      const FusedGrad fg{w.g, V, a.g_ce, a.g_tvd, nullptr, nullptr, a.g_scale};
+      if (hipError_t e = launch_linear_onepass(f, fg, op, st)) return e;
+    } else {
+      if (hipError_t e = launch_forward(f, plan_forward(rows, V, 4, teacher), Dt::F32, st)) return e;
+    }
+    if (!grads) continue;
+    // G = dL/dz in bf16 (when the one pass has not formed it)
+    if (op.K == 0) {
+      BwdArgs b{};
+      b.grad = w.g;
+      b.student = w.z;
+      b.teacher = w.u;
+      b.target = a.target + r0;
+      b.BT = rows;
+      b.V = V;
+      b.ignore_index = a.ignore_index;
+      b.ldg = V;
+      b.lds = V;
+      b.ldt = V;
+      b.lse_s = f.lse_s;
+      b.lse_t = f.lse_t;
+      b.sigma = f.sigma;
+      b.g_ce = a.g_ce;
+      b.g_tvd = a.g_tvd;
+      b.g_scale = a.g_scale;
+      b.vec = 1;  // V % 8 == 0 and 256-byte aligned chunks: every fp32 and bf16 row on a 16-byte boundary
+      b.v0 = 0;
+      b.V_total = V;
+      if (hipError_t e = launch_backward_f32_to_bf16(b, st)) return e;
+    }
     if (a.grad_x_s) {  // dX_s[chunk] = G W_s
       GemmArgs gx{w.g, V, a.w_s, a.H_s, a.grad_x_s + r0 * a.H_s, a.H_s, rows, a.H_s, V, true, false, false};
       if (hipError_t e = launch_gemm_bf16(gx, st)) return e;
