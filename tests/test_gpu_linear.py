@@ -12,6 +12,10 @@
   The gradients of x and w carry G rounded to bf16, so their bound is
   2^-8 relative to the matching product of magnitudes, |G| |w| and |G|^T |x|,
   plus the fp32 accumulation bound K 2^-23 of the same magnitudes.
+* The one pass over the fp32 logits element by element: with identity hidden
+  states the logits are exact and grad_w = G^T exactly, so G is checked like
+  the one-pass kernels' gradient (member counts with and without an LDS part,
+  a short last member, both the fp16-p and the logits-reloading step 3).
 * The benchmark's configuration (8192 x 151936, hidden size 4096) on sampled
   rows, and the identity <dW, w> = <dX, x> (both equal <G, z>).
 """
@@ -23,7 +27,7 @@ import torch
 
 import oracle
 import workloads as W
-from _parity import DEV, TIE_ABS, TIE_REL, announce, check_forward, to_dev
+from _parity import DEV, TIE_ABS, TIE_REL, announce, bits32, check_forward, check_grad, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +162,31 @@ def test_linear_matches_the_oracle(BT, V, H_s, H_t, chunk, teacher):
     assert np.all(ex <= bx), f"{label}: grad_x_s max excess {np.max(ex / bx)} of its bound"
     assert np.all(ew <= bw), f"{label}: grad_w_s max excess {np.max(ew / bw)} of its bound"
     assert np.all(gx.cpu().numpy()[t == II] == 0.0), "ignored rows must have a zero hidden-state gradient"
+
+
+@pytest.mark.parametrize("BT,V,g_ce,g_tvd", [(64, 151936, 1e-3, 1e-3), (64, 151936, 0.5, 1.5), (40, 8200, 0.5, 1.5)],
+                         ids=["64x151936_fp16_p", "64x151936_reloaded_p", "40x8200_ragged_members"])
+def test_linear_one_pass_gradient_elementwise(BT, V, g_ce, g_tvd):
+    """Identity hidden states (H = BT) make the logits the weights' columns exactly
+    and grad_w_s = G^T exactly (one product per element), so the one pass over the
+    fp32 logits is checked element by element: the outputs against the oracle and G
+    within the gradient tolerance; 64 x 151936 runs K = 8 members with an LDS part,
+    once with the gradient scale inside the fp16-p bound and once beyond it (the
+    groups with a large p formed from their logits); 40 x 8200 has a short last
+    member."""
+    _, w_s, _, w_t, t = W.linear_inputs(BT, V, BT, BT, seed=BT + V, logit_scale=2.5 * np.sqrt(BT))
+    eye = W.bf16_bits_rne(np.eye(BT, dtype=np.float32))
+    label = f"linear one pass {BT}x{V} g {g_ce}/{g_tvd}"
+    announce(label)
+    out, _, gw = run_linear(eye, w_s, eye, w_t, t, g_ce, g_tvd, BT)
+    z = oracle.decode(w_s).T.astype(np.float32)
+    u = oracle.decode(w_t).T.astype(np.float32)
+    check_forward(out, z, u, t, II, label)
+    G = gw.cpu().numpy().T.astype(np.float64)
+    valid = t != II
+    assert np.all(G[~valid] == 0.0), f"{label}: ignored rows must have a zero gradient"
+    bits = np.where(valid[:, None], bits32(G.astype(np.float32)), 0)
+    check_grad(G, bits, z, u, t, II, g_ce, g_tvd, label)
 
 
 def test_linear_forward_only_and_device_scale():
