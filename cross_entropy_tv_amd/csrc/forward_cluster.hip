@@ -661,17 +661,19 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
 
 // ---------------------------------------------------------------- one pass over fp32 logits (lm_head path)
 //
-// The lm_head path's logits are fp32 (the matrix products' output) and its
-// student gradient G is bf16, in a buffer of its own.  cluster_f32_kernel is
-// cluster_kernel<..., FUSED = true> for that case, with groups of 4 fp32
-// logits (16 bytes) where the bf16 kernel has 8: half the logits per
-// register, so a 151936-logit row takes K = 8 member workgroups.  Step 2
-// keeps the quad's p' and s' (fp16, 8 bytes each) in the registers of its
-// student logits, and step 3 writes 4 bf16 gradients (8 bytes) per quad.
-// Rows are contiguous (row stride V), V a multiple of 4, every row of the
-// logits on a 16-byte boundary.  Per element the arithmetic is that of
-// cluster_kernel<..., true>, and with a gradient scale beyond kKeepP16Bound
-// the quads that hold a large p are formed from their logits, loaded again.
+// cluster_f32_kernel is cluster_kernel<..., FUSED = true> for fp32 logits,
+// with groups of 4 fp32 logits (16 bytes) where the bf16 kernel has 8: half
+// the logits per register, so a 151936-logit row takes K = 8 member
+// workgroups.  Step 2 keeps the quad's p' and s' (fp16, 8 bytes each) in the
+// registers of its student logits, and step 3 writes 4 gradients per quad, as
+// fp32 (TG = float: the one pass of fp32 logits, gradient in place or not)
+// or as bf16 (TG = uint16_t: the lm_head path, whose logits are the matrix
+// products' fp32 output and whose gradient G feeds bf16 products).  V a
+// multiple of 4, every row on a 16-byte boundary.  Per element the
+// arithmetic is that of cluster_kernel<..., true>, per-row factors
+// included, and with a gradient scale beyond kKeepP16Bound the quads that
+// hold a large p are formed from their logits, loaded again (each before its
+// own gradient is stored, so in place holds).
 
 namespace {
 
@@ -717,9 +719,38 @@ __device__ __forceinline__ void tv4f_signs(u32x4_t& wz, const u32x4_t& wu, float
   }
   wz = (u32x4_t){pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(s[0], s[1]), pack_f16x2(s[2], s[3])};
 }
+// four gradients in the output type: bf16 pairs (8 bytes) or fp32 (16 bytes)
+template <typename TG>
+struct Out4;
+template <>
+struct Out4<uint16_t> {
+  typedef u32x2_t type;
+  static __device__ __forceinline__ type pack(const float (&o)[4]) {
+    return (u32x2_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  }
+  static __device__ __forceinline__ type fill(unsigned w) { return (u32x2_t){w, w}; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int q, type v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, q * 8, 0, kStreamPolicy);
+  }
+  static constexpr unsigned kNaN = kQNaN16 | ((unsigned)kQNaN16 << 16);
+};
+template <>
+struct Out4<float> {
+  typedef u32x4_t type;
+  static __device__ __forceinline__ type pack(const float (&o)[4]) {
+    return (u32x4_t){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+  }
+  static __device__ __forceinline__ type fill(unsigned w) { return (u32x4_t){w, w, w, w}; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int q, type v) {
+    st_stream(rs, q * 16, v);
+  }
+  static constexpr unsigned kNaN = kQNaN32;
+};
+
 // step 3 of a quad from its p' and s' (the target element, rel in [0, 4), from pt in fp32)
-__device__ __forceinline__ u32x2_t grad4f(const u32x4_t& w, float a1, float b1, float zero, int rel, float pt,
-                                          float kce) {
+template <typename TG>
+__device__ __forceinline__ typename Out4<TG>::type grad4f(const u32x4_t& w, float a1, float b1, float zero, int rel,
+                                                          float pt, float kce) {
   float p[4], sg[4], o[4];
   const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
   unpack_f16x2(w0, p[0], p[1]);
@@ -732,11 +763,12 @@ __device__ __forceinline__ u32x2_t grad4f(const u32x4_t& w, float a1, float b1, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (e == rel) ? pt * __builtin_fmaf(sg[e], b1, a1) - kce : o[e];
   }
-  return (u32x2_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  return Out4<TG>::pack(o);
 }
 // as grad4f with p' recomputed in fp32 from the quad's student logits wz
-__device__ __forceinline__ u32x2_t grad4f_exact(const u32x4_t& wz, const u32x4_t& w, float nbs, int rel, float a1,
-                                                float b1, float kce) {
+template <typename TG>
+__device__ __forceinline__ typename Out4<TG>::type grad4f_exact(const u32x4_t& wz, const u32x4_t& w, float nbs,
+                                                                int rel, float a1, float b1, float kce) {
   float x[4], sg[4], o[4];
   unpack4f(wz, x);
   const unsigned w2 = w.z, w3 = w.w;
@@ -748,7 +780,7 @@ __device__ __forceinline__ u32x2_t grad4f_exact(const u32x4_t& wz, const u32x4_t
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
   }
-  return (u32x2_t){pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  return Out4<TG>::pack(o);
 }
 // true when one of the quad's four fp16 p' (words x, y) exceeds thr
 __device__ __forceinline__ bool any_above4(const u32x4_t& w, _Float16 thr) {
@@ -756,20 +788,19 @@ __device__ __forceinline__ bool any_above4(const u32x4_t& w, _Float16 thr) {
   const h2_t m = __builtin_elementwise_max(as_h2(w0), as_h2(w1));
   return m.x > thr || m.y > thr;
 }
-__device__ __forceinline__ void st8_stream(__amdgpu_buffer_rsrc_t rs, int byte_off, u32x2_t v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, rs, byte_off, 0, kStreamPolicy);
-}
 
 }  // namespace
 
-template <int NT, int G, int GL, int WPE>
+template <typename TG, int NT, int G, int GL, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
-void cluster_f32_kernel(const float* __restrict__ student, const float* __restrict__ teacher,
-                        const int64_t* __restrict__ target, int V, int64_t ignore_index, int K, int qpm,
+void cluster_f32_kernel(const float* student, const float* __restrict__ teacher, const int64_t* __restrict__ target,
+                        int V, int64_t lds, int64_t ldt, int64_t ldg, int64_t ignore_index, int K, int qpm,
                         float* __restrict__ ce, float* __restrict__ tvd, float* __restrict__ lse_s_out,
-                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out, uint16_t* __restrict__ grad,
-                        float g_ce, float g_tvd, const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
+                        float* __restrict__ lse_t_out, float* __restrict__ sigma_out, TG* grad, float g_ce,
+                        float g_tvd, const float* __restrict__ gce_rows, const float* __restrict__ gtvd_rows,
+                        const float* __restrict__ g_scale, uint64_t* __restrict__ slot1,
                         uint64_t* __restrict__ slot2, unsigned* __restrict__ ticket) {
+  typedef Out4<TG> O;
   constexpr int W = NT / 64;
   __shared__ Lse red_z[W], red_u[W];
   __shared__ float red_a[W], red_s[W];
@@ -786,21 +817,24 @@ void cluster_f32_kernel(const float* __restrict__ student, const float* __restri
   const int64_t r = tile / (unsigned)K;
   const int j = (int)(tile - (unsigned)r * (unsigned)K);
   const int64_t t = target[r];
+  // the row's upstream gradients, read now so that the loads are long done by step 3
   const float k = g_scale ? *g_scale : 1.0f;
+  const float gce = g_ce * (gce_rows ? gce_rows[r] : 1.0f);
+  const float gtvd = g_tvd * (gtvd_rows ? gtvd_rows[r] : 1.0f);
 
   // ---- this member's chunk: quads [qb, qe) of the row; thread tid owns qb + tid + i * NT
   const int NQ = V >> 2;
   const int qb = j * qpm;
   const int qe = min(NQ, qb + qpm);
   const int cnt = qe - qb;
-  const int64_t row = r * (int64_t)V;
-  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + row + 4 * (int64_t)qb, cnt * 8);
+  const int64_t rowz = r * lds, rowu = r * ldt, rowg = r * ldg;
+  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 4 * (int64_t)qb, cnt * 4 * (int)sizeof(TG));
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
       ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < G + GL; ++i) st8_stream(rsg, (tid + i * NT) * 8, (u32x2_t){0u, 0u});
+    for (int i = 0; i < G + GL; ++i) O::store(rsg, tid + i * NT, O::fill(0u));
     return;
   }
   const int n = tid < cnt ? min(G, (cnt - tid - 1) / NT + 1) : 0;
@@ -808,10 +842,10 @@ void cluster_f32_kernel(const float* __restrict__ student, const float* __restri
   const bool t_ok = t >= 0 && t < V;
   const int jt = t_ok ? (int)(t >> 2) / qpm : 0;  // the member whose chunk holds the target
   float zt = 0.f;
-  if (j == jt && tid == 0 && t_ok) zt = student[row + t];
+  if (j == jt && tid == 0 && t_ok) zt = student[rowz + t];
 
-  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + row + 4 * (int64_t)qb, cnt * 16);
-  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + row + 4 * (int64_t)qb, cnt * 16);
+  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + rowz + 4 * (int64_t)qb, cnt * 16);
+  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + rowu + 4 * (int64_t)qb, cnt * 16);
   u32x4_t rz[G], ru[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -822,8 +856,8 @@ void cluster_f32_kernel(const float* __restrict__ student, const float* __restri
     // the rest of the chunk goes straight to LDS, 64 quads (1 KB) per load
     const int lcnt = cnt - NT * G;
     const int64_t lo = 4 * (int64_t)(qb + NT * G);
-    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + row + lo, lcnt * 16);
-    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + row + lo, lcnt * 16);
+    const __amdgpu_buffer_rsrc_t lrz = chunk_rsrc(student + rowz + lo, lcnt * 16);
+    const __amdgpu_buffer_rsrc_t lru = chunk_rsrc(teacher + rowu + lo, lcnt * 16);
     const int lane = tid & 63;
     for (int b = tid >> 6; b < (lcnt + 63) >> 6; b += W) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrz, (__attribute__((address_space(3))) void*)&lz[b * 64], 16,
@@ -986,23 +1020,22 @@ void cluster_f32_kernel(const float* __restrict__ student, const float* __restri
   }
   __syncthreads();
 
-  // ---- step 3: G = p' * (a1 + b1 * s') - k * g_ce * [v == t], in bf16
-  const float kce = k * g_ce;
-  const float beta = 0.5f * k * g_tvd;
+  // ---- step 3: g = p' * (a1 + b1 * s') - k * g_ce * [v == t]
+  const float kce = k * gce;
+  const float beta = 0.5f * k * gtvd;
   const float alpha = kce - beta * s_bc[2];
   const float a1 = alpha * kInvPqBias, b1 = beta * kTvScale;
   const int trel = j == jt ? (int)(t - 4 * (int64_t)qb) : -1;
   if (!t_ok) {
     // a target outside [0, V) makes the row's gradient NaN
-    const unsigned h = kQNaN16 | ((unsigned)kQNaN16 << 16);
 #pragma unroll
-    for (int i = 0; i < G + GL; ++i) st8_stream(rsg, (tid + i * NT) * 8, (u32x2_t){h, h});
+    for (int i = 0; i < G + GL; ++i) O::store(rsg, tid + i * NT, O::fill(O::kNaN));
     return;
   }
   const float pt = exp2_hw(exparg(s_zt, nbs));
   float zero = 0.f;
   asm volatile("" : "+v"(zero));
-  const float M = k * (fabsf(g_ce) + fabsf(g_tvd));
+  const float M = k * (fabsf(gce) + fabsf(gtvd));
   if (!(M <= kKeepP16Bound)) {
     // a quad holding a p' above thr is formed from its student logits, loaded again
     const _Float16 thr = (_Float16)(0x1p15f * kKeepP16Bound * (1.0f - 0x1p-9f) / M);
@@ -1010,29 +1043,31 @@ void cluster_f32_kernel(const float* __restrict__ student, const float* __restri
     for (int i = 0; i < G; ++i) {
       const int q = tid + i * NT;
       launder(rz[i]);
-      const u32x2_t o = any_above4(rz[i], thr) ? grad4f_exact(ld_stream(rsz, q * 16), rz[i], nbs, trel - 4 * q, a1, b1, kce)
-                                               : grad4f(rz[i], a1, b1, zero, trel - 4 * q, pt, kce);
-      st8_stream(rsg, q * 8, o);
+      const typename O::type o =
+          any_above4(rz[i], thr) ? grad4f_exact<TG>(ld_stream(rsz, q * 16), rz[i], nbs, trel - 4 * q, a1, b1, kce)
+                                 : grad4f<TG>(rz[i], a1, b1, zero, trel - 4 * q, pt, kce);
+      O::store(rsg, q, o);
     }
 #pragma unroll
     for (int i = 0; i < GL; ++i) {
       const int q = NT * G + tid + i * NT;
       const u32x4_t w = lz[tid + i * NT];
-      const u32x2_t o = any_above4(w, thr) ? grad4f_exact(ld_stream(rsz, q * 16), w, nbs, trel - 4 * q, a1, b1, kce)
-                                           : grad4f(w, a1, b1, zero, trel - 4 * q, pt, kce);
-      st8_stream(rsg, q * 8, o);
+      const typename O::type o =
+          any_above4(w, thr) ? grad4f_exact<TG>(ld_stream(rsz, q * 16), w, nbs, trel - 4 * q, a1, b1, kce)
+                             : grad4f<TG>(w, a1, b1, zero, trel - 4 * q, pt, kce);
+      O::store(rsg, q, o);
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int q = tid + i * NT;
-    st8_stream(rsg, q * 8, grad4f(rz[i], a1, b1, zero, trel - 4 * q, pt, kce));
+    O::store(rsg, q, grad4f<TG>(rz[i], a1, b1, zero, trel - 4 * q, pt, kce));
   }
 #pragma unroll
   for (int i = 0; i < GL; ++i) {
     const int q = NT * G + tid + i * NT;
-    st8_stream(rsg, q * 8, grad4f(lz[tid + i * NT], a1, b1, zero, trel - 4 * q, pt, kce));
+    O::store(rsg, q, grad4f<TG>(lz[tid + i * NT], a1, b1, zero, trel - 4 * q, pt, kce));
   }
 }
 
@@ -1235,7 +1270,7 @@ static ClusterPlan plan_cfg(int64_t BT, int64_t V, int esize, int nt, int groups
   return plan_units(BT, V / 8, nt, groups);
 }
 
-// fp32 one pass of the lm_head path: quads of 4 logits, 15 in registers and
+// fp32 one pass (fp32 logits, and the lm_head path): quads of 4 logits, 15 in registers and
 // 4 in LDS per thread and tensor (the bf16 kernel's budget)
 constexpr int kF32Groups = 15;
 constexpr int kF32LdsGroups = 4;
@@ -1251,6 +1286,7 @@ ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
 }
 
 ClusterPlan plan_fused(int64_t BT, int64_t V, int esize, bool teacher) {
+  if (esize == 4) return teacher ? plan_linear_onepass(BT, V) : ClusterPlan{0, 0, 0};
   return teacher ? plan_cfg(BT, V, esize, kClThreads, kClGroups + kClLdsGroups)
                  : plan_cfg(BT, V, esize, kFusedCeThreads, kFusedCeGroups);
 }
@@ -1312,18 +1348,25 @@ static hipError_t launch_fused_cluster_t(const FwdArgs& a, const FusedGrad& g, c
   return hipGetLastError();
 }
 
-hipError_t launch_linear_onepass(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
+template <typename TG>
+static hipError_t launch_f32_onepass_t(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
-  hipLaunchKernelGGL((cluster_f32_kernel<kClThreads, kF32Groups, kF32LdsGroups, kClWavesPerSimd>),
+  hipLaunchKernelGGL((cluster_f32_kernel<TG, kClThreads, kF32Groups, kF32LdsGroups, kClWavesPerSimd>),
                      dim3((unsigned)(a.BT * (int64_t)c.K)), dim3(kClThreads), 0, st,
                      static_cast<const float*>(a.student), static_cast<const float*>(a.teacher), a.target, (int)a.V,
-                     a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
-                     static_cast<uint16_t*>(g.grad), g.g_ce, g.g_tvd, g.g_scale, w.slot1, w.slot2, w.ticket);
+                     a.lds, a.ldt, g.ldg, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,
+                     static_cast<TG*>(g.grad), g.g_ce, g.g_tvd, g.gce_rows, g.gtvd_rows, g.g_scale, w.slot1, w.slot2,
+                     w.ticket);
   return hipGetLastError();
 }
 
+hipError_t launch_linear_onepass(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
+  return launch_f32_onepass_t<uint16_t>(a, g, c, st);
+}
+
 hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, Dt dt, hipStream_t st) {
+  if (dt == Dt::F32) return launch_f32_onepass_t<float>(a, g, c, st);  // with a teacher (plan_fused)
   return dt == Dt::F16 ? launch_fused_cluster_t<_Float16>(a, g, c, st) : launch_fused_cluster_t<uint16_t>(a, g, c, st);
 }
 

@@ -84,9 +84,10 @@ struct FusedGrad {
 hipError_t launch_fused_cluster(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, Dt dt,
                                 hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, Dt dt, hipStream_t stream);
-// One pass over contiguous fp32 logits with a teacher (row stride V, V a
-// multiple of 4, rows on 16-byte boundaries), the student gradient in bf16
-// (g.grad, row stride V, no row factors): the lm_head path's loss.
+// One pass over fp32 logits with a teacher (V a multiple of 4, rows on
+// 16-byte boundaries), the student gradient in bf16 (g.grad, row stride
+// g.ldg): the lm_head path's loss.  launch_fused_cluster with Dt::F32 runs
+// the same kernel with an fp32 gradient.
 ClusterPlan plan_linear_onepass(int64_t BT, int64_t V);
 hipError_t launch_linear_onepass(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t stream);
 // fp32 logits, bf16 gradient (rounded to nearest even); vec must be 0 unless

@@ -80,7 +80,9 @@ def test_forward_validation():
     assert wf >= ws and any(wf == (8192 * k * 24 + counters + 255) // 256 * 256 for k in range(2, 33))
     # CE-only one pass: one exchange slot per member is used, the same layout is reserved
     assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 1, 0) > 0
-    assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 0, 1) == 0   # f32: two passes
+    # f32 with a teacher: the one pass over quads of 4 fp32 logits, 8 members per row
+    assert lx.lx_ce_tvd_forward_backward_workspace_bytes(8192, 151936, 0, 1) == \
+        (8192 * 8 * 24 + (8192 + 1) * 4 + 255) // 256 * 256
     assert fwd(V=100000, teacher=A * 2) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6, wsb=need - 4) == lx.LX_ERR_WORKSPACE
     assert fwd(V=100000, teacher=A * 2, ws=A * 6 + 16, wsb=need) == lx.LX_ERR_WORKSPACE  # 256-B alignment
