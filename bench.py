@@ -279,6 +279,13 @@ def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
 
     # the headline call again, for reference next to the variants (same process, same memory state)
     record("reference", _time_call(plain, steps, warmup))
+    # per-row upstream gradients of an unreduced loss (factors ~ U(0.5, 1.5))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    wce = torch.rand(BT, generator=gen, device=dev) + 0.5
+    wtv = torch.rand(BT, generator=gen, device=dev) + 0.5
+    record("row_factors", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
+        zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, wce, wtv, inv, ws, stream), steps, warmup))
     # binary16 logits: the bf16 batch rounded to binary16
     z16, u16 = zs.to(torch.float16), us.to(torch.float16)
     g16 = torch.empty_like(z16)
@@ -298,13 +305,6 @@ def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
         zv, uv, tg, -100, ce, tvd, lse_s, lse_t, sigma, gv, 1.0, 1.0, g_scale=inv, workspace=ws, stream=stream),
         steps, warmup), {"row_stride": V + pad})
     del zbig, ubig, gbig
-    # per-row upstream gradients of an unreduced loss (factors ~ U(0.5, 1.5))
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(20261202)
-    wce = torch.rand(BT, generator=gen, device=dev) + 0.5
-    wtv = torch.rand(BT, generator=gen, device=dev) + 0.5
-    record("row_factors", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
-        zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, wce, wtv, inv, ws, stream), steps, warmup))
     record("reference_after", _time_call(plain, steps, warmup))
     return out
 
