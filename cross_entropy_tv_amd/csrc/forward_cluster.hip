@@ -791,7 +791,10 @@ __device__ __forceinline__ bool any_above4(const u32x4_t& w, _Float16 thr) {
 
 }  // namespace
 
-template <typename TG, int NT, int G, int GL, int WPE>
+// GRAD = false: the forward alone (no gradient, grad may be NULL): every
+// member still waits for exchange 2, and the member holding the target writes
+// the row's outputs.
+template <typename TG, bool GRAD, int NT, int G, int GL, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(WPE, WPE)))
 void cluster_f32_kernel(const float* student, const float* __restrict__ teacher, const int64_t* __restrict__ target,
                         int V, int64_t lds, int64_t ldt, int64_t ldg, int64_t ignore_index, int K, int qpm,
@@ -833,8 +836,10 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
     if (j == 0 && tid == 0) {
       ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
     }
+    if (GRAD) {
 #pragma unroll
-    for (int i = 0; i < G + GL; ++i) O::store(rsg, tid + i * NT, O::fill(0u));
+      for (int i = 0; i < G + GL; ++i) O::store(rsg, tid + i * NT, O::fill(0u));
+    }
     return;
   }
   const int n = tid < cnt ? min(G, (cnt - tid - 1) / NT + 1) : 0;
@@ -1018,6 +1023,7 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
       sigma_out[r] = S;
     }
   }
+  if (!GRAD) return;
   __syncthreads();
 
   // ---- step 3: g = p' * (a1 + b1 * s') - k * g_ce * [v == t]
@@ -1282,6 +1288,7 @@ ClusterPlan plan_linear_onepass(int64_t BT, int64_t V) {
 
 ClusterPlan plan_cluster(int64_t BT, int64_t V, int esize, bool teacher) {
   if (!teacher) return ClusterPlan{0, 0, 0};  // CE-only: one stream, the row path already reads it once
+  if (esize == 4) return plan_linear_onepass(BT, V);
   return plan_cfg(BT, V, esize, kClThreads, kClGroups + kClLdsGroups);
 }
 
@@ -1323,7 +1330,14 @@ static hipError_t launch_forward_cluster_t(const FwdArgs& a, const ClusterPlan& 
   return hipGetLastError();
 }
 
+template <typename TG, bool GRAD = true>
+static hipError_t launch_f32_onepass_t(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st);
+
 hipError_t launch_forward_cluster(const FwdArgs& a, const ClusterPlan& c, Dt dt, hipStream_t st) {
+  if (dt == Dt::F32) {  // the fp32 one-pass kernel without its step 3
+    const FusedGrad none{nullptr, a.V, 0.f, 0.f, nullptr, nullptr, nullptr};
+    return launch_f32_onepass_t<float, false>(a, none, c, st);
+  }
   return dt == Dt::F16 ? launch_forward_cluster_t<_Float16>(a, c, st) : launch_forward_cluster_t<uint16_t>(a, c, st);
 }
 
@@ -1348,11 +1362,11 @@ static hipError_t launch_fused_cluster_t(const FwdArgs& a, const FusedGrad& g, c
   return hipGetLastError();
 }
 
-template <typename TG>
+template <typename TG, bool GRAD>
 static hipError_t launch_f32_onepass_t(const FwdArgs& a, const FusedGrad& g, const ClusterPlan& c, hipStream_t st) {
   (void)hipGetLastError();
   const ClusterWs w = cluster_ws(a.workspace, a.BT, c.K, st);
-  hipLaunchKernelGGL((cluster_f32_kernel<TG, kClThreads, kF32Groups, kF32LdsGroups, kClWavesPerSimd>),
+  hipLaunchKernelGGL((cluster_f32_kernel<TG, GRAD, kClThreads, kF32Groups, kF32LdsGroups, kClWavesPerSimd>),
                      dim3((unsigned)(a.BT * (int64_t)c.K)), dim3(kClThreads), 0, st,
                      static_cast<const float*>(a.student), static_cast<const float*>(a.teacher), a.target, (int)a.V,
                      a.lds, a.ldt, g.ldg, a.ignore_index, c.K, c.gpm, a.ce, a.tvd, a.lse_s, a.lse_t, a.sigma,

@@ -70,7 +70,8 @@ def test_forward_validation():
     need = lx.lx_ce_tvd_workspace_bytes(4, 100000, 1, 1)
     assert need > 0 and lx.lx_ce_tvd_workspace_bytes(4, 100000, 1, 0) < need
     assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 0) == 0   # CE-only: one stream, no exchange
-    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 0, 1) == 0   # f32 rows: one workgroup per row
+    # f32 with a teacher: the read-once forward over quads of 4 fp32 logits, 8 members per row
+    assert lx.lx_ce_tvd_workspace_bytes(8192, 151936, 0, 1) == (8192 * 8 * 24 + (8192 + 1) * 4 + 255) // 256 * 256
     # bf16 with a teacher: the read-once path exchanges per-row partials of its K >= 2
     # member workgroups (3 64-bit slots per member) and keeps a counter per row + a ticket
     ws = lx.lx_ce_tvd_workspace_bytes(8192, 151936, 1, 1)
