@@ -332,6 +332,10 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
 
   const int tid = tid_x();
+  // A new tile's waves run at raised priority until its chunk's loads are
+  // issued, so that they go out ahead of the arithmetic of the other
+  // workgroups on the compute unit (1.5-2% on the 8192 x 151936 one passes).
+  __builtin_amdgcn_s_setprio(3);
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -396,6 +400,7 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- step 1: sums of exponentials against this thread's reference maxima
   float mz = kMFloor, mu = kMFloor;
   if (n > 0) {
@@ -814,6 +819,10 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
   __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
 
   const int tid = tid_x();
+  // A new tile's waves run at raised priority until its chunk's loads are
+  // issued, so that they go out ahead of the arithmetic of the other
+  // workgroups on the compute unit (1.5-2% on the 8192 x 151936 one passes).
+  __builtin_amdgcn_s_setprio(3);
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -872,6 +881,7 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- step 1: sums of exponentials against this thread's reference maxima
   float mz = kMFloor, mu = kMFloor;
   if (n > 0) {
@@ -1100,6 +1110,10 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   __shared__ float s_zt;
 
   const int tid = tid_x();
+  // A new tile's waves run at raised priority until its chunk's loads are
+  // issued, so that they go out ahead of the arithmetic of the other
+  // workgroups on the compute unit (1.5-2% on the 8192 x 151936 one passes).
+  __builtin_amdgcn_s_setprio(3);
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -1135,6 +1149,7 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
     u32x4_t rz[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       unpack8<T>(rz[i], ez[i]);
