@@ -819,10 +819,10 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
   __shared__ u32x4_t lz[GL > 0 ? GL * NT : 1], lu[GL > 0 ? GL * NT : 1];  // the LDS part of the chunk
 
   const int tid = tid_x();
-  // A new tile's waves run at raised priority until its chunk's loads are
-  // issued, so that they go out ahead of the arithmetic of the other
-  // workgroups on the compute unit (1.5-2% on the 8192 x 151936 one passes).
-  __builtin_amdgcn_s_setprio(3);
+  // Raised priority while the chunk's loads issue, as in cluster_kernel.  Over
+  // 8192 x 151936 fp32 logits it gains 1.5% when the gradient is fp32 but
+  // costs 4% when it is bf16 (2.12 against 2.04 ms), so only the former.
+  if constexpr (sizeof(TG) == 4) __builtin_amdgcn_s_setprio(3);
   if (tid == 0) s_tile = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned tile = s_tile;
@@ -881,7 +881,7 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
     }
   }
 
-  __builtin_amdgcn_s_setprio(0);
+  if constexpr (sizeof(TG) == 4) __builtin_amdgcn_s_setprio(0);
   // ---- step 1: sums of exponentials against this thread's reference maxima
   float mz = kMFloor, mu = kMFloor;
   if (n > 0) {
