@@ -145,9 +145,12 @@ def grad_bounds(ref, x_s, w_s, t, teacher, g_tvd, with_w=True):
 @pytest.mark.parametrize("teacher", [True, False], ids=["ce_tvd", "ce_only"])
 @pytest.mark.parametrize("BT,V,H_s,H_t,chunk", [(300, 8200, 136, 200, 300), (300, 8200, 136, 200, 128),
                                                 (600, 4096, 64, 96, 600), (600, 4096, 64, 96, 1000),
-                                                (37, 2056, 256, 128, 16)],
+                                                (37, 2056, 256, 128, 16), (12, 2056, 256, 128, 2)],
                          ids=["300x8200_one_chunk", "300x8200_chunks_128", "600x4096_rowpath",
-                              "600x4096_chunk_above_rows", "37x2056_chunks_16"])
+                              "600x4096_chunk_above_rows", "37x2056_chunks_16",
+                              # chunks too short for the transposed copies of G and x to fit
+                              # over the logits: grad_w from G and x as they are
+                              "12x2056_chunks_2"])
 def test_linear_matches_the_oracle(BT, V, H_s, H_t, chunk, teacher):
     x_s, w_s, x_t, w_t, t = W.linear_inputs(BT, V, H_s, H_t if teacher else None, seed=BT + V + H_s)
     g_ce, g_tvd = 0.5, 1.5
