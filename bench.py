@@ -353,17 +353,19 @@ def run_linear(steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192):
     gen = torch.Generator(device=dev)
     gen.manual_seed(78)
     G = (torch.randn((R, V), generator=gen, device=dev) * 1e-5).to(torch.bfloat16)
+    Gt, Xt = G.t().contiguous(), X[:R].t().contiguous()
     gemms = {
         "logits_XWt": (lambda: lx.lx_gemm_bf16(X[:R], True, Wd, True, z, R, V, H, False, stream), R, V, H),
         "grad_x_GW": (lambda: lx.lx_gemm_bf16(G, True, Wd, False, gx[:R], R, H, V, False, stream), R, H, V),
-        "grad_w_GtX": (lambda: lx.lx_gemm_bf16(G, False, X[:R], False, gw, V, H, R, True, stream), V, H, R),
+        # as the call forms it: from the transposed copies of G and x (both K-contiguous)
+        "grad_w_GtX": (lambda: lx.lx_gemm_bf16(Gt, True, Xt, True, gw, V, H, R, True, stream), V, H, R),
     }
     for name, (fn, M, N, K) in gemms.items():
         t_ms = _time_call(fn, steps, warmup)
         fl = 2.0 * M * N * K
         out[name] = {"M": M, "N": N, "K": K, "ms": round(t_ms, 4), "TFLOPs": round(fl / t_ms / 1e9, 1),
                      "pct_mfma_peak": round(100.0 * fl / t_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
-    del z, G, ws, gx, gw
+    del z, G, Gt, Xt, ws, gx, gw
     return out
 
 
