@@ -96,11 +96,27 @@ def probs_rows(x: np.ndarray, lse: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- forward
 
-def forward(z_raw, u_raw, target, ignore_index: int = -100) -> dict:
+def _branch_signs(signs, valid: np.ndarray, shape) -> np.ndarray:
+    """The caller's sign vector for the valid rows (values -1, 0 or +1)."""
+    s = np.broadcast_to(np.asarray(signs, dtype=np.float64), shape)[valid]
+    if not np.all((s == -1.0) | (s == 0.0) | (s == 1.0)):
+        raise ValueError("signs must hold -1, 0 or +1")
+    return s
+
+
+def forward(z_raw, u_raw, target, ignore_index: int = -100, signs=None) -> dict:
     """Per-row forward outputs (float64 arrays of shape [R]).
 
     Returns dict(ce, tvd, lse_s, lse_t, sigma).  ``u_raw=None`` selects CE-only
     mode, where tvd, lse_t and sigma are returned as None.
+
+    ``signs`` (optional, shape [R, V], values -1, 0, +1) replaces sign(p - q) in
+    sigma.  |p - q| has a subgradient of every sign where p = q, and where p
+    and q agree to within the rounding of the arithmetic at hand any sign
+    branch is a correct answer; the page's tie rule (0 at ties) is the
+    default.  With explicit signs the result is the one for that branch, so a
+    kernel's output can be compared with the branch it took.  tvd does not
+    depend on the signs.
     """
     z = decode(z_raw)
     R, V = z.shape
@@ -124,16 +140,17 @@ def forward(z_raw, u_raw, target, ignore_index: int = -100) -> dict:
     p = probs_rows(zv, lse_s)
     q = probs_rows(uv, lse_t)
     d = p - q
+    s = np.sign(d) if signs is None else _branch_signs(signs, valid, z.shape)
     out["lse_t"][valid] = lse_t
     out["tvd"][valid] = 0.5 * np.sum(np.abs(d), axis=-1)
-    out["sigma"][valid] = np.sum(p * np.sign(d), axis=-1)
+    out["sigma"][valid] = np.sum(p * s, axis=-1)
     return out
 
 
 # ---------------------------------------------------------------- backward
 
 def backward(z_raw, u_raw, target, ignore_index: int = -100,
-             g_ce=1.0, g_tvd=1.0) -> np.ndarray:
+             g_ce=1.0, g_tvd=1.0, signs=None) -> np.ndarray:
     """d(sum_r g_ce[r] * ce[r] + g_tvd[r] * tvd[r])/dz for every row, float64 [R, V].
 
     "Backward Pass" of the PR #1384 analysis page: the cross-entropy part is
@@ -142,7 +159,9 @@ def backward(z_raw, u_raw, target, ignore_index: int = -100,
     recomputes lse, p, q and sigma itself from the logits.  Ignored rows are
     all +0.0.  ``u_raw=None`` is CE-only mode.  g_ce and g_tvd are the
     upstream gradients of each row's ce and tvd: scalars (the page's case)
-    or arrays of R per-row values (an unreduced loss).
+    or arrays of R per-row values (an unreduced loss).  ``signs`` is as in
+    ``forward``: the gradient of the branch with those signs (sigma formed
+    from them too).
     """
     z = decode(z_raw)
     R, V = z.shape
@@ -164,7 +183,7 @@ def backward(z_raw, u_raw, target, ignore_index: int = -100,
         uv = decode(u_raw)[valid]
         _check_rows(uv, "teacher")
         q = probs_rows(uv, logsumexp_rows(uv))
-        s = np.sign(p - q)
+        s = np.sign(p - q) if signs is None else _branch_signs(signs, valid, z.shape)
         sigma = np.sum(p * s, axis=-1, keepdims=True)
         gv = gv + g_tvd * 0.5 * p * (s - sigma)
     grad[valid] = gv

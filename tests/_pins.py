@@ -19,6 +19,9 @@ and raises AssertionError when it disagrees with an independent source:
   out-of-range targets raise; mean reduction including the all-ignored case;
 * ``row_weights``: per-row upstream gradients (an unreduced loss) against
   torch float64 autograd of sum_r w_ce[r] * CE_r + w_tvd[r] * TVD_r;
+* ``sign_branches``: results for an explicit sign vector (a near-tie branch)
+  against torch float64 autograd of the loss with |p - q| replaced by
+  s * (p - q), sigma recovered from that gradient;
 * ``linear_chain_rule``: the lm_head variant against torch float64 autograd
   through x @ w.T and central differences on single entries of x and w;
 * ``decoding``: every finite bf16 and binary16 bit pattern decodes to the value
@@ -307,6 +310,50 @@ def row_weights(orc):
            orc.backward(z, u, t, -100, 0.3, -1.1), what="constant row weights")
 
 
+# ------------------------------------------------------------ explicit sign branches
+
+def sign_branches(orc):
+    """Results for a given sign vector s (the branch of |p - q| a kernel took at
+    near ties): the loss g_ce*CE + g_tvd*0.5*sum_v s_v (p_v - q_v) has the
+    gradient the oracle gives for that branch (torch float64 autograd; s is a
+    constant), sigma of the branch follows from that gradient (with g_ce = 0 and
+    g_tvd = 1 every element is 0.5 p_v (s_v - sigma)), tvd does not move, and
+    the true signs reproduce the default results."""
+    import torch
+
+    rng = np.random.default_rng(17)
+    R, V = 5, 13
+    z = rng.normal(0, 2.0, size=(R, V))
+    u = rng.normal(0, 2.0, size=(R, V))
+    t = rng.integers(0, V, size=R)
+    t[3] = -100
+    valid = t != -100
+    s = rng.integers(-1, 2, size=(R, V)).astype(np.float64)
+    for g_ce, g_tvd in ((0.6, 1.4), (0.0, 1.0)):
+        zt = torch.from_numpy(z).requires_grad_(True)
+        ce = torch.nn.functional.cross_entropy(zt, torch.from_numpy(t), reduction="none", ignore_index=-100)
+        tv = 0.5 * (torch.from_numpy(s) * (torch.softmax(zt, -1) - torch.softmax(torch.from_numpy(u), -1))).sum(-1)
+        (g_ce * ce + g_tvd * tv * torch.from_numpy(valid.astype(np.float64))).sum().backward()
+        g = orc.backward(z, u, t, -100, g_ce, g_tvd, signs=s)
+        _close(g, zt.grad.numpy(), what=f"branch gradient vs autograd {g_ce},{g_tvd}")
+    # sigma of the branch from the autograd gradient of the total-variation part alone
+    pz = np.exp(z - z.max(1, keepdims=True))
+    pz /= pz.sum(1, keepdims=True)
+    gt = zt.grad.numpy()
+    fw = orc.forward(z, u, t, -100, signs=s)
+    for r in np.nonzero(valid)[0]:
+        v = int(np.argmax(pz[r]))
+        _close(fw["sigma"][r], s[r, v] - 2.0 * gt[r, v] / pz[r, v], tol=1e-10, what="branch sigma from gradient")
+    _close(fw["tvd"], orc.forward(z, u, t, -100)["tvd"], what="tvd independent of the branch")
+    # the true signs (softmaxes computed here) give the default results
+    pu = np.exp(u - u.max(1, keepdims=True))
+    pu /= pu.sum(1, keepdims=True)
+    st = np.sign(pz - pu)
+    _close(orc.forward(z, u, t, -100, signs=st)["sigma"], orc.forward(z, u, t, -100)["sigma"], what="true signs")
+    _close(orc.backward(z, u, t, -100, 0.3, 0.9, signs=st), orc.backward(z, u, t, -100, 0.3, 0.9),
+           what="true-sign gradient")
+
+
 # ------------------------------------------------------------ logits decoding
 
 def _ieee_value(bits: int, exp_bits: int, frac_bits: int) -> float:
@@ -387,5 +434,5 @@ def linear_chain_rule(orc):
                what=f"grad_w_s[{v},{k}] central difference")
 
 
-ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules, row_weights, decoding,
-            linear_chain_rule)
+ALL_PINS = (brute_force_decimal, closed_forms, library, invariants, ignore_rules, row_weights, sign_branches,
+            decoding, linear_chain_rule)

@@ -30,6 +30,8 @@ MUTANTS = {
     "linear_grad_x_sign": ('out["grad_x_s"] = g @ ws', 'out["grad_x_s"] = -g @ ws'),
     "linear_grad_w_from_teacher_hidden": ('out["grad_w_s"] = g.T @ xs', 'out["grad_w_s"] = g.T @ (xs if x_t_raw is None else decode(x_t_raw)[:, :xs.shape[1]])'),
     "linear_teacher_logits_transposed": ("decode(x_t_raw) @ decode(w_t_raw).T", "(decode(w_t_raw) @ decode(x_t_raw).T).T[:, ::-1]"),
+    "branch_signs_ignored_in_forward": ("s = np.sign(d) if signs is None else", "s = np.sign(d) if True else"),
+    "branch_signs_ignored_in_backward": ("s = np.sign(p - q) if signs is None else", "s = np.sign(p - q) if True else"),
     "ignored_rows_not_zeroed": ('valid = _valid_mask(target, V, ignore_index)\n    grad', 'valid = _valid_mask(target, V, ignore_index) | True\n    grad'),
 }
 
