@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import workloads as W
-from _parity import DEV, announce, check_forward, check_grad, grad_bits, grad_to_host, to_dev
+from _parity import DEV, G_REL, G_REL_P16, announce, check_forward, check_grad, grad_bits, grad_to_host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,7 @@ def test_binary16_logits(BT, V, teacher):
     g = torch.full_like(zs, SENTINEL)
     lx.lx_ce_tvd_backward(g, zs, us, tg, II, out["lse_s"], out.get("lse_t"), out.get("sigma"), 0.5, 1.5)
     torch.cuda.synchronize()
-    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, label + " backward")
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, label + " backward", fmt="f16")
     if teacher and BT > 4:
         assert o["tvd"][2] == 0.0 and o["sigma"][2] == 0.0, "identical rows must give exactly 0"
     if BT > 4:
@@ -99,7 +99,8 @@ def test_binary16_logits(BT, V, teacher):
     lx.lx_ce_tvd_forward_backward(zs, us, tg, II, out2["ce"], out2.get("tvd"), out2["lse_s"], out2.get("lse_t"),
                                   out2.get("sigma"), zs, 0.5, 1.5)
     check_forward(host(out2), z, u, t, II, label + " forward_backward")
-    check_grad(grad_to_host(zs), grad_bits(zs), z, u, t, II, 0.5, 1.5, label + " forward_backward in place")
+    check_grad(grad_to_host(zs), grad_bits(zs), z, u, t, II, 0.5, 1.5, label + " forward_backward in place",
+               rel=G_REL_P16, fmt="f16")
 
 
 def test_binary16_vocabulary_parallel():
@@ -134,7 +135,7 @@ def test_binary16_vocabulary_parallel():
         parts.append(g)
     g = torch.cat(parts, dim=1)
     torch.cuda.synchronize()
-    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, "f16 vocabulary-parallel backward")
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, "f16 vocabulary-parallel backward", fmt="f16")
 
 
 # ---------------------------------------------------------------- row strides
@@ -175,7 +176,7 @@ def test_strided_rows(BT, V, stride, dtype, teacher):
     lx.lx_ce_tvd_backward_ex(g, zs, us, tg, II, out["lse_s"], out.get("lse_t"), out.get("sigma"), 0.5, 1.5)
     torch.cuda.synchronize()
     gc = g.contiguous()
-    check_grad(grad_to_host(gc), grad_bits(gc), z, u, t, II, 0.5, 1.5, label + " backward_ex")
+    check_grad(grad_to_host(gc), grad_bits(gc), z, u, t, II, 0.5, 1.5, label + " backward_ex", fmt=dtype)
     assert np.all(pad_bits(gbig, V) == sent), f"{label}: backward_ex wrote into the padding"
     # one call, out of place, then in place into the student's own view
     gbig.fill_(SENTINEL)
@@ -184,13 +185,15 @@ def test_strided_rows(BT, V, stride, dtype, teacher):
                                      out2.get("sigma"), g, 0.5, 1.5)
     check_forward(host(out2), z, u, t, II, label + " forward_backward_ex")
     gc = g.contiguous()
-    check_grad(grad_to_host(gc), grad_bits(gc), z, u, t, II, 0.5, 1.5, label + " forward_backward_ex")
+    check_grad(grad_to_host(gc), grad_bits(gc), z, u, t, II, 0.5, 1.5, label + " forward_backward_ex",
+               rel=G_REL_P16, fmt=dtype)
     assert np.all(pad_bits(gbig, V) == sent), f"{label}: forward_backward_ex wrote into the padding"
     lx.lx_ce_tvd_forward_backward_ex(zs, us, tg, II, out2["ce"], out2.get("tvd"), out2["lse_s"], out2.get("lse_t"),
                                      out2.get("sigma"), zs, 0.5, 1.5)
     torch.cuda.synchronize()
     zc = zs.contiguous()
-    check_grad(grad_to_host(zc), grad_bits(zc), z, u, t, II, 0.5, 1.5, label + " forward_backward_ex in place")
+    check_grad(grad_to_host(zc), grad_bits(zc), z, u, t, II, 0.5, 1.5, label + " forward_backward_ex in place",
+               rel=G_REL_P16, fmt=dtype)
     assert np.all(pad_bits(zbig, V) == sent), f"{label}: in-place gradient wrote into the padding"
 
 
@@ -221,7 +224,8 @@ def test_strided_training_batch_sampled():
     sel = torch.from_numpy(rows).to(DEV)
     gsel = zs[sel].contiguous()
     check_forward({kk: v[rows] for kk, v in o.items()}, zr, ur, t[rows], II, "strided train")
-    check_grad(grad_to_host(gsel), grad_bits(gsel), zr, ur, t[rows], II, k, k, "strided train")
+    check_grad(grad_to_host(gsel), grad_bits(gsel), zr, ur, t[rows], II, k, k, "strided train", rel=G_REL_P16,
+               sigma_gpu=o["sigma"][rows])
     gs = zs.float()
     rs, ra = gs.sum(1).abs().cpu().numpy(), gs.abs().sum(1).cpu().numpy()
     del gs
@@ -273,7 +277,8 @@ def test_per_row_upstream_gradients(entry, teacher, dtype, BT, V):
     check_forward(host(out), z, u, t, II, label)
     eff_ce = k * g_ce * w_ce.astype(np.float64)
     eff_tvd = k * g_tvd * w_tvd.astype(np.float64)
-    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, eff_ce, eff_tvd, label)
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, eff_ce, eff_tvd, label,
+               rel=G_REL_P16 if entry == "forward_backward_ex" else G_REL, fmt=dtype)
     # rows whose factors are both 0 have an exactly zero gradient
     both0 = (w_ce == 0) & ((w_tvd == 0) | (u is None))
     assert np.all(grad_to_host(g)[both0] == 0.0)

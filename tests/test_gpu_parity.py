@@ -1,10 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
 
 Small cases compare every output element; they span several tiles, ragged
-tails, unaligned rows, both forward paths (one workgroup per row, and rows
-split across workgroups) and the degenerate cases.  Full-size workloads run
-in the launch configuration the benchmark times and compare sampled rows
-element by element, plus properties on every row.
+tails, unaligned rows, every forward path (one workgroup per row, rows split
+across workgroups, rows read once by cooperating workgroups) and the
+degenerate cases.  The full-size workloads are in test_gpu_fullsize.py.
 """
 from __future__ import annotations
 
@@ -27,6 +26,16 @@ import cross_entropy_tv_amd as lx  # noqa: E402
 
 II = W.IGNORE_INDEX
 SENTINEL = 12345.0
+
+
+def forward_path(BT, V, dtype, teacher):
+    """Which forward kernel a contiguous, 16-byte aligned (BT, V) case takes (the
+    planning rules of the library, read off its workspace queries)."""
+    dt = {"bf16": lx.LX_BF16, "f16": lx.LX_F16, "f32": lx.LX_F32}[dtype]
+    if lx.lx_ce_tvd_workspace_bytes(BT, V, dt, teacher) == 0:
+        return "row"
+    read_once = teacher and (V % (4 if dtype == "f32" else 8) == 0) and V >= (1024 if dtype == "f32" else 2048)
+    return "read-once" if read_once else "split-V"
 
 
 def fwd_outputs(BT, teacher=True):
@@ -97,16 +106,14 @@ def test_tiny_workload_end_to_end():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("teacher", [True, False], ids=["ce_tvd", "ce_only"])
 @pytest.mark.parametrize("BT,V", [(520, 4099), (515, 1031), (6, 50001), (3, 40000), (64, 8200)],
-                         ids=["rowpath_520x4099", "rowpath_515x1031", "split_6x50001", "split_3x40000",
-                              "split_64x8200"])
+                         ids=["520x4099", "515x1031", "6x50001", "3x40000", "64x8200"])
 def test_ragged_shapes(BT, V, dtype, teacher):
     ign = [1, BT - 1] if BT > 4 else [1]
     ident = [2] if BT > 4 else []
     unif = [3] if BT > 4 else []
     z, u, t = W.custom(BT, V, dtype, seed=BT * 7 + V, scale=3.0, teacher_noise=0.5, ignore_rows=ign,
                        identical_rows=ident, uniform_rows=unif)
-    split = lx.lx_ce_tvd_workspace_bytes(BT, V, lx.LX_BF16 if dtype == "bf16" else lx.LX_F32, teacher) > 0
-    label = f"{'split' if split else 'row'} {BT}x{V} {dtype} {'ce_tvd' if teacher else 'ce_only'}"
+    label = f"{forward_path(BT, V, dtype, teacher)} {BT}x{V} {dtype} {'ce_tvd' if teacher else 'ce_only'}"
     out, g = full_case(label, z, u if teacher else None, t)
     if teacher and ident:
         o = host(out)
@@ -319,77 +326,3 @@ def test_deterministic_bitwise():
             for k in o:
                 assert np.array_equal(bits32(o[k]), bits32(runs[0][0][k])), k
             assert torch.equal(gb, runs[0][1])
-
-
-# ---------------------------------------------------------------- full-size workloads, as benchmarked
-
-def _sample_rows(w, n=48, seed=0):
-    rng = np.random.default_rng(1234 + seed)
-    rows = set(rng.choice(w.BT, size=min(n, w.BT), replace=False).tolist()) | {0, w.BT - 1}
-    ro = W.roles(w)
-    for role in (W.ROLE_IGNORED, W.ROLE_IDENTICAL, W.ROLE_UNIFORM):
-        idx = np.nonzero(ro == role)[0]
-        rows |= set(idx[:4].tolist())
-    return np.array(sorted(rows))
-
-
-@pytest.mark.parametrize("name,teacher", [("pr", True), ("train", True), ("train", False), ("ties", True),
-                                          ("hugev", True), ("hugev", False)])
-def test_full_workload_sampled_rows(name, teacher):
-    w = W.get(name)
-    announce(f"workload {name} {w.BT}x{w.V} {w.dtype} teacher={teacher}: generating inputs")
-    z, u, t = W.full(w)
-    zs, tg = to_dev(z), to_dev(t)
-    us = to_dev(u) if teacher else None
-    if not teacher:
-        del u
-    announce(f"workload {name}: forward + mean + backward (in place for pr)")
-    out = run_fwd(zs, us, tg)
-    mean = torch.zeros(2, device=DEV)
-    inv = torch.zeros(1, device=DEV)
-    lx.lx_ce_tvd_reduce_mean(out["ce"], out.get("tvd"), tg, II, mean, None, inv)
-    in_place = name == "pr"
-    grad = zs if in_place else torch.empty_like(zs)
-    o = host(out)
-    # properties on every row
-    ro = W.roles(w)
-    valid = t != II
-    assert np.all(bits32(o["ce"][~valid]) == 0)
-    assert np.all(o["ce"][valid] >= -1e-5)
-    vmax = zs.float().amax(1).cpu().numpy()
-    assert np.all(o["lse_s"][valid] >= vmax[valid] - 1e-4)
-    assert np.all(o["lse_s"][valid] <= vmax[valid] + math.log(w.V) + 1e-4)
-    if teacher:
-        assert np.all((o["tvd"] >= 0) & (o["tvd"] <= 1 + 1e-6)) and np.all(np.abs(o["sigma"]) <= 1 + 1e-5)
-        ident = ro == W.ROLE_IDENTICAL
-        assert np.all(o["tvd"][ident] == 0.0) and np.all(o["sigma"][ident] == 0.0)
-    unif = ro == W.ROLE_UNIFORM
-    assert np.all(np.abs(o["ce"][unif] - math.log(w.V)) <= 1e-4)
-    # the mean is the float64 mean of the device's own per-row values (a property of
-    # the reduction, not an oracle comparison; the oracle checks it on the tiny workload)
-    m = mean.cpu().numpy()
-    assert abs(m[0] - o["ce"][valid].astype(np.float64).mean()) <= 1e-6 * max(1.0, abs(m[0]))
-    if teacher:
-        assert abs(m[1] - o["tvd"][valid].astype(np.float64).mean()) <= 1e-7
-    rows = _sample_rows(w)
-    keep = {k: v[rows] for k, v in o.items()}
-    # backward with the device-side 1/n_valid
-    run_bwd(out, zs, us, tg, 1.0, 1.0, grad=grad, g_scale=inv)
-    torch.cuda.synchronize()
-    n_valid = int(valid.sum())
-    assert abs(inv.item() - 1.0 / n_valid) <= 1e-7 / n_valid
-    sel = torch.from_numpy(rows).to(DEV)
-    gb = grad_bits(grad[sel])
-    gh = grad_to_host(grad[sel])
-    # every row sums to zero, up to the bf16 rounding of each element
-    gs = grad.float()
-    rs = gs.sum(1).abs().cpu().numpy()
-    ra = gs.abs().sum(1).cpu().numpy()
-    del gs
-    assert np.all(rs <= 2.0 ** -8 * ra + w.V * 1e-6 / n_valid + 1e-9)
-    if (~valid).any():
-        assert np.all(grad_bits(grad[torch.from_numpy(np.nonzero(~valid)[0]).to(DEV)]) == 0)
-    announce(f"workload {name}: oracle on {len(rows)} sampled rows")
-    zr, ur = W.rows(w, rows)
-    check_forward(keep, zr, ur if teacher else None, t[rows], II, f"{name} sampled")
-    check_grad(gh, gb, zr, ur if teacher else None, t[rows], II, 1.0 / n_valid, 1.0 / n_valid, f"{name} sampled")
