@@ -21,6 +21,7 @@ LX_ERR_UNSUPPORTED_DTYPE = 2
 LX_ERR_ALIAS = 3
 LX_ERR_WORKSPACE = 4
 LX_ERR_HIP = 5
+LX_ERR_TOO_LARGE = 6
 LX_F32 = 0
 LX_BF16 = 1
 LX_F16 = 2
@@ -65,6 +66,8 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_forward_backward_workspace_bytes.restype = sz
     L.lx_ce_tvd_forward_backward.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p, p, f32, f32, p, i32, p, sz, p]
     L.lx_ce_tvd_forward_backward.restype = i32
+    L.lx_ce_tvd_forward_backward_noalloc.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p, p, f32, f32, p, i32, p]
+    L.lx_ce_tvd_forward_backward_noalloc.restype = i32
     L.lx_ce_tvd_count_valid.argtypes = [p, i64, i64, p, p, p]
     L.lx_ce_tvd_count_valid.restype = i32
     L.lx_ce_tvd_vp_stats.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, p]
@@ -212,6 +215,23 @@ def lx_ce_tvd_forward_backward(student, teacher, target, ignore_index, ce, tvd, 
                                           _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t), _ptr(sigma), _ptr(grad),
                                           float(g_ce), float(g_tvd), _ptr(g_scale), dt, _ptr(workspace), wbytes,
                                           _stream(stream)), "lx_ce_tvd_forward_backward")
+
+
+def lx_ce_tvd_forward_backward_noalloc(student, teacher, target, ignore_index, ce, tvd, lse_s, lse_t, sigma, grad,
+                                       g_ce: float, g_tvd: float, g_scale=None, stream=None) -> None:
+    """lx_ce_tvd_forward_backward with its scratch memory in the library's static
+    device buffer instead of a workspace (nothing is allocated; calls that
+    overlap on one device race)."""
+    BT, V = _logits2d(student, "student")
+    dt = _dtype_code(student)
+    if teacher is not None and (teacher.shape != student.shape or teacher.dtype != student.dtype):
+        raise ValueError("teacher must match student in shape and dtype")
+    if grad.shape != student.shape or grad.dtype != student.dtype or not grad.is_contiguous():
+        raise ValueError("grad must match student in shape and dtype and be contiguous")
+    _check(lib.lx_ce_tvd_forward_backward_noalloc(_ptr(student), _ptr(teacher), _ptr(target), BT, V,
+                                                  int(ignore_index), _ptr(ce), _ptr(tvd), _ptr(lse_s), _ptr(lse_t),
+                                                  _ptr(sigma), _ptr(grad), float(g_ce), float(g_tvd), _ptr(g_scale),
+                                                  dt, _stream(stream)), "lx_ce_tvd_forward_backward_noalloc")
 
 
 def lx_ce_tvd_count_valid(target, ignore_index, n_valid=None, inv_n_valid=None, stream=None) -> None:

@@ -198,7 +198,8 @@ lx_status forward_backward_impl(Tensor zs, Tensor us, const int64_t* target, int
                                 int64_t ignore_index, float* ce, float* tvd, float* lse_s, float* lse_t,
                                 float* sigma, void* grad, int64_t ldg, float g_ce, float g_tvd,
                                 const float* gce_rows, const float* gtvd_rows, const float* g_scale, lx_dtype dt,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                lx::ScratchProvider scratch = nullptr) {
   const int es = esize_of(dt);
   if (!es) return LX_ERR_UNSUPPORTED_DTYPE;
   if (lx_status s = check_shape(BT, V, es)) return s;
@@ -235,6 +236,10 @@ lx_status forward_backward_impl(Tensor zs, Tensor us, const int64_t* target, int
   if (!in_place && overlaps(g, sp[0])) return LX_ERR_ALIAS;
   for (int i = 1; i < 12; ++i)
     if (overlaps(g, sp[i])) return LX_ERR_ALIAS;
+  if (need && scratch) {
+    // the library's own scratch (after validation: nothing is looked up for a rejected call)
+    if (lx_status s = scratch(need, &workspace, &workspace_bytes)) return s;
+  }
   if (need) {
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LX_ERR_WORKSPACE;
   }
@@ -291,6 +296,19 @@ lx_status forward_backward_impl(Tensor zs, Tensor us, const int64_t* target, int
 
 }  // namespace
 
+namespace lx {
+void record_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
+
+lx_status forward_backward_scratch(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                                   int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s,
+                                   float* lse_t, float* sigma, void* grad, float g_ce, float g_tvd,
+                                   const float* g_scale, lx_dtype dt, void* stream, ScratchProvider scratch) {
+  return forward_backward_impl(Tensor{student, V}, Tensor{teacher, V}, target, BT, V, ignore_index, ce, tvd, lse_s,
+                               lse_t, sigma, grad, V, g_ce, g_tvd, nullptr, nullptr, g_scale, dt, nullptr, 0,
+                               stream, scratch);
+}
+}  // namespace lx
+
 extern "C" {
 
 const char* lx_status_string(lx_status s) {
@@ -301,6 +319,7 @@ const char* lx_status_string(lx_status s) {
     case LX_ERR_ALIAS: return "LX_ERR_ALIAS";
     case LX_ERR_WORKSPACE: return "LX_ERR_WORKSPACE";
     case LX_ERR_HIP: return "LX_ERR_HIP";
+    case LX_ERR_TOO_LARGE: return "LX_ERR_TOO_LARGE";
   }
   return "LX_ERR_UNKNOWN";
 }

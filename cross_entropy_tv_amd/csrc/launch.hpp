@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "lx_ce_tvd.h"
+
 namespace lx {
 
 // How the forward is run for a shape.
@@ -112,6 +114,19 @@ hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* t
                                  hipStream_t stream);
 hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,
                               float* tvd, float* sigma, hipStream_t stream);
+
+// Records e as the calling thread's last HIP error (lx_last_hip_error).
+void record_hip_error(hipError_t e);
+
+// Supplies `need` bytes of scratch memory of the library's own (*ws, with its
+// size in *bytes), or an error status.
+typedef lx_status (*ScratchProvider)(size_t need, void** ws, size_t* bytes);
+// lx_ce_tvd_forward_backward with the scratch memory from `scratch`, asked for
+// after the arguments are validated.
+lx_status forward_backward_scratch(const void* student, const void* teacher, const int64_t* target, int64_t BT,
+                                   int64_t V, int64_t ignore_index, float* ce, float* tvd, float* lse_s,
+                                   float* lse_t, float* sigma, void* grad, float g_ce, float g_tvd,
+                                   const float* g_scale, lx_dtype dt, void* stream, ScratchProvider scratch);
 
 hipError_t launch_reduce_mean(const float* ce, const float* tvd, const int64_t* target, int64_t BT,
                               int64_t ignore_index, float* mean_out, int64_t* n_valid, float* inv_n_valid,

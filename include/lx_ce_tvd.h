@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 5
+#define LX_CE_TVD_ABI_VERSION 6
 
 typedef enum lx_status {
   LX_OK = 0,
@@ -74,7 +74,9 @@ typedef enum lx_status {
   LX_ERR_UNSUPPORTED_DTYPE = 2, /* dt is not LX_F32, LX_BF16 or LX_F16 */
   LX_ERR_ALIAS = 3,             /* an output overlaps an input or another output */
   LX_ERR_WORKSPACE = 4,         /* workspace NULL or smaller than required */
-  LX_ERR_HIP = 5                /* the HIP runtime rejected a launch */
+  LX_ERR_HIP = 5,               /* the HIP runtime rejected a launch or a symbol lookup */
+  LX_ERR_TOO_LARGE = 6          /* the shape needs more scratch than the static buffer of
+                                   lx_ce_tvd_forward_backward_noalloc holds */
 } lx_status;
 
 typedef enum lx_dtype {
@@ -183,6 +185,30 @@ lx_status lx_ce_tvd_forward_backward(const void* student, const void* teacher, c
                                      float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
                                      void* grad, float g_ce, float g_tvd, const float* g_scale,
                                      lx_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of lx_ce_tvd_forward_backward, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * results and errors as lx_ce_tvd_forward_backward without the workspace: the
+ * scratch memory lives in a static device array of the library,
+ * LX_NOALLOC_SCRATCH_BYTES per device, held by each device the library runs on
+ * until the process ends.  Its device address is looked up once per device, on
+ * the first call with that device current (the stream's device), so the first
+ * call can return LX_ERR_HIP if the lookup fails.  The call allocates nothing.
+ * Shapes whose scratch (lx_ce_tvd_forward_backward_workspace_bytes) exceeds
+ * LX_NOALLOC_SCRATCH_BYTES return LX_ERR_TOO_LARGE (e.g. more than about 80000
+ * rows of 151936 bf16 logits with a teacher) and enqueue nothing.  Every call on
+ * a device shares that device's array (each call re-initialises what it needs),
+ * so calls that overlap on one device, on different streams or from different
+ * host threads, race: serialise them.
+ */
+#define LX_NOALLOC_SCRATCH_BYTES (8u << 20)
+lx_status lx_ce_tvd_forward_backward_noalloc(const void* student, const void* teacher, const int64_t* target,
+                                             int64_t BT, int64_t V, int64_t ignore_index,
+                                             float* ce, float* tvd, float* lse_s, float* lse_t, float* sigma,
+                                             void* grad, float g_ce, float g_tvd, const float* g_scale,
+                                             lx_dtype dt, void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -32,9 +32,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 5
+    assert lx.lx_abi_version() == 6
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
-                       (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP")):
+                       (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP"), (6, "LX_ERR_TOO_LARGE")):
         assert lx.lx_status_string(code) == name
 
 
@@ -130,6 +130,29 @@ def test_forward_backward_validation():
     assert fwdbwd(**big, ws=A * 16, wsb=need - 256) == lx.LX_ERR_WORKSPACE
     assert fwdbwd(**big, ws=A * 16 + 64, wsb=need) == lx.LX_ERR_WORKSPACE   # 256-B alignment
     assert fwdbwd(**big, ws=A * 12, wsb=need) == lx.LX_ERR_ALIAS          # workspace inside the gradient
+
+
+def noalloc(student=A, teacher=A + (1 << 31), target=A * 3, BT=4, V=100, ce=A * 4, tvd=A * 4 + 64,
+            lse_s=A * 4 + 128, lse_t=A * 4 + 192, sigma=A * 4 + 256, grad=A * 5, g_scale=None, dt=1):
+    return L.lx_ce_tvd_forward_backward_noalloc(student, teacher, target, BT, V, -100, ce, tvd, lse_s, lse_t, sigma,
+                                                grad, 1.0, 1.0, g_scale, dt, None)
+
+
+def test_noalloc_validation():
+    """The allocation-free entry point validates like lx_ce_tvd_forward_backward
+    before it looks anything up, and rejects shapes beyond its static scratch."""
+    assert noalloc(BT=0) == lx.LX_OK
+    assert noalloc(dt=5) == lx.LX_ERR_UNSUPPORTED_DTYPE
+    assert noalloc(grad=None) == lx.LX_ERR_INVALID_ARG
+    assert noalloc(sigma=None) == lx.LX_ERR_INVALID_ARG
+    assert noalloc(grad=A + 2) == lx.LX_ERR_ALIAS
+    assert noalloc(ce=A * 5 + 8) == lx.LX_ERR_ALIAS
+    limit = 8 << 20
+    BT = 100000
+    assert lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, 151936, 1, 1) > limit
+    big = dict(BT=BT, V=151936, student=A * 100, teacher=A * 200, target=A * 3, ce=A * 4, tvd=A * 4 + (1 << 20),
+               lse_s=A * 4 + (2 << 20), lse_t=A * 4 + (3 << 20), sigma=A * 4 + (4 << 20), grad=A * 300)
+    assert noalloc(**big) == lx.LX_ERR_TOO_LARGE
 
 
 def test_count_valid_validation():
