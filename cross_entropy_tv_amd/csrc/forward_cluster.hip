@@ -63,6 +63,17 @@ __device__ __forceinline__ u32x4_t ld_stream(__amdgpu_buffer_rsrc_t rs, int byte
 __device__ __forceinline__ void st_stream(__amdgpu_buffer_rsrc_t rs, int byte_off, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, byte_off, 0, kStreamPolicy);
 }
+// Buffer resource of column i of a chunk of `bytes` bytes, for a workgroup of
+// NT threads whose thread tid owns the 16-byte units tid + i * NT: the chunk
+// from byte i * NT * 16 on.  Every column is then addressed with the same
+// per-thread offset tid * 16, and the column's own offset lives in the
+// resource (scalar registers) instead of costing vector instructions per
+// group; the resource's size keeps the range check exact for a ragged chunk.
+template <int NT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t col_rsrc(const void* chunk, int bytes, int i) {
+  const int off = i * NT * 16;
+  return chunk_rsrc(static_cast<const char*>(chunk) + off, bytes > off ? bytes - off : 0);
+}
 
 // Two logits packed in a 32-bit word, widened to f32: T = uint16_t holds
 // bf16, T = _Float16 binary16.
@@ -244,6 +255,17 @@ __device__ __forceinline__ u32x4_t grad8(const u32x4_t& wp, const u32x4_t& ws, f
   }
   return pack8<T>(o);
 }
+// As grad8 for a group that does not hold the target element.
+template <typename T>
+__device__ __forceinline__ u32x4_t grad8_plain(const u32x4_t& wp, const u32x4_t& ws, float a1, float b1,
+                                              float zero) {
+  float p[8], sg[8], o[8];
+  unpack8_f16(wp, p);
+  unpack8_f16(ws, sg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(p[e], __builtin_fmaf(sg[e], b1, a1), zero);
+  return pack8<T>(o);
+}
 
 // true when one of the eight fp16 values of w exceeds thr
 __device__ __forceinline__ bool any_above(const u32x4_t& w, _Float16 thr) {
@@ -360,9 +382,10 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
       ce[r] = 0.f; tvd[r] = 0.f; lse_s_out[r] = 0.f; lse_t_out[r] = 0.f; sigma_out[r] = 0.f;
     }
     if (FUSED) {
-      const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
 #pragma unroll
-      for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
+      for (int i = 0; i < G + GL; ++i)
+        st_stream(col_rsrc<NT>(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16, i), tid * 16,
+                  (u32x4_t){0u, 0u, 0u, 0u});
     }
     return;
   }
@@ -377,13 +400,13 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   float zt = 0.f;
   if (FUSED && j == jt && tid == 0 && t_ok) zt = load1(student + rowz + t);
 
-  const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + rowz + 8 * (int64_t)gb, (ge - gb) * 16);
-  const __amdgpu_buffer_rsrc_t rsu = chunk_rsrc(teacher + rowu + 8 * (int64_t)gb, (ge - gb) * 16);
+  const T* zc = student + rowz + 8 * (int64_t)gb;  // this member's chunk of the student row
+  const int cbytes = cnt * 16;
   u32x4_t rz[G], ru[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
-    ru[i] = ld_stream(rsu, (tid + i * NT) * 16);
+    rz[i] = ld_stream(col_rsrc<NT>(zc, cbytes, i), tid * 16);
+    ru[i] = ld_stream(col_rsrc<NT>(teacher + rowu + 8 * (int64_t)gb, cbytes, i), tid * 16);
   }
   if (GL > 0 && cnt > NT * G) {
     // the rest of the chunk goes straight to LDS, 64 groups (1 KB) per load
@@ -611,13 +634,17 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
   const float beta = 0.5f * k * gtvd;
   const float alpha = kce - beta * s_bc[2];
   const float a1 = alpha * kInvPqBias, b1 = beta * kTvScale;
-  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
+  T* gc = grad + rowg + 8 * (int64_t)gb;  // this member's chunk of the gradient row
   // target element relative to the chunk; only the member holding it reads pt
   const int trel = j == jt ? (int)(t - 8 * (int64_t)gb) : -1;
+  // the column (group index / NT) and thread of the target's group, uniform
+  // across the workgroup, so the per-group test is a scalar comparison
+  const int tcol = trel >= 0 ? (trel >> 3) / NT : -1;
+  const int tthr = trel >= 0 ? (trel >> 3) % NT : -1;
   if (!t_ok) {
     // a target outside [0, V) makes the row's gradient NaN
 #pragma unroll
-    for (int i = 0; i < G + GL; ++i) st_stream(rsg, (tid + i * NT) * 16, nan8<T>());
+    for (int i = 0; i < G + GL; ++i) st_stream(col_rsrc<NT>(gc, cbytes, i), tid * 16, nan8<T>());
     return;
   }
   const float pt = exp2_hw(exparg(s_zt, nbs));
@@ -637,30 +664,35 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
       launder(rz[i]);
       launder(ru[i]);
       const u32x4_t o = any_above(rz[i], thr)
-                            ? grad8_exact<T>(ld_stream(rsz, g * 16), ru[i], nbs, trel - 8 * g, a1, b1, kce)
+                            ? grad8_exact<T>(ld_stream(col_rsrc<NT>(zc, cbytes, i), tid * 16), ru[i], nbs,
+                                             trel - 8 * g, a1, b1, kce)
                             : grad8<T>(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce);
-      st_stream(rsg, g * 16, o);
+      st_stream(col_rsrc<NT>(gc, cbytes, i), tid * 16, o);
     }
 #pragma unroll
     for (int i = 0; i < GL; ++i) {
       const int g = NT * G + tid + i * NT;
       const u32x4_t wp = lz[tid + i * NT], ws = lu[tid + i * NT];
       const u32x4_t o = any_above(wp, thr)
-                            ? grad8_exact<T>(ld_stream(rsz, g * 16), ws, nbs, trel - 8 * g, a1, b1, kce)
+                            ? grad8_exact<T>(ld_stream(col_rsrc<NT>(zc, cbytes, G + i), tid * 16), ws, nbs,
+                                             trel - 8 * g, a1, b1, kce)
                             : grad8<T>(wp, ws, a1, b1, zero, trel - 8 * g, pt, kce);
-      st_stream(rsg, g * 16, o);
+      st_stream(col_rsrc<NT>(gc, cbytes, G + i), tid * 16, o);
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = tid + i * NT;
-    st_stream(rsg, g * 16, grad8<T>(rz[i], ru[i], a1, b1, zero, trel - 8 * g, pt, kce));
+    const u32x4_t o = i == tcol ? grad8<T>(rz[i], ru[i], a1, b1, zero, tid == tthr ? (trel & 7) : -1, pt, kce)
+                                : grad8_plain<T>(rz[i], ru[i], a1, b1, zero);
+    st_stream(col_rsrc<NT>(gc, cbytes, i), tid * 16, o);
   }
 #pragma unroll
   for (int i = 0; i < GL; ++i) {
-    const int g = NT * G + tid + i * NT;
-    st_stream(rsg, g * 16, grad8<T>(lz[tid + i * NT], lu[tid + i * NT], a1, b1, zero, trel - 8 * g, pt, kce));
+    const u32x4_t wp = lz[tid + i * NT], ws = lu[tid + i * NT];
+    const u32x4_t o = G + i == tcol ? grad8<T>(wp, ws, a1, b1, zero, tid == tthr ? (trel & 7) : -1, pt, kce)
+                                    : grad8_plain<T>(wp, ws, a1, b1, zero);
+    st_stream(col_rsrc<NT>(gc, cbytes, G + i), tid * 16, o);
   }
 }
 
@@ -1127,14 +1159,15 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   const bool t_ok = t >= 0 && t < V;
   // the row's upstream gradient, read now so that the load is long done after the exchange
   const float kce = (g_scale ? *g_scale : 1.0f) * g_ce * (gce_rows ? gce_rows[r] : 1.0f);
-  const __amdgpu_buffer_rsrc_t rsg = chunk_rsrc(grad + rowg + 8 * (int64_t)gb, (ge - gb) * 16);
+  T* gc = grad + rowg + 8 * (int64_t)gb;  // this member's chunk of the gradient row
+  const int cbytes = (ge - gb) * 16;
   if (t == ignore_index) {
     if (j == 0 && tid == 0) {
       ce[r] = 0.f;
       lse_s_out[r] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) st_stream(rsg, (tid + i * NT) * 16, (u32x4_t){0u, 0u, 0u, 0u});
+    for (int i = 0; i < G; ++i) st_stream(col_rsrc<NT>(gc, cbytes, i), tid * 16, (u32x4_t){0u, 0u, 0u, 0u});
     return;
   }
   const int n = gb + tid < ge ? (ge - gb - tid - 1) / NT + 1 : 0;
@@ -1145,10 +1178,9 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   float ez[G][8];
   float mz = kMFloor;
   {
-    const __amdgpu_buffer_rsrc_t rsz = chunk_rsrc(student + rowz + 8 * (int64_t)gb, (ge - gb) * 16);
     u32x4_t rz[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i) rz[i] = ld_stream(rsz, (tid + i * NT) * 16);
+    for (int i = 0; i < G; ++i) rz[i] = ld_stream(col_rsrc<NT>(student + rowz + 8 * (int64_t)gb, cbytes, i), tid * 16);
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -1207,18 +1239,20 @@ void fused_ce_kernel(const T* student, const int64_t* __restrict__ target, int V
   // ---- g = k * g_ce * (p - [v == t])
   const float alpha = kce * cz;
   const int trel = t_ok ? (int)(t - 8 * (int64_t)gb) : -1;  // target element relative to the chunk
+  // the column and thread of the target's group (uniform: a scalar test per group)
+  const int tcol = trel >= 0 && trel < cbytes / 2 ? (trel >> 3) / NT : -1;
+  const int tthr = trel >= 0 ? (trel >> 3) % NT : -1;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const int g = tid + i * NT;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = ez[i][e] * alpha;
-    const int rel = trel - 8 * g;
-    if ((unsigned)rel < 8u) {
+    if (i == tcol && tid == tthr) {
+      const int rel = trel & 7;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (e == rel) ? o[e] - kce : o[e];
     }
-    st_stream(rsg, g * 16, t_ok ? pack8<T>(o) : nan8<T>());
+    st_stream(col_rsrc<NT>(gc, cbytes, i), tid * 16, t_ok ? pack8<T>(o) : nan8<T>());
   }
 }
 
