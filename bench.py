@@ -7,20 +7,29 @@ logits.  Two paths compute that step and both are timed:
   fused    : count valid rows (1/n_valid on the device) -> one forward+backward
              pass over the logits -> mean (the headline when a teacher is given);
   separate : forward -> mean (and 1/n_valid) -> backward.
-The default workload is the training batch: 8192 rows x 151936 classes, bf16
+The headline workload is the training batch: 8192 rows x 151936 classes, bf16
 logits, LM-like synthetic logits (N(0, 1.5^2) plus 32 N(8, 2^2) spikes per row,
-independent teacher).  Prints one JSON line.
+independent teacher).  The other workloads (pr: 1024 rows, the PR page's own
+shape; ties: 16384 rows with identical / uniform / ignored rows; hugev: 64 x
+262144) and CE-only mode get lines of their own under "configs".
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train]
-                    [--mode ce_tvd|ce] [--no-cpu-baseline] [--no-ce-only]
+Timing: every timed rep is preceded, outside the timed region, by a 1 GiB
+write that flushes the L2 caches and the Infinity Cache, and is bracketed by
+HIP events on the stream the kernels run on; ms_per_step is the mean over the
+timed reps.  The practical ceilings are the library's own reference streams
+(read-only, and two reads + one write), measured the same way.  Prints one
+JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+                    [--no-linear] [--no-vocab-parallel] [--no-ex]
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
+import platform
 import sys
 import time
 
@@ -30,8 +39,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "fwd+bwd tokens/s and achieved HBM GB/s (% of peak), BT=8192 V=151936 bf16"
+FLUSH_BYTES = 1 << 30
 # sources of the kernels whose HBM counters are committed (profiles/pmc_traffic.json)
 KERNEL_SOURCES = ["common.hpp", "ids.hpp", "launch.hpp", "forward.hip", "forward_cluster.hip", "backward.hip"]
+II = -100
 
 
 def kernel_source_hash() -> str:
@@ -42,17 +53,68 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# ---------------------------------------------------------------- timing
+
+class Timer:
+    """Per-rep HIP-event timing of a sequence of calls, with a cache flush before
+    every rep (outside the timed region)."""
+
+    def __init__(self, dev):
+        import torch
+        self.torch = torch
+        self.flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def flush(self):
+        self.flush_buf.add_(1)
+
+    def run(self, calls, steps, warmup):
+        """calls: list of zero-argument callables forming one step.  Returns
+        (mean ms of each call, mean ms of the step, wall seconds of the timed loop)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            self.flush()
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.flush()
+            for i, c in enumerate(calls):
+                evs[k][i].record(stream)
+                c()
+            evs[k][-1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(len(calls))]
+        step = sum(e[0].elapsed_time(e[-1]) for e in evs) / steps
+        return per, step, wall
+
+
+def roofline(alg_bytes, ms, kernel):
+    gbs = alg_bytes / ms / 1e6
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": kernel, "alg_bytes_per_launch": int(alg_bytes),
+            "avg_launch_ms": round(ms, 4)}
+
+
 def algorithmic_bytes(BT, V, es, n_valid, teacher):
-    """Unique bytes each kernel must move (see the design notes, 'algorithmic bytes')."""
+    """Unique bytes each kernel must move: logits read once per pass that needs
+    them, the gradient written once, plus the per-row state (see the design notes)."""
     n_ign = BT - n_valid
     streams = 2 if teacher else 1
     fwd = n_valid * streams * V * es + BT * 8 + BT * 4 * (5 if teacher else 2)
     bwd = n_valid * (streams + 1) * V * es + n_ign * V * es + BT * 8 + BT * 4 * (3 if teacher else 1) + 4
     red = BT * (4 * (2 if teacher else 1) + 8) + 16
-    return {"forward": fwd, "reduce": red, "backward": bwd}
+    fused = n_valid * (streams + 1) * V * es + n_ign * V * es + BT * 8 + BT * 4 * (5 if teacher else 2) + 4
+    return {"forward": fwd, "reduce": red, "backward": bwd, "forward_backward": fused}
 
 
-def run_mode(w, zs, us, tg, n_valid, steps, warmup, teacher):
+# ---------------------------------------------------------------- the two paths
+
+def measure(timer, w, zs, us, tg, n_valid, steps, warmup, teacher):
+    """Both paths on one device-resident batch; returns their timings and rooflines."""
     import torch
     import cross_entropy_tv_amd as lx
 
@@ -61,110 +123,44 @@ def run_mode(w, zs, us, tg, n_valid, steps, warmup, teacher):
     f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
     ce, lse_s = f(), f()
     tvd, lse_t, sigma = (f(), f(), f()) if teacher else (None, None, None)
+    u = us if teacher else None
     mean = torch.empty(2, dtype=torch.float32, device=dev)
     inv = torch.empty(1, dtype=torch.float32, device=dev)
     grad = torch.empty_like(zs)
     dt = lx.LX_BF16 if w.dtype == "bf16" else lx.LX_F32
-    nws = lx.lx_ce_tvd_workspace_bytes(BT, V, dt, teacher)
+    nws = max(lx.lx_ce_tvd_workspace_bytes(BT, V, dt, teacher),
+              lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    u = us if teacher else None
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        lx.lx_ce_tvd_forward(zs, u, tg, -100, ce, tvd, lse_s, lse_t, sigma, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        lx.lx_ce_tvd_reduce_mean(ce, tvd, tg, -100, mean, None, inv, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        lx.lx_ce_tvd_backward(grad, zs, u, tg, -100, lse_s, lse_t, sigma, 1.0, 1.0, inv, stream)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    red_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    s = torch.cuda.current_stream()
     ab = algorithmic_bytes(BT, V, w.esize, n_valid, teacher)
-    res = {
-        "ms_per_step": wall * 1e3 / steps,
-        "tokens_per_s": BT * steps / wall,
-        "forward_ms": fwd_ms, "reduce_ms": red_ms, "backward_ms": bwd_ms,
-        "forward_GBs": ab["forward"] / fwd_ms / 1e6, "backward_GBs": ab["backward"] / bwd_ms / 1e6,
-        "alg_bytes": ab,
-        "mean": mean.cpu().tolist(),
+
+    sep_calls = [lambda: lx.lx_ce_tvd_forward(zs, u, tg, II, ce, tvd, lse_s, lse_t, sigma, ws, s),
+                 lambda: lx.lx_ce_tvd_reduce_mean(ce, tvd, tg, II, mean, None, inv, s),
+                 lambda: lx.lx_ce_tvd_backward(grad, zs, u, tg, II, lse_s, lse_t, sigma, 1.0, 1.0, inv, s)]
+    (fwd_ms, red_ms, bwd_ms), sep_ms, _ = timer.run(sep_calls, steps, warmup)
+    sep_mean = mean.cpu().tolist()
+    one_calls = [lambda: lx.lx_ce_tvd_count_valid(tg, II, None, inv, s),
+                 lambda: lx.lx_ce_tvd_forward_backward(zs, u, tg, II, ce, tvd, lse_s, lse_t, sigma, grad, 1.0, 1.0,
+                                                       inv, ws, s),
+                 lambda: lx.lx_ce_tvd_reduce_mean(ce, tvd, tg, II, mean, None, None, s)]
+    (cnt_ms, fb_ms, red2_ms), one_ms, wall = timer.run(one_calls, steps, warmup)
+    del grad, ws
+    r = lambda x: round(x, 4)  # noqa: E731
+    return {
+        "workload": f"{w.name} {BT}x{V} {w.dtype}", "mode": "ce_tvd" if teacher else "ce_only",
+        "n_valid_rows": n_valid,
+        "one_pass": {"ms_per_step": r(one_ms), "tokens_per_s": round(BT / one_ms * 1e3, 1), "count_ms": r(cnt_ms),
+                     "forward_backward_ms": r(fb_ms), "reduce_ms": r(red2_ms),
+                     "roofline": roofline(ab["forward_backward"], fb_ms, "forward_backward"),
+                     "mean": mean.cpu().tolist(), "wall_s_timed_loop": round(wall, 4)},
+        "separate": {"ms_per_step": r(sep_ms), "tokens_per_s": round(BT / sep_ms * 1e3, 1), "forward_ms": r(fwd_ms),
+                     "reduce_ms": r(red_ms), "backward_ms": r(bwd_ms),
+                     "forward_roofline": roofline(ab["forward"], fwd_ms, "forward"),
+                     "backward_roofline": roofline(ab["backward"], bwd_ms, "backward"), "mean": sep_mean},
     }
-    res["forward_pct_peak"] = 100.0 * res["forward_GBs"] / HBM_PEAK_GBS
-    res["backward_pct_peak"] = 100.0 * res["backward_GBs"] / HBM_PEAK_GBS
-    return res
 
 
-def run_fused(w, zs, us, tg, n_valid, steps, warmup, teacher=True):
-    """One step = count the valid rows (1/n_valid on the device) -> one fused forward +
-    backward pass -> mean of the per-row losses."""
-    import torch
-    import cross_entropy_tv_amd as lx
-
-    BT, V = w.BT, w.V
-    dev = zs.device
-    f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
-    ce, lse_s = f(), f()
-    tvd, lse_t, sigma = (f(), f(), f()) if teacher else (None, None, None)
-    u = us if teacher else None
-    mean = torch.empty(2, dtype=torch.float32, device=dev)
-    inv = torch.empty(1, dtype=torch.float32, device=dev)
-    grad = torch.empty_like(zs)
-    dt = lx.LX_BF16 if w.dtype == "bf16" else lx.LX_F32
-    nws = lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, dt, teacher)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        lx.lx_ce_tvd_forward_backward(zs, u, tg, -100, ce, tvd, lse_s, lse_t, sigma, grad, 1.0, 1.0, inv, ws,
-                                      stream)
-        if ev is not None:
-            ev[2].record(stream)
-        lx.lx_ce_tvd_reduce_mean(ce, tvd, tg, -100, mean, None, None, stream)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    cnt_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    fb_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    red_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
-    n_ign = BT - n_valid
-    streams = 2 if teacher else 1
-    alg = n_valid * (streams + 1) * V * w.esize + n_ign * V * w.esize + BT * 8 + BT * 4 * (5 if teacher else 2) + 4
-    return {"ms_per_step": wall * 1e3 / steps, "tokens_per_s": BT * steps / wall, "count_ms": cnt_ms,
-            "fused_ms": fb_ms, "reduce_ms": red_ms, "fused_GBs": alg / fb_ms / 1e6,
-            "fused_pct_peak": 100.0 * alg / fb_ms / 1e6 / HBM_PEAK_GBS, "alg_bytes": alg,
-            "mean": mean.cpu().tolist()}
-
-
-def run_vocab_parallel(w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
+def run_vocab_parallel(timer, w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
     """The per-device passes of an n_shards-way vocabulary-parallel layout at its real
     shape: one device's column shard (BT, V / n_shards) of the same logits.  One step =
     step-1 partials -> merge of the n_shards gathered partials -> step-2 partials ->
@@ -182,36 +178,19 @@ def run_vocab_parallel(w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
     ce, lse_s, lse_t, tvd, sigma = f(), f(), f(), f(), f()
     inv = torch.empty(1, dtype=torch.float32, device=dev)
     grad = torch.empty_like(zsh)
-    stream = torch.cuda.current_stream()
-    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
+    s = torch.cuda.current_stream()
+    lx.lx_ce_tvd_count_valid(tg, II, None, inv, s)
     for n in range(n_shards):  # stand-ins for the other devices' partials
-        lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, -100, stats[n], stream)
-    lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, -100, ce, lse_s, lse_t, stream)
+        lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, II, stats[n], s)
+    lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, II, ce, lse_s, lse_t, s)
     for n in range(n_shards):
-        lx.lx_ce_tvd_vp_tv(zsh, ush, tg, -100, lse_s, lse_t, tv[n], stream)
-
-    def step(ev=None):
-        calls = (lambda: lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, -100, stats[0], stream),
-                 lambda: lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, -100, ce, lse_s, lse_t, stream),
-                 lambda: lx.lx_ce_tvd_vp_tv(zsh, ush, tg, -100, lse_s, lse_t, tv[0], stream),
-                 lambda: lx.lx_ce_tvd_vp_merge_tv(tv, tg, -100, tvd, sigma, stream),
-                 lambda: lx.lx_ce_tvd_backward_shard(grad, zsh, ush, tg, 0, V, -100, lse_s, lse_t, sigma, 1.0,
-                                                     1.0, inv, stream))
-        for k, c in enumerate(calls):
-            if ev is not None:
-                ev[k].record(stream)
-            c()
-        if ev is not None:
-            ev[len(calls)].record(stream)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    for k in range(steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(5)]
+        lx.lx_ce_tvd_vp_tv(zsh, ush, tg, II, lse_s, lse_t, tv[n], s)
+    calls = [lambda: lx.lx_ce_tvd_vp_stats(zsh, ush, tg, 0, II, stats[0], s),
+             lambda: lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, II, ce, lse_s, lse_t, s),
+             lambda: lx.lx_ce_tvd_vp_tv(zsh, ush, tg, II, lse_s, lse_t, tv[0], s),
+             lambda: lx.lx_ce_tvd_vp_merge_tv(tv, tg, II, tvd, sigma, s),
+             lambda: lx.lx_ce_tvd_backward_shard(grad, zsh, ush, tg, 0, V, II, lse_s, lse_t, sigma, 1.0, 1.0, inv, s)]
+    ms, step_ms, _ = timer.run(calls, steps, warmup)
     n_ign = BT - n_valid
     es = w.esize
     alg = {"stats": n_valid * 2 * Vs * es + BT * 8 + BT * 20,
@@ -225,33 +204,16 @@ def run_vocab_parallel(w, zs, us, tg, n_valid, steps, warmup, n_shards=8):
         out[f"{name}_GBs"] = round(b / t / 1e6, 1)
         if name in ("stats", "tv", "backward"):
             out[f"{name}_pct_peak"] = round(100.0 * b / t / 1e6 / HBM_PEAK_GBS, 2)
-    out["device_step_ms"] = round(sum(ms), 4)
+    out["device_step_ms"] = round(step_ms, 4)
     return out
 
 
-def _time_call(fn, steps, warmup):
-    """Average HIP-event time (ms) of fn() on the current stream."""
-    import torch
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
-
-
-def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
+def run_ex(timer, w, zs, us, tg, n_valid, steps, warmup, pad=128):
     """The one-pass forward + backward of the ABI-breadth entry points on the same batch:
     binary16 copies of the logits; the logits inside arrays padded to V + pad columns
-    (row strides, e.g. a vocabulary rounded up to a multiple of 256), gradient in
-    place; per-row upstream gradients (an unreduced loss).  Each is timed alone, with
-    its algorithmic bytes those of the one pass (read student and teacher once, write
-    the gradient once)."""
+    (row strides, e.g. a vocabulary rounded up to a multiple of 256); per-row upstream
+    gradients (an unreduced loss).  Each is timed alone, with its algorithmic bytes
+    those of the one pass (read student and teacher once, write the gradient once)."""
     import torch
     import cross_entropy_tv_amd as lx
 
@@ -259,41 +221,34 @@ def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
     dev = zs.device
     f = lambda: torch.empty(BT, dtype=torch.float32, device=dev)  # noqa: E731
     ce, lse_s, tvd, lse_t, sigma = f(), f(), f(), f(), f()
-    stream = torch.cuda.current_stream()
-    n_ign = BT - n_valid
-    alg = n_valid * 3 * V * w.esize + n_ign * V * w.esize + BT * 8 + BT * 4 * 5 + 4
+    s = torch.cuda.current_stream()
+    alg = algorithmic_bytes(BT, V, w.esize, n_valid, True)["forward_backward"]
     inv = torch.empty(1, dtype=torch.float32, device=dev)
-    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
+    lx.lx_ce_tvd_count_valid(tg, II, None, inv, s)
     nws = lx.lx_ce_tvd_forward_backward_workspace_bytes(BT, V, lx.LX_BF16, True)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     out = {}
 
-    def record(name, ms, extra=None):
+    def record(name, fn, extra=None):
+        (ms,), _, _ = timer.run([fn], steps, warmup)
         out[name] = {"ms": round(ms, 4), "GBs": round(alg / ms / 1e6, 1),
                      "pct_peak": round(100.0 * alg / ms / 1e6 / HBM_PEAK_GBS, 2), **(extra or {})}
 
     g = torch.empty_like(zs)
-
-    def plain():
-        lx.lx_ce_tvd_forward_backward(zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, inv, ws, stream)
-
-    # the headline call again, for reference next to the variants (same process, same memory state)
-    record("reference", _time_call(plain, steps, warmup))
-    # per-row upstream gradients of an unreduced loss (factors ~ U(0.5, 1.5))
+    plain = lambda: lx.lx_ce_tvd_forward_backward(zs, us, tg, II, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, inv,  # noqa: E731
+                                                   ws, s)
+    record("reference", plain)
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261202)
     wce = torch.rand(BT, generator=gen, device=dev) + 0.5
     wtv = torch.rand(BT, generator=gen, device=dev) + 0.5
-    record("row_factors", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
-        zs, us, tg, -100, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, wce, wtv, inv, ws, stream), steps, warmup))
-    # binary16 logits: the bf16 batch rounded to binary16
+    record("row_factors", lambda: lx.lx_ce_tvd_forward_backward_ex(
+        zs, us, tg, II, ce, tvd, lse_s, lse_t, sigma, g, 1.0, 1.0, wce, wtv, inv, ws, s))
     z16, u16 = zs.to(torch.float16), us.to(torch.float16)
     g16 = torch.empty_like(z16)
-    record("f16", _time_call(lambda: lx.lx_ce_tvd_forward_backward(
-        z16, u16, tg, -100, ce, tvd, lse_s, lse_t, sigma, g16, 1.0, 1.0, inv, ws, stream), steps, warmup),
-        {"logits": "f16"})
+    record("f16", lambda: lx.lx_ce_tvd_forward_backward(z16, u16, tg, II, ce, tvd, lse_s, lse_t, sigma, g16, 1.0, 1.0,
+                                                        inv, ws, s), {"logits": "f16"})
     del z16, u16, g16
-    # row strides: views into arrays of V + pad columns, gradient in place over a scratch copy
     zbig = torch.empty((BT, V + pad), dtype=zs.dtype, device=dev)
     ubig = torch.empty((BT, V + pad), dtype=us.dtype, device=dev)
     zbig[:, :V] = zs
@@ -301,21 +256,17 @@ def run_ex(w, zs, us, tg, n_valid, steps, warmup, pad=128):
     zv, uv = zbig[:, :V], ubig[:, :V]
     gbig = torch.empty_like(zbig)
     gv = gbig[:, :V]
-    record("strided", _time_call(lambda: lx.lx_ce_tvd_forward_backward_ex(
-        zv, uv, tg, -100, ce, tvd, lse_s, lse_t, sigma, gv, 1.0, 1.0, g_scale=inv, workspace=ws, stream=stream),
-        steps, warmup), {"row_stride": V + pad})
+    record("strided", lambda: lx.lx_ce_tvd_forward_backward_ex(
+        zv, uv, tg, II, ce, tvd, lse_s, lse_t, sigma, gv, 1.0, 1.0, g_scale=inv, workspace=ws, stream=s),
+        {"row_stride": V + pad})
     del zbig, ubig, gbig
-    record("reference_after", _time_call(plain, steps, warmup))
     return out
 
 
-def run_linear(steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192):
+def run_linear(timer, steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192):
     """The lm_head products + CE + TVD in one call (student and teacher lm_heads of
-    hidden size H over the vocabulary, seeded synthetic hidden states and weights):
-    the whole call, and each bf16 matrix product alone at the call's shapes, timed
-    with HIP events; FLOP/s against the dense bf16 matrix-core peak.  The whole
-    batch is one chunk (a workspace of ~10 B per logit, 12.4 GB here): chunks of
-    4096 rows cost 2.4% more time, of 2048 rows 8%."""
+    hidden size H over the vocabulary, seeded synthetic hidden states and weights),
+    timed with HIP events; FLOP/s against the dense bf16 matrix-core peak."""
     import numpy as np
     import torch
     import cross_entropy_tv_amd as lx
@@ -334,61 +285,41 @@ def run_linear(steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192):
     gx = torch.empty((BT, H), dtype=torch.float32, device=dev)
     gw = torch.empty((V, H), dtype=torch.float32, device=dev)
     inv = torch.empty(1, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    lx.lx_ce_tvd_count_valid(tg, -100, None, inv, stream)
-    ws = torch.empty(lx.lx_ce_tvd_linear_workspace_bytes(BT, V, True, chunk_rows), dtype=torch.uint8, device=dev)
-    ms = _time_call(lambda: lx.lx_ce_tvd_linear_forward_backward(
-        X, Wd, Xt, Wt, tg, -100, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, inv, chunk_rows, ws, stream),
-        steps, warmup)
+    s = torch.cuda.current_stream()
+    lx.lx_ce_tvd_count_valid(tg, II, None, inv, s)
+    wsb = lx.lx_ce_tvd_linear_workspace_bytes(BT, V, True, chunk_rows)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    (ms,), _, _ = timer.run([lambda: lx.lx_ce_tvd_linear_forward_backward(
+        X, Wd, Xt, Wt, tg, II, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, inv, chunk_rows, ws, s)],
+        max(3, steps // 4), max(1, warmup // 2))
     flops = 2.0 * BT * V * H * 4  # student and teacher logits, grad of x, grad of w
-    out = {"shape": f"BT={BT} V={V} H_s=H_t={H} chunk_rows={chunk_rows}", "ms": round(ms, 3),
-           "tokens_per_s": round(BT / ms * 1e3, 1), "TFLOPs": round(flops / ms / 1e9, 1),
+    out = {"shape": f"BT={BT} V={V} H_s=H_t={H} chunk_rows={chunk_rows}", "workspace_bytes": int(wsb),
+           "ms": round(ms, 3), "tokens_per_s": round(BT / ms * 1e3, 1), "TFLOPs": round(flops / ms / 1e9, 1),
            "pct_mfma_peak": round(100.0 * flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
-    # each product alone, at the shapes of one chunk
-    R = chunk_rows
-    z = torch.empty((R, V), dtype=torch.float32, device=dev)
-    # G with gradient-like values: an all-zero operand lets the matrix cores
-    # draw less power, and the products on it ran 14-28% faster than on the
-    # gradient the call itself produces
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(78)
-    G = (torch.randn((R, V), generator=gen, device=dev) * 1e-5).to(torch.bfloat16)
-    Gt, Xt = G.t().contiguous(), X[:R].t().contiguous()
-    gemms = {
-        "logits_XWt": (lambda: lx.lx_gemm_bf16(X[:R], True, Wd, True, z, R, V, H, False, stream), R, V, H),
-        "grad_x_GW": (lambda: lx.lx_gemm_bf16(G, True, Wd, False, gx[:R], R, H, V, False, stream), R, H, V),
-        # as the call forms it: from the transposed copies of G and x (both K-contiguous)
-        "grad_w_GtX": (lambda: lx.lx_gemm_bf16(Gt, True, Xt, True, gw, V, H, R, True, stream), V, H, R),
-    }
-    for name, (fn, M, N, K) in gemms.items():
-        t_ms = _time_call(fn, steps, warmup)
-        fl = 2.0 * M * N * K
-        out[name] = {"M": M, "N": N, "K": K, "ms": round(t_ms, 4), "TFLOPs": round(fl / t_ms / 1e9, 1),
-                     "pct_mfma_peak": round(100.0 * fl / t_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
-    del z, G, Gt, Xt, ws, gx, gw
+    del ws, gx, gw
     return out
 
 
-def copy_ceiling(dev, nbytes=2 << 30, reps=10):
-    """Achieved GB/s of a plain device copy (read + write), the practical streaming ceiling."""
+def stream_ceilings(timer, dev, steps, warmup, nbytes=2 << 30):
+    """Achieved GB/s of the library's reference streams: read-only over 2 * nbytes,
+    and two reads + one write of nbytes each (3 * nbytes moved)."""
     import torch
-    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
-    a.fill_(1)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    del a, b
-    return 2 * nbytes / ms / 1e6
+    import cross_entropy_tv_amd as lx
+
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.full((nbytes // 4,), 3, dtype=torch.int32, device=dev)
+    o = torch.empty_like(a)
+    big = torch.cat([a, b])
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    (rd,), _, _ = timer.run([lambda: lx.lx_stream_read(big, sink, s)], steps, warmup)
+    (rw,), _, _ = timer.run([lambda: lx.lx_stream_read2_write(a, b, o, s)], steps, warmup)
+    del a, b, o, big
+    return {"read_GBs": round(2 * nbytes / rd / 1e6, 1), "read2_write_GBs": round(3 * nbytes / rw / 1e6, 1),
+            "read_bytes": 2 * nbytes, "read2_write_bytes": 3 * nbytes}
 
 
-def traffic_from_profiles(kernel_key, launches_bytes):
+def traffic_from_profiles(kernel_key):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
     if they were taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -406,25 +337,40 @@ def traffic_from_profiles(kernel_key, launches_bytes):
     return k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds_per_worker=1.5, batch=4, workers=None):
+# ---------------------------------------------------------------- CPU baseline (the oracle as it stands)
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, seconds_per_worker=1.5, batch=4, workers=None, one_core_seconds=6.0):
     """The float64 oracle, as it stands, timed on the host cores over a bounded sample of
     the same workload's rows (forward + backward per row).  Each worker process takes
     its own rows in batches and stops once its timed oracle work passes
     ``seconds_per_worker``; the rate is the sum of the workers' rates (they run
-    concurrently)."""
+    concurrently).  A single process alone gives the 1-core figure."""
     import multiprocessing as mp
     cores = len(os.sched_getaffinity(0))
     workers = workers or min(cores, 16)
     ctx = mp.get_context("spawn")
     with ctx.Pool(workers) as pool:
         res = pool.map(_cpu_worker, [(w.name, i, workers, batch, seconds_per_worker) for i in range(workers)])
+    with ctx.Pool(1) as pool:
+        one = pool.map(_cpu_worker, [(w.name, 0, 1, batch, one_core_seconds)])[0]
     rate = sum(r[0] / r[1] for r in res)
     nrows = sum(r[0] for r in res)
     cpu_s = sum(r[1] for r in res)
     return {"value": round(rate, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "one_core_value": round(one[0] / one[1], 1), "cpu_model": cpu_model(), "host_cores_available": cores,
             "sample": f"{nrows} rows of the {w.name} workload ({w.BT}x{w.V} {w.dtype}), float64 numpy oracle "
                       f"forward+backward per row, {workers} single-threaded processes, {cpu_s:.1f} s of timed "
-                      f"CPU work in total"}
+                      f"CPU work in total; 1-core figure: {one[0]} rows in {one[1]:.1f} s in one process"}
 
 
 def _cpu_worker(arg):
@@ -448,17 +394,36 @@ def _cpu_worker(arg):
     return done, spent
 
 
+# ---------------------------------------------------------------- main
+
+def load_workload(name, dev):
+    import numpy as np
+    import torch
+    import workloads as W
+
+    w = W.get(name)
+    t0 = time.perf_counter()
+    z, u, t = W.full(w)
+    print(f"[bench] generated {w.name} {w.BT}x{w.V} {w.dtype} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+
+    def dev_copy(raw):
+        if raw.dtype == np.uint16:
+            return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(raw).to(dev)
+
+    zs, us, tg = dev_copy(z), dev_copy(u), dev_copy(t)
+    return w, zs, us, tg, int((t != W.IGNORE_INDEX).sum())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="train")
-    ap.add_argument("--mode", default="ce_tvd", choices=["ce_tvd", "ce"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ce-only", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload lines other than train")
     ap.add_argument("--no-ceiling", action="store_true")
-    ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-vocab-parallel", action="store_true")
     ap.add_argument("--no-ex", action="store_true", help="skip the binary16 / strided / per-row one-pass legs")
     ap.add_argument("--no-linear", action="store_true", help="skip the lm_head product + loss leg")
@@ -469,94 +434,73 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import cross_entropy_tv_amd as lx  # noqa: F401  (fails loudly if the HIP library is missing)
-    import workloads as W
 
     dev = torch.device("cuda:0")
-    w = W.get(args.workload)
-    t_gen = time.perf_counter()
-    z, u, t = W.full(w)
-    gen_s = time.perf_counter() - t_gen
-    print(f"[bench] generated {w.name} {w.BT}x{w.V} {w.dtype} in {gen_s:.1f} s", file=sys.stderr, flush=True)
-
-    def dev_copy(raw):
-        if raw.dtype == np.uint16:
-            return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(raw).to(dev)
-
-    zs, us, tg = dev_copy(z), dev_copy(u), dev_copy(t)
-    del z, u
-    n_valid = int((t != W.IGNORE_INDEX).sum())
-    teacher = args.mode == "ce_tvd"
-    main_res = run_mode(w, zs, us, tg, n_valid, args.steps, args.warmup, teacher)
-    print(f"[bench] {args.mode}: {main_res['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
-    extra = {}
-    if teacher and not args.no_ce_only:
-        ce_res = run_mode(w, zs, us, tg, n_valid, args.steps, args.warmup, False)
-        extra["ce_only"] = {k: ce_res[k] for k in ("tokens_per_s", "ms_per_step", "forward_ms", "backward_ms",
-                                                    "forward_GBs", "backward_GBs", "forward_pct_peak",
-                                                    "backward_pct_peak")}
-        if not args.no_fused:
-            cf = run_fused(w, zs, us, tg, n_valid, args.steps, args.warmup, teacher=False)
-            extra["ce_only"]["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cf.items()
-                                         if k != "mean"}
-    if teacher and not args.no_fused:
-        fu = run_fused(w, zs, us, tg, n_valid, args.steps, args.warmup)
-        extra["fused"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in fu.items()}
-    if teacher and not args.no_vocab_parallel and w.V % 8 == 0:
-        extra["vocab_parallel"] = run_vocab_parallel(w, zs, us, tg, n_valid, args.steps, args.warmup)
-    if teacher and not args.no_ex and w.dtype == "bf16":
-        extra["one_pass_ex"] = run_ex(w, zs, us, tg, n_valid, args.steps, args.warmup)
-    if teacher and not args.no_linear:
-        extra["linear"] = run_linear(args.steps, args.warmup)
+    timer = Timer(dev)
+    K, Wm = args.steps, args.warmup
+    w, zs, us, tg, n_valid = load_workload("train", dev)
+    head = measure(timer, w, zs, us, tg, n_valid, K, Wm, True)
+    print(f"[bench] train ce_tvd: one pass {head['one_pass']['ms_per_step']:.4f} ms/step, separate "
+          f"{head['separate']['ms_per_step']:.4f}", file=sys.stderr, flush=True)
+    extra = {"configs": {}}
+    extra["configs"]["train_ce_only"] = measure(timer, w, zs, us, tg, n_valid, K, Wm, False)
+    if not args.no_vocab_parallel:
+        extra["vocab_parallel"] = run_vocab_parallel(timer, w, zs, us, tg, n_valid, K, Wm)
+    if not args.no_ex:
+        extra["one_pass_ex"] = run_ex(timer, w, zs, us, tg, n_valid, K, Wm)
+    del zs, us, tg
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        for name in ("pr", "ties", "hugev"):
+            wc, zc, uc, tc, nc = load_workload(name, dev)
+            extra["configs"][name] = measure(timer, wc, zc, uc, tc, nc, K, Wm, True)
+            if name == "hugev":
+                extra["configs"]["hugev_ce_only"] = measure(timer, wc, zc, uc, tc, nc, K, Wm, False)
+            del zc, uc, tc
+            torch.cuda.empty_cache()
+    if not args.no_linear:
+        extra["linear"] = run_linear(timer, K, Wm)
+        torch.cuda.empty_cache()
     if not args.no_ceiling:
-        extra["copy_ceiling_GBs"] = copy_ceiling(dev)
+        c = stream_ceilings(timer, dev, K, Wm)
+        fwd = head["separate"]["forward_roofline"]["achieved"]
+        fb = head["one_pass"]["roofline"]["achieved"]
+        bwd = head["separate"]["backward_roofline"]["achieved"]
+        c["read_ceiling_covers_forward"] = c["read_GBs"] >= fwd
+        c["read2_write_ceiling_covers_one_pass_and_backward"] = c["read2_write_GBs"] >= max(fb, bwd)
+        extra["ceilings"] = c
 
-    # Headline: the fused path when it ran (forward and backward in one pass over the
-    # logits, then the mean), else the separate passes.  Both are reported.
-    if "fused" in extra:
-        fu = extra["fused"]
-        path = "fused"
-        value, ms_step = fu["tokens_per_s"], fu["ms_per_step"]
-        kname, kms, kbytes = "forward_backward", fu["fused_ms"], fu["alg_bytes"]
-    else:
-        path = "separate"
-        value, ms_step = main_res["tokens_per_s"], main_res["ms_per_step"]
-        # dominant kernel: the pass with the larger share of the step
-        kname = "backward" if main_res["backward_ms"] >= main_res["forward_ms"] else "forward"
-        kms, kbytes = main_res[f"{kname}_ms"], main_res["alg_bytes"][kname]
-    achieved = kbytes / kms / 1e6
-    traffic = traffic_from_profiles(f"{kname}_{args.mode}_{w.name}", kbytes)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
-                "alg_bytes_per_launch": kbytes, "avg_launch_ms": round(kms, 4)}
+    one, sep = head["one_pass"], head["separate"]
+    rl = dict(one["roofline"])
+    rl["traffic"] = traffic_from_profiles("forward_backward_ce_tvd_train")
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": one["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": one["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "BT": w.BT, "V": w.V, "logits": w.dtype, "mode": args.mode,
-                   "path": path, "global_batch": w.BT, "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
-        "separate_step": {"tokens_per_s": round(main_res["tokens_per_s"], 1),
-                          "ms_per_step": round(main_res["ms_per_step"], 4)},
-        "passes": {"forward_ms": round(main_res["forward_ms"], 4), "reduce_ms": round(main_res["reduce_ms"], 4),
-                   "backward_ms": round(main_res["backward_ms"], 4),
-                   "forward_GBs": round(main_res["forward_GBs"], 1),
-                   "backward_GBs": round(main_res["backward_GBs"], 1),
-                   "forward_pct_peak": round(main_res["forward_pct_peak"], 2),
-                   "backward_pct_peak": round(main_res["backward_pct_peak"], 2)},
-        "mean_loss": main_res["mean"],
+        "config": {"workload": "train", "BT": w.BT, "V": w.V, "logits": w.dtype, "mode": "ce_tvd",
+                   "path": "one pass (count -> forward_backward -> mean)", "global_batch": w.BT,
+                   "parallelism": "none (1 GPU)", "timing": "per rep, HIP events, 1 GiB cache flush before each rep"},
+        "roofline": rl,
+        "separate_step": {"tokens_per_s": sep["tokens_per_s"], "ms_per_step": sep["ms_per_step"]},
+        "passes": {"forward_ms": sep["forward_ms"], "reduce_ms": sep["reduce_ms"], "backward_ms": sep["backward_ms"],
+                   "forward_GBs": sep["forward_roofline"]["achieved"],
+                   "backward_GBs": sep["backward_roofline"]["achieved"],
+                   "forward_pct_peak": round(100 * sep["forward_roofline"]["frac"], 2),
+                   "backward_pct_peak": round(100 * sep["backward_roofline"]["frac"], 2),
+                   "one_pass_ms": one["forward_backward_ms"], "one_pass_pct_peak": round(100 * one["roofline"]["frac"], 2)},
+        "mean_loss": one["mean"],
+        "wall_s_timed_loop_incl_flush": one["wall_s_timed_loop"],
         **extra,
     }
     if not args.no_cpu_baseline:

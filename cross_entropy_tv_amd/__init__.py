@@ -68,6 +68,10 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_forward_backward.restype = i32
     L.lx_ce_tvd_forward_backward_noalloc.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p, p, f32, f32, p, i32, p]
     L.lx_ce_tvd_forward_backward_noalloc.restype = i32
+    L.lx_stream_read.argtypes = [p, i64, p, p]
+    L.lx_stream_read.restype = i32
+    L.lx_stream_read2_write.argtypes = [p, p, p, i64, p]
+    L.lx_stream_read2_write.restype = i32
     L.lx_ce_tvd_count_valid.argtypes = [p, i64, i64, p, p, p]
     L.lx_ce_tvd_count_valid.restype = i32
     L.lx_ce_tvd_vp_stats.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, p]
@@ -420,3 +424,17 @@ __all__ = [
     "lx_ce_tvd_backward_shard", "lx_ce_tvd_forward_ex", "lx_ce_tvd_backward_ex", "lx_ce_tvd_forward_backward_ex",
     "lx_gemm_bf16", "lx_ce_tvd_linear_workspace_bytes", "lx_ce_tvd_linear_forward_backward",
 ]
+
+
+def lx_stream_read(src, sink, stream=None) -> None:
+    """Reference stream: read every byte of src once (sink: int32/uint32 [1])."""
+    _check(lib.lx_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "lx_stream_read")
+
+
+def lx_stream_read2_write(a, b, out, stream=None) -> None:
+    """Reference stream: out = a XOR b over their bytes (all the same size)."""
+    nb = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nb or out.numel() * out.element_size() != nb:
+        raise ValueError("a, b and out must have the same number of bytes")
+    _check(lib.lx_stream_read2_write(_ptr(a), _ptr(b), _ptr(out), nb, _stream(stream)), "lx_stream_read2_write")

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblx_ce_tvd.so")
 SOURCES = ["api.hip", "forward.hip", "forward_cluster.hip", "backward.hip", "reduce.hip", "vocab_parallel.hip",
-           "gemm.hip", "linear.hip", "noalloc.hip"]
+           "gemm.hip", "linear.hip", "noalloc.hip", "stream.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -328,6 +328,22 @@ int lx_abi_version(void) { return LX_CE_TVD_ABI_VERSION; }
 
 int lx_last_hip_error(void) { return g_last_hip_error; }
 
+lx_status lx_stream_read(const void* src, int64_t bytes, unsigned* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > ((int64_t)1 << 40)) return LX_ERR_INVALID_ARG;
+  if (bytes == 0) return LX_OK;
+  if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4)) return LX_ERR_INVALID_ARG;
+  if (overlaps(span(src, bytes), span(sink, 4))) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+lx_status lx_stream_read2_write(const void* a, const void* b, void* out, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > ((int64_t)1 << 40)) return LX_ERR_INVALID_ARG;
+  if (bytes == 0) return LX_OK;
+  if (!a || !b || !out || !aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16)) return LX_ERR_INVALID_ARG;
+  if (overlaps(span(out, bytes), span(a, bytes)) || overlaps(span(out, bytes), span(b, bytes))) return LX_ERR_ALIAS;
+  return from_hip(lx::launch_stream_read2_write(a, b, out, bytes, static_cast<hipStream_t>(stream)));
+}
+
 size_t lx_ce_tvd_workspace_bytes(int64_t BT, int64_t V, lx_dtype dt, int has_teacher) {
   const int es = esize_of(dt);
   if (!es || check_shape(BT, V, es) != LX_OK) return 0;

@@ -115,6 +115,10 @@ hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* t
 hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,
                               float* tvd, float* sigma, hipStream_t stream);
 
+// Reference streams (stream.hip): bytes a multiple of 16, buffers 16-byte aligned.
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream);
+hipError_t launch_stream_read2_write(const void* a, const void* b, void* out, int64_t bytes, hipStream_t stream);
+
 // Records e as the calling thread's last HIP error (lx_last_hip_error).
 void record_hip_error(hipError_t e);
 

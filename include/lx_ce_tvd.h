@@ -451,6 +451,25 @@ lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, in
                                             int64_t chunk_rows, void* workspace, size_t workspace_bytes,
                                             void* stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Reference streams: the practical HBM ceilings the loss kernels are measured
+ * against (not part of the loss).  They move bytes the way the loss kernels
+ * do: 16-byte buffer loads and stores with the streamed-once cache policy.
+ *
+ * lx_stream_read reads `bytes` bytes of src once (the forward's pattern); it
+ * may write one uint32 to sink (only to keep the reads alive).
+ * lx_stream_read2_write reads a and b and writes out = a XOR b, `bytes` bytes
+ * each (the backward's and the one pass's pattern: two tensors in, one out).
+ *
+ * Inputs : device buffers, 16-byte aligned (sink 4-byte aligned); bytes a
+ *          multiple of 16, at most 2^40; 0 is a no-op.
+ * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS (out overlapping a or b, sink
+ *          overlapping src), LX_ERR_HIP.
+ */
+lx_status lx_stream_read(const void* src, int64_t bytes, unsigned* sink, void* stream);
+lx_status lx_stream_read2_write(const void* a, const void* b, void* out, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -155,6 +155,18 @@ def test_noalloc_validation():
     assert noalloc(**big) == lx.LX_ERR_TOO_LARGE
 
 
+def test_reference_stream_validation():
+    assert L.lx_stream_read(A, 0, A * 2, None) == lx.LX_OK
+    assert L.lx_stream_read(A, 24, A * 2, None) == lx.LX_ERR_INVALID_ARG      # not a multiple of 16
+    assert L.lx_stream_read(A + 8, 32, A * 2, None) == lx.LX_ERR_INVALID_ARG  # misaligned
+    assert L.lx_stream_read(None, 32, A * 2, None) == lx.LX_ERR_INVALID_ARG
+    assert L.lx_stream_read(A, 64, A + 16, None) == lx.LX_ERR_ALIAS          # sink inside src
+    assert L.lx_stream_read2_write(A, A * 2, A * 3, 0, None) == lx.LX_OK
+    assert L.lx_stream_read2_write(A, A * 2, A * 3, -16, None) == lx.LX_ERR_INVALID_ARG
+    assert L.lx_stream_read2_write(A, A * 2, A + 32, 64, None) == lx.LX_ERR_ALIAS
+    assert L.lx_stream_read2_write(A, None, A * 3, 64, None) == lx.LX_ERR_INVALID_ARG
+
+
 def test_count_valid_validation():
     c = L.lx_ce_tvd_count_valid
     assert c(A, -1, -100, A * 2, None, None) == lx.LX_ERR_INVALID_ARG
