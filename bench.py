@@ -287,7 +287,7 @@ def run_linear(timer, steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192)
     inv = torch.empty(1, dtype=torch.float32, device=dev)
     s = torch.cuda.current_stream()
     lx.lx_ce_tvd_count_valid(tg, II, None, inv, s)
-    wsb = lx.lx_ce_tvd_linear_workspace_bytes(BT, V, True, chunk_rows)
+    wsb = lx.lx_ce_tvd_linear_workspace_bytes(BT, V, H, True, chunk_rows)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     (ms,), _, _ = timer.run([lambda: lx.lx_ce_tvd_linear_forward_backward(
         X, Wd, Xt, Wt, tg, II, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, inv, chunk_rows, ws, s)],

@@ -93,7 +93,7 @@ def _load() -> ctypes.CDLL:
     L.lx_ce_tvd_forward_backward_ex.restype = i32
     L.lx_gemm_bf16.argtypes = [p, i64, i32, p, i64, i32, p, i64, i64, i64, i64, i32, p]
     L.lx_gemm_bf16.restype = i32
-    L.lx_ce_tvd_linear_workspace_bytes.argtypes = [i64, i64, i32, i64]
+    L.lx_ce_tvd_linear_workspace_bytes.argtypes = [i64, i64, i64, i32, i64]
     L.lx_ce_tvd_linear_workspace_bytes.restype = sz
     L.lx_ce_tvd_linear_forward_backward.argtypes = [p, p, i64, p, p, i64, p, i64, i64, i64, p, p, p, p, p, p, p,
                                                     f32, f32, p, i64, p, sz, p]
@@ -386,8 +386,8 @@ def lx_gemm_bf16(A, a_k_contiguous: bool, B, b_k_contiguous: bool, C, M: int, N:
                             int(bool(accumulate)), _stream(stream)), "lx_gemm_bf16")
 
 
-def lx_ce_tvd_linear_workspace_bytes(BT: int, V: int, has_teacher: bool, chunk_rows: int) -> int:
-    return lib.lx_ce_tvd_linear_workspace_bytes(BT, V, int(bool(has_teacher)), chunk_rows)
+def lx_ce_tvd_linear_workspace_bytes(BT: int, V: int, H_s: int, has_teacher: bool, chunk_rows: int) -> int:
+    return lib.lx_ce_tvd_linear_workspace_bytes(BT, V, H_s, int(bool(has_teacher)), chunk_rows)
 
 
 def lx_ce_tvd_linear_forward_backward(x_s, w_s, x_t, w_t, target, ignore_index, ce, tvd, lse_s, lse_t, sigma,
@@ -404,7 +404,7 @@ def lx_ce_tvd_linear_forward_backward(x_s, w_s, x_t, w_t, target, ignore_index, 
         if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
     chunk = BT if chunk_rows is None else int(chunk_rows)
-    need = lx_ce_tvd_linear_workspace_bytes(BT, V, x_t is not None, chunk)
+    need = lx_ce_tvd_linear_workspace_bytes(BT, V, x_s.shape[1], x_t is not None, chunk)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_s.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

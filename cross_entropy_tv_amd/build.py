@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblx_ce_tvd.so")
 SOURCES = ["api.hip", "forward.hip", "forward_cluster.hip", "backward.hip", "reduce.hip", "vocab_parallel.hip",
-           "gemm.hip", "linear.hip", "noalloc.hip", "stream.hip"]
+           "lm_head.hip", "noalloc.hip", "stream.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -64,7 +64,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lhipblaslt"]
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

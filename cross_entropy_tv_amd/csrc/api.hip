@@ -555,11 +555,11 @@ lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const voi
   return from_hip(lx::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)));
 }
 
-size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, int64_t chunk_rows) {
-  if (BT < 1 || V < 1 || V > (int64_t)INT_MAX || chunk_rows < 1) return 0;
+size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int64_t H_s, int has_teacher, int64_t chunk_rows) {
+  if (BT < 1 || V < 1 || V > (int64_t)INT_MAX || chunk_rows < 1 || H_s < 1 || H_s > lx::kGemmMaxLd) return 0;
   const int64_t rows = chunk_rows < BT ? chunk_rows : BT;
-  if (rows > INT64_MAX / V / 16) return 0;
-  return lx::linear_workspace_bytes(BT, chunk_rows, V, has_teacher != 0);
+  if (rows > INT64_MAX / V / 16 || BT > INT64_MAX / V / 16) return 0;
+  return lx::linear_workspace_bytes(BT, chunk_rows, V, H_s, has_teacher != 0);
 }
 
 lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, int64_t H_s, const void* x_t,
@@ -583,7 +583,7 @@ lx_status lx_ce_tvd_linear_forward_backward(const void* x_s, const void* w_s, in
       !aligned(grad_x_s, 4) || !aligned(grad_w_s, 4) ||
       (has_t && (!aligned(tvd, 4) || !aligned(lse_t, 4) || !aligned(sigma, 4))))
     return LX_ERR_INVALID_ARG;
-  const size_t need = lx_ce_tvd_linear_workspace_bytes(BT, V, has_t, chunk_rows);
+  const size_t need = lx_ce_tvd_linear_workspace_bytes(BT, V, H_s, has_t, chunk_rows);
   if (!need) return LX_ERR_INVALID_ARG;
   const int64_t fb = BT * 4;
   // 0..5 inputs (may overlap each other), 6..13 outputs and the workspace

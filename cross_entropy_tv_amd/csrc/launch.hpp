@@ -112,6 +112,11 @@ hipError_t launch_vp_tv(const VpArgs& a, Dt dt, hipStream_t stream);
 hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
                                  int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
                                  hipStream_t stream);
+// As launch_vp_merge_stats, also writing each row's target logit (the sum of
+// the shards' target parts; 0 for ignored rows) to zt (nullptr: not written).
+hipError_t launch_vp_merge_stats_zt(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
+                                    int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
+                                    float* zt, hipStream_t stream);
 hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,
                               float* tvd, float* sigma, hipStream_t stream);
 

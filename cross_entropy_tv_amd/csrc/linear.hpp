@@ -23,7 +23,7 @@ struct LinearArgs {
 };
 
 // Workspace for BT rows processed in chunks of at most chunk_rows rows.
-size_t linear_workspace_bytes(int64_t BT, int64_t chunk_rows, int64_t V, bool teacher);
+size_t linear_workspace_bytes(int64_t BT, int64_t chunk_rows, int64_t V, int64_t Hs, bool teacher);
 hipError_t run_linear(const LinearArgs& a, hipStream_t stream);
 
 }  // namespace lx

@@ -1,0 +1,741 @@
+// The lm_head product and the CE + TVD loss together, on the matrix cores,
+// with the logits kept on chip.
+//
+// The aibars.net Liger-Kernel project page lists a fused linear
+// cross-entropy among its kernels (the lm_head projection and the loss in one
+// operation, so the full logits are never kept); the Liger-Kernel PR #1384
+// analysis page describes the CE + TVD loss ("Forward Pass", "Backward Pass").
+// For student hidden states X_s (BT, H_s), student weight W_s (V, H_s) and
+// teacher X_t, W_t, with logits z = X_s W_s^T and u = X_t W_t^T:
+//
+//   pass 1 (stats)  every 256 x 128 tile of z and u is computed on the matrix
+//                   cores and reduced in registers to per-row (max, sum-exp)
+//                   partials of z and of u, plus z at the target column when
+//                   the tile holds it; the tiles' partials are merged in tile
+//                   order (the vocabulary-parallel merge: each tile is a
+//                   column shard) -> lse_s, lse_t, ce;
+//   pass 2 (TV)     the same tiles are computed again and reduced to per-row
+//                   (sum |p - q|, sum p * sign(p - q)) partials, merged in tile
+//                   order -> tvd, sigma; when gradients are wanted the pass also
+//                   writes 2^15 p as binary16 with the sign of p - q in its sign
+//                   bit, and a bit per logit marking exact ties (sign 0);
+//   G               from those, the per-row sigma and the target logit:
+//                   G = k (g_ce (p - [v == t]) + g_tvd / 2 * p (s - sigma)), bf16
+//                   (rounded to nearest even), written over the binary16 p and
+//                   also transposed;
+//   grad_x = G W_s  and  grad_w = G^T X_s on the matrix cores, from W_s^T and
+//                   X_s^T so that both operands of every product are contiguous
+//                   along K.
+//
+// z and u never reach memory: each pass recomputes its tiles from X and W
+// (the same kernel, the same accumulation order, so bit-identical logits in
+// both passes).  Rows go in chunks for pass 2 and the gradients; what a chunk
+// keeps in the workspace is 2 bytes of binary16 p and 1 bit per logit
+// (becoming G), the transposed G (2 bytes per logit), and O(rows x V / 128)
+// partials.
+#include "launch.hpp"
+#include "linear.hpp"
+#include "gemm.hpp"
+#include "mm.hpp"
+#include "common.hpp"
+
+namespace lx {
+
+namespace {
+
+using mm::f32x16_t;
+
+// K-slice stages in LDS: 256 x 256 tiles take 32 KB a stage, the dual 256 x
+// 128 tiles 24 KB; with 4 and 6 stages each keeps 3 and 5 slices in flight
+// (about 3000 and 2500 cycles of matrix-core time to cover a load's latency).
+constexpr int kStages = 4;
+constexpr int kStagesDual = 6;
+constexpr int kLds = kStages * 32768;
+constexpr int kLdsDual = kStagesDual * (16384 + 8192);
+
+// ---------------------------------------------------------------- plain products (fp32 C)
+
+// C[m][n] (+)= sum_k A(m, k) B(n, k): 256 x 256 tiles, one workgroup of 4 waves
+// per compute unit (the accumulators take all 256 AGPRs).
+template <bool AK, bool BK, bool ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end, const uint16_t* __restrict__ B,
+                      int64_t ldb, int64_t b_end, float* __restrict__ C, int64_t ldc, int M, int N, int K,
+                      int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  int tm, tn;
+  if (!mm::tile_coords(tiles_m, tiles_n, tm, tn)) return;
+  const int m0 = tm * mm::kBM, n0 = tn * 256;
+  const int lane = tid_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+  mm::SliceLoader<AK, 256> la;
+  mm::SliceLoader<BK, 256> lb;
+  la.init(A, lda, a_end, M, K, m0, wave);
+  lb.init(B, ldb, b_end, N, K, n0, wave);
+  mm::mainloop<AK, BK, 4, 256, kStages>(acc, lds, la, lb, K, wm, wn, wave);
+  // (accumulating: the 16 values of a 32 x 32 tile are all read before any is
+  // written back, so the reads are in flight together)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 32 * j + (lane & 31);
+      float old[16];
+      if (ACC) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm + 32 * i + mm::acc_row(r, lane);
+          old[r] = (m < M && n < N) ? C[(int64_t)m * ldc + n] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm + 32 * i + mm::acc_row(r, lane);
+        if (m < M && n < N) C[(int64_t)m * ldc + n] = ACC ? old[r] + acc[i][j][r] : acc[i][j][r];
+      }
+    }
+  }
+}
+
+template <bool AK, bool BK, bool ACC>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + mm::kBM - 1) / mm::kBM);
+  const int tiles_n = (int)((g.N + 255) / 256);
+  // bytes from each operand's start to the end of its last stored row
+  const int64_t a_end = 2 * (AK ? (g.M - 1) * g.lda + g.K : (g.K - 1) * g.lda + g.M);
+  const int64_t b_end = 2 * (BK ? (g.N - 1) * g.ldb + g.K : (g.K - 1) * g.ldb + g.N);
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, ACC>), dim3(mm::grid_for(tiles_m, tiles_n)), dim3(mm::kThreads), 0, st,
+                     g.A, g.lda, a_end, g.B, g.ldb, b_end, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- the loss passes over logit tiles
+
+constexpr int kDualBN = 128;  // logit columns per tile (each of z and u)
+// 32-bit words of tie bits per row
+__host__ __device__ __forceinline__ int64_t tie_words(int64_t V) { return (V + 31) >> 5; }
+constexpr float kInvPqBiasG = 0x1p-15f;  // 2^-kPqBias
+
+enum class Epi { Stats, TV };
+
+struct DualArgs {
+  const uint16_t *xs, *ws, *xt, *wt;  // bf16 X_s (rows, H_s), W_s (V, H_s), X_t, W_t (nullptr: CE-only)
+  int64_t Hs, Ht;
+  int rows, V;                        // this launch's rows (from row 0 of xs / xt) and the vocabulary
+  const int64_t* target;              // target of row 0 of this launch
+  int64_t ignore_index;
+  float* partials;                    // [tiles_n][rows][P] (Stats: P = 5 / 3; TV: 2)
+  const float *lse_s, *lse_t;         // TV: per row
+  uint16_t* p16;                      // TV with gradients: binary16 2^15 p, (rows, V), or nullptr
+  uint32_t* ties;                     // TV with gradients and a teacher: (rows, tie_words(V)) tie bits
+  int tiles_m, tiles_n;
+};
+
+// Per-row (max, sum-exp) of one tensor's tile values for the wave's 128 rows x
+// 32 NJ columns, merged with the other wave of the same rows through LDS: the
+// wave's result for tile row `lr` lands in red[(wn != 0) * 256 + lr]
+// (workgroup-visible after the caller's barrier).  Columns n >= V do not count.
+template <int NJ>
+__device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, int wn, int n0, int V, int lane,
+                                         Lse* red /* [2][256] */) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v[NJ];
+      float m = kMFloor;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool ok = n0 + wn + 32 * j + (lane & 31) < V;
+        v[j] = acc[i][j][r];
+        m = ok ? fmaxf(m, v[j]) : m;
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const float nb = -(m * kLog2e);
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool ok = n0 + wn + 32 * j + (lane & 31) < V;
+        s += ok ? exp2_hw(__builtin_fmaf(v[j], kLog2e, nb)) : 0.0f;
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+      if ((lane & 31) == 0) red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(r, lane)] = Lse{m, s};
+    }
+  }
+}
+
+// Pass 1 for one tensor: a 256 x 256 tile of its logits (the plain product's
+// main loop and tile), reduced to per-row (max, sum-exp) over the tile's
+// columns, written to slots `slot`, `slot + 1` of the row's record in
+// partials [tiles_n][rows][P]; the student's launch (slot 0) also writes the
+// target logit (or +0) to slot P - 1.  The teacher's launch fills slots 2, 3 of
+// the same records.
+struct StatsArgs {
+  const uint16_t *x, *w;
+  int64_t H;
+  int rows, V;
+  const int64_t* target;
+  int64_t ignore_index;
+  float* partials;
+  int P, slot;
+  int tiles_m, tiles_n;
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
+void lm_stats_kernel(StatsArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  int tm, tn;
+  if (!mm::tile_coords(a.tiles_m, a.tiles_n, tm, tn)) return;
+  const int m0 = tm * mm::kBM, n0 = tn * 256;
+  const int lane = tid_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+  {
+    mm::SliceLoader<true, 256> la;
+    mm::SliceLoader<true, 256> lb;
+    la.init(a.x, a.H, 2 * ((int64_t)(a.rows - 1) * a.H + a.H), a.rows, (int)a.H, m0, wave);
+    lb.init(a.w, a.H, 2 * ((int64_t)(a.V - 1) * a.H + a.H), a.V, (int)a.H, n0, wave);
+    mm::mainloop<true, true, 4, 256, kStages>(acc, lds, la, lb, (int)a.H, wm, wn, wave);
+  }
+  const int tid = tid_x();
+  const bool student = a.slot == 0;
+  int* tcol = reinterpret_cast<int*>(lds);
+  float* ztp = reinterpret_cast<float*>(lds + 1024);  // [2][256]
+  Lse* red = reinterpret_cast<Lse*>(lds + 4096);      // [2][256]
+  if (student) {
+    const int m = m0 + tid;
+    int c = -1;
+    if (m < a.rows) {
+      const int64_t t = a.target[m];
+      if (t != a.ignore_index && t >= n0 && t < n0 + 256 && t < a.V) c = (int)(t - n0);
+    }
+    tcol[tid] = c;
+    ztp[tid] = 0.0f;
+    ztp[256 + tid] = 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm + 32 * i + mm::acc_row(r, lane);
+        const int c = tcol[lr] - wn;
+        if (c >= 0 && c < 128 && (c & 31) == (lane & 31)) {
+          const int jj = c >> 5;
+          ztp[(wn != 0) * 256 + lr] = jj == 0 ? acc[i][0][r] : jj == 1 ? acc[i][1][r] : jj == 2 ? acc[i][2][r] : acc[i][3][r];
+        }
+      }
+    }
+  }
+  tile_lse<4>(acc, wm, wn, n0, a.V, lane, red);
+  __syncthreads();
+  const int m = m0 + tid;
+  if (m < a.rows) {
+    float* o = a.partials + ((int64_t)tn * a.rows + m) * a.P;
+    Lse f = red[tid];
+    lse_merge(f, red[256 + tid]);
+    o[a.slot] = f.m;
+    o[a.slot + 1] = f.s;
+    if (student) o[a.P - 1] = ztp[tid] + ztp[256 + tid];  // one of the two is the logit, the other +0
+  }
+}
+
+// One pass over the logit tiles: the products of a 256 x 128 tile of z (and
+// u), then the epilogue of the pass.  Four waves, 2 x 2, each 128 x 64 of each
+// tensor (4 x 2 MFMA accumulators per tensor: 128 + 128 AGPRs).
+template <Epi EPI, bool TEACHER, bool WRITE_P>
+__global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
+void lm_tile_kernel(DualArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDual];
+  int tm, tn;
+  if (!mm::tile_coords(a.tiles_m, a.tiles_n, tm, tn)) return;
+  const int m0 = tm * mm::kBM, n0 = tn * kDualBN;
+  const int lane = tid_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 64;
+
+  f32x16_t az[4][2], au[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      az[i][j] = (f32x16_t){};
+      au[i][j] = (f32x16_t){};
+    }
+  {
+    mm::SliceLoader<true, 256> la;
+    mm::SliceLoader<true, 128> lb;
+    la.init(a.xs, a.Hs, 2 * ((int64_t)(a.rows - 1) * a.Hs + a.Hs), a.rows, (int)a.Hs, m0, wave);
+    lb.init(a.ws, a.Hs, 2 * ((int64_t)(a.V - 1) * a.Hs + a.Hs), a.V, (int)a.Hs, n0, wave);
+    mm::mainloop<true, true, 2, 128, kStagesDual>(az, lds, la, lb, (int)a.Hs, wm, wn, wave);
+  }
+  if (TEACHER) {
+    mm::SliceLoader<true, 256> la;
+    mm::SliceLoader<true, 128> lb;
+    la.init(a.xt, a.Ht, 2 * ((int64_t)(a.rows - 1) * a.Ht + a.Ht), a.rows, (int)a.Ht, m0, wave);
+    lb.init(a.wt, a.Ht, 2 * ((int64_t)(a.V - 1) * a.Ht + a.Ht), a.V, (int)a.Ht, n0, wave);
+    mm::mainloop<true, true, 2, 128, kStagesDual>(au, lds, la, lb, (int)a.Ht, wm, wn, wave);
+  }
+  // LDS is free again (every wave is past the main loops' final barrier)
+  const int tid = tid_x();
+
+  if constexpr (EPI == Epi::Stats) {
+    // per tile row: its target column relative to the tile, or -1
+    int* tcol = reinterpret_cast<int*>(lds);
+    float* ztp = reinterpret_cast<float*>(lds + 1024);   // [2][256] target logit (or 0) per wave column
+    Lse* red_z = reinterpret_cast<Lse*>(lds + 4096);      // [2][256]
+    Lse* red_u = reinterpret_cast<Lse*>(lds + 8192);      // [2][256]
+    {
+      const int m = m0 + tid;
+      int c = -1;
+      if (m < a.rows) {
+        const int64_t t = a.target[m];
+        if (t != a.ignore_index && t >= n0 && t < n0 + kDualBN && t < a.V) c = (int)(t - n0);
+      }
+      tcol[tid] = c;
+      ztp[tid] = 0.0f;
+      ztp[256 + tid] = 0.0f;
+    }
+    __syncthreads();
+    // the target logit: the lane holding column tcol of the row takes it from its accumulators
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm + 32 * i + mm::acc_row(r, lane);
+        const int c = tcol[lr] - wn;
+        if (c >= 0 && c < 64 && (c & 31) == (lane & 31)) ztp[(wn != 0) * 256 + lr] = (c >> 5) ? az[i][1][r] : az[i][0][r];
+      }
+    }
+    tile_lse<2>(az, wm, wn, n0, a.V, lane, red_z);
+    if (TEACHER) tile_lse<2>(au, wm, wn, n0, a.V, lane, red_u);
+    __syncthreads();
+    const int m = m0 + tid;
+    if (m < a.rows) {
+      constexpr int P = TEACHER ? 5 : 3;
+      float* o = a.partials + ((int64_t)tn * a.rows + m) * P;
+      Lse fz = red_z[tid];
+      lse_merge(fz, red_z[256 + tid]);
+      o[0] = fz.m;
+      o[1] = fz.s;
+      if (TEACHER) {
+        Lse fu = red_u[tid];
+        lse_merge(fu, red_u[256 + tid]);
+        o[2] = fu.m;
+        o[3] = fu.s;
+      }
+      o[P - 1] = ztp[tid] + ztp[256 + tid];  // one of the two is the logit, the other +0
+    }
+  } else {
+    // TV: p' = 2^15 p, q' = 2^15 q and s' = 2^-24 sign(p - q) from the arguments
+    // a = x log2(e) - lse log2(e) + 15, exactly as the other TV kernels form them
+    float* nbs = reinterpret_cast<float*>(lds);         // [256]
+    float* nbt = reinterpret_cast<float*>(lds + 1024);  // [256]
+    float* red = reinterpret_cast<float*>(lds + 2048);  // [2][256][2] (S, Q) per wave column
+    {
+      const int m = m0 + tid;
+      float bs = kMFloor, bt = kMFloor;  // ignored and absent rows: p = q = 0
+      if (m < a.rows && a.target[m] != a.ignore_index) {
+        bs = pq_bias(a.lse_s[m]);
+        if (TEACHER) bt = pq_bias(a.lse_t[m]);
+      }
+      nbs[tid] = bs;
+      nbt[tid] = bt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm + 32 * i + mm::acc_row(r, lane);
+        const int m = m0 + lr;
+        const float bs = nbs[lr], bt = nbt[lr];
+        float S = 0.0f, Q = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn + 32 * j + (lane & 31);
+          const bool ok = n < a.V;
+          const float ap = exparg(az[i][j][r], bs);
+          const float pp = exp2_hw(ap);
+          float sg = 0.0f;
+          if (TEACHER) {
+            const float aq = exparg(au[i][j][r], bt);
+            sg = sign_eps(ap, aq);
+            S = __builtin_fmaf(ok ? pp : 0.0f, sg, S);
+            Q = __builtin_fmaf(ok ? exp2_hw(aq) : 0.0f, sg, Q);
+          }
+          if (WRITE_P) {
+            const bool in = ok && m < a.rows;
+            uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)pp);
+            if (TEACHER && sg < 0.0f) h |= 0x8000u;
+            if (in) a.p16[(int64_t)m * a.V + n] = h;
+            if (TEACHER) {
+              // one bit per logit: sign(p - q) = 0 exactly (the lanes of a half
+              // hold 32 consecutive columns of one row)
+              const uint64_t tie = __ballot(in && sg == 0.0f);
+              const int first = lane & 32;
+              if ((lane & 31) == 0 && m < a.rows && n < a.V)
+                a.ties[(int64_t)m * tie_words(a.V) + (n >> 5)] = (uint32_t)(tie >> first);
+            }
+          }
+        }
+        if (TEACHER) {
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) {
+            S += __shfl_xor(S, off, 64);
+            Q += __shfl_xor(Q, off, 64);
+          }
+          if ((lane & 31) == 0) {
+            red[((wn != 0) * 256 + lr) * 2] = S;
+            red[((wn != 0) * 256 + lr) * 2 + 1] = Q;
+          }
+        }
+      }
+    }
+    if (TEACHER) {
+      __syncthreads();
+      const int m = m0 + tid;
+      if (m < a.rows) {
+        const float S = red[tid * 2] + red[(256 + tid) * 2];
+        const float Q = red[tid * 2 + 1] + red[(256 + tid) * 2 + 1];
+        float* o = a.partials + ((int64_t)tn * a.rows + m) * 2;
+        o[0] = (S - Q) * kTvScale;  // sum |p - q| over the tile's columns
+        o[1] = S * kTvScale;        // sum p * sign(p - q)
+      }
+    }
+  }
+}
+
+template <Epi EPI, bool TEACHER, bool WRITE_P>
+hipError_t launch_tiles(const DualArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((lm_tile_kernel<EPI, TEACHER, WRITE_P>), dim3(mm::grid_for(a.tiles_m, a.tiles_n)),
+                     dim3(mm::kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- G from binary16 p
+
+constexpr int kGRows = 64;   // rows per tile
+constexpr int kGCols = 256;  // columns per tile
+
+struct GformArgs {
+  const int64_t* target;
+  int rows, V;
+  int64_t ignore_index;
+  const float *lse_s, *sigma, *zt;   // per row (sigma nullptr: CE-only)
+  const uint32_t* ties;              // (rows, tie_words(V)) or nullptr (CE-only)
+  uint16_t* g;                       // (rows, V): binary16 p in, bf16 G out (in place)
+  uint16_t* gt;                      // (V, ldr) transposed G, or nullptr
+  int64_t ldr;
+  float g_ce, g_tvd;
+  const float* g_scale;
+};
+
+// G = p (alpha + beta s) - k g_ce [v == t] with alpha = k g_ce - beta sigma,
+// beta = k g_tvd / 2 (the one-pass kernels' step 3: p' (a1 + b1 s'), p' =
+// 2^15 p from the binary16 copy, a1 = alpha 2^-15, b1 = beta 2^9, s' = 2^-24
+// sign), the target element from its logit in fp32.  A tile of 64 rows x 256
+// columns per workgroup: each thread converts 8 groups of 8 consecutive
+// values (16 bytes in, 16 bytes out in place), and the tile goes through LDS
+// to be written transposed (16-byte stores along the rows of G^T).
+__global__ __launch_bounds__(256) void gform_kernel(GformArgs a) {
+  constexpr int kStride = kGCols + 2;  // halves per LDS row
+  __shared__ uint32_t tile32[kGRows * kStride / 2];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(tile32);
+  const int tid = tid_x();
+  const unsigned tiles_c = (unsigned)(a.V + kGCols - 1) / kGCols;
+  const unsigned b = bid_x();
+  const unsigned tr = b / tiles_c;
+  const int r0 = (int)tr * kGRows, c0 = (int)(b - tr * tiles_c) * kGCols;
+  const int lc = (tid & 7) * 8;
+  const float k = a.g_scale ? *a.g_scale : 1.0f;
+  const float kce = k * a.g_ce;
+  const float beta = a.sigma ? 0.5f * k * a.g_tvd : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // (row half, 64-column block)
+    const int lr = (tid >> 3) + 32 * (i & 1), cc = lc + 64 * (i >> 1);
+    const int r = r0 + lr, c = c0 + cc;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (r < a.rows && c < a.V) {
+      const int64_t t = a.target[r];
+      uint16_t* gp = a.g + (int64_t)r * a.V + c;
+      if (t != a.ignore_index) {
+        const bool t_ok = t >= 0 && t < a.V;
+        const float alpha = kce - beta * (a.sigma ? a.sigma[r] : 0.0f);
+        const float a1 = alpha * kInvPqBiasG, b1 = beta * kTvScale;
+        const uint4 in = *reinterpret_cast<const uint4*>(gp);
+        const uint32_t tb = a.ties ? a.ties[(int64_t)r * tie_words(a.V) + (c >> 5)] >> (c & 31) : 0u;
+        // the target element from its logit in fp32 (p may be close to 1 there)
+        const float pt = t_ok ? exp2_hw(exparg(a.zt[r], pq_bias(a.lse_s[r]))) : 0.0f;
+        const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t h = (uint16_t)(iw[e >> 1] >> (16 * (e & 1)));
+          const float pp = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0x7fffu));
+          const float sg = ((tb >> e) & 1u) ? 0.0f : ((h & 0x8000u) ? -kSignEps : kSignEps);
+          const float f = __builtin_fmaf(sg, b1, a1);
+          o[e] = (c + e == t) ? pt * f - kce : pp * f;
+        }
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        w[2] = pack_bf16x2(o[4], o[5]);
+        w[3] = pack_bf16x2(o[6], o[7]);
+        if (!t_ok) w[0] = w[1] = w[2] = w[3] = (uint32_t)kQNaN16 * 0x10001u;
+      }
+      *reinterpret_cast<uint4*>(gp) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile32[(lr * kStride + cc) / 2 + q] = w[q];
+  }
+  if (!a.gt) return;
+  __syncthreads();
+  const int lr = (tid & 7) * 8;  // 8 consecutive rows = columns of G^T
+  const int r = r0 + lr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int oc = (tid >> 3) + 32 * i;  // a column of G = a row of G^T
+    const int c = c0 + oc;
+    if (c < a.V && r < a.ldr) {  // r % 8 == 0 and ldr % 8 == 0: the 8 values fit the row
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)tile[(lr + 2 * q) * kStride + oc] | ((uint32_t)tile[(lr + 2 * q + 1) * kStride + oc] << 16);
+      *reinterpret_cast<uint4*>(a.gt + (int64_t)c * a.ldr + r) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- transpose (bf16)
+
+constexpr int kTrRows = 64;   // input rows per tile
+constexpr int kTrCols = 256;  // input columns per tile
+
+// out (cols x ld_out) = the transpose of in (rows x cols, row stride ld_in),
+// bf16 bit patterns, through a 64 x 256 LDS tile per workgroup: 16-byte loads
+// along the input rows, 16-byte stores along the output rows; output columns
+// rows..ld_out-1 are written as zeros.  ld_out % 8 == 0, out 16-byte aligned;
+// vec_in says whether in's rows are 16-byte aligned (else element loads).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
+                                                             int rows, int cols, uint16_t* __restrict__ out,
+                                                             int64_t ld_out, int vec_in) {
+  constexpr int kStride = kTrCols + 2;
+  __shared__ uint32_t tile32[kTrRows * kStride / 2];
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile32);
+  const int tid = tid_x();
+  const unsigned tiles_c = (unsigned)(cols + kTrCols - 1) / kTrCols;
+  const unsigned b = bid_x();
+  const unsigned tr = b / tiles_c;
+  const int r0 = (int)tr * kTrRows, c0 = (int)(b - tr * tiles_c) * kTrCols;
+  const int lc = (tid & 7) * 8;
+  uint32_t w[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int lr = (tid >> 3) + 32 * (i & 1), c = c0 + lc + 64 * (i >> 1), r = r0 + lr;
+    w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+    if (r < rows) {
+      const uint16_t* src = in + (int64_t)r * ld_in + c;
+      if (vec_in && c + 8 <= cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (c + k < cols) w[i][k >> 1] |= (uint32_t)src[k] << (16 * (k & 1));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int lr = (tid >> 3) + 32 * (i & 1), cc = lc + 64 * (i >> 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tile32[(lr * kStride + cc) / 2 + k] = w[i][k];
+  }
+  __syncthreads();
+  const int lr = (tid & 7) * 8;
+  const int r = r0 + lr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int oc = (tid >> 3) + 32 * i;
+    const int c = c0 + oc;
+    if (c < cols && r < ld_out) {
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = (uint32_t)tile[(lr + 2 * k) * kStride + oc] | ((uint32_t)tile[(lr + 2 * k + 1) * kStride + oc] << 16);
+      *reinterpret_cast<uint4*>(out + (int64_t)c * ld_out + r) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t ld_in, int64_t rows, int64_t cols, uint16_t* out,
+                                 int64_t ld_out, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (ld_out % 8 || ld_out < rows || reinterpret_cast<uintptr_t>(out) % 16 || ld_in < cols) return hipErrorInvalidValue;
+  const int64_t tiles = ((rows + kTrRows - 1) / kTrRows) * ((cols + kTrCols - 1) / kTrCols);
+  if (rows > INT32_MAX || cols > INT32_MAX || tiles > UINT32_MAX) return hipErrorInvalidValue;
+  const int vec_in = (ld_in % 8 == 0 && reinterpret_cast<uintptr_t>(in) % 16 == 0) ? 1 : 0;
+  transpose_bf16_kernel<<<dim3((unsigned)tiles), dim3(256), 0, st>>>(in, ld_in, (int)rows, (int)cols, out, ld_out,
+                                                                     vec_in);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- workspace
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct LinearWs {
+  float* stats;      // [V / 256 tiles][BT][P]
+  float* zt;         // [BT]
+  float* tv;         // [tiles_n][chunk][2]
+  uint16_t* p16;     // (chunk, V): binary16 p, then bf16 G
+  uint32_t* ties;    // (chunk, tie_words(V))
+  uint16_t* gt;      // (V, ldr): G^T
+  uint16_t* wst;     // (H_s, V): W_s^T
+  uint16_t* xst;     // (H_s, ldr): X_s[chunk]^T
+  int64_t ldr;
+  size_t bytes;
+};
+
+LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs, bool teacher, bool gx, bool gw) {
+  LinearWs w{};
+  const int64_t tiles_n = (V + kDualBN - 1) / kDualBN;
+  const int P = teacher ? 5 : 3;
+  const bool grads = gx || gw;
+  w.ldr = (chunk + 7) & ~(int64_t)7;
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  w.stats = reinterpret_cast<float*>(take((size_t)((V + 255) / 256) * BT * P * 4));
+  w.zt = reinterpret_cast<float*>(take((size_t)BT * 4));
+  w.tv = teacher ? reinterpret_cast<float*>(take((size_t)tiles_n * chunk * 2 * 4)) : nullptr;
+  w.p16 = grads ? reinterpret_cast<uint16_t*>(take((size_t)chunk * V * 2)) : nullptr;
+  w.ties = (grads && teacher) ? reinterpret_cast<uint32_t*>(take((size_t)chunk * tie_words(V) * 4)) : nullptr;
+  w.gt = gw ? reinterpret_cast<uint16_t*>(take((size_t)V * w.ldr * 2)) : nullptr;
+  w.wst = gx ? reinterpret_cast<uint16_t*>(take((size_t)Hs * V * 2)) : nullptr;
+  w.xst = gw ? reinterpret_cast<uint16_t*>(take((size_t)Hs * w.ldr * 2)) : nullptr;
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- entry points
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
+  (void)hipGetLastError();
+  if (g.a_kc) {
+    if (g.b_kc) return g.accumulate ? launch_gemm_t<true, true, true>(g, st) : launch_gemm_t<true, true, false>(g, st);
+    return g.accumulate ? launch_gemm_t<true, false, true>(g, st) : launch_gemm_t<true, false, false>(g, st);
+  }
+  if (g.b_kc) return g.accumulate ? launch_gemm_t<false, true, true>(g, st) : launch_gemm_t<false, true, false>(g, st);
+  return g.accumulate ? launch_gemm_t<false, false, true>(g, st) : launch_gemm_t<false, false, false>(g, st);
+}
+
+size_t linear_workspace_bytes(int64_t BT, int64_t chunk_rows, int64_t V, int64_t Hs, bool teacher) {
+  if (BT <= 0) return 0;
+  const int64_t chunk = chunk_rows < BT ? chunk_rows : BT;
+  return linear_ws(nullptr, BT, chunk, V, Hs, teacher, true, true).bytes;
+}
+
+hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
+  const bool teacher = a.x_t != nullptr;
+  const int64_t V = a.V;
+  const int64_t chunk = a.chunk_rows < a.BT ? a.chunk_rows : a.BT;
+  const bool gx = a.grad_x_s != nullptr, gw = a.grad_w_s != nullptr, grads = gx || gw;
+  const LinearWs w = linear_ws(a.workspace, a.BT, chunk, V, a.H_s, teacher, true, true);
+  const int tiles_n = (int)((V + kDualBN - 1) / kDualBN);
+
+  // pass 1 over all rows: per-tile (max, sum-exp) of z and of u (256 x 256 tiles,
+  // one launch per tensor) and the target logit
+  {
+    const int stiles_n = (int)((V + 255) / 256);
+    StatsArgs sa{};
+    sa.x = a.x_s; sa.w = a.w_s; sa.H = a.H_s; sa.rows = (int)a.BT; sa.V = (int)V; sa.target = a.target;
+    sa.ignore_index = a.ignore_index; sa.partials = w.stats; sa.P = teacher ? 5 : 3; sa.slot = 0;
+    sa.tiles_m = (int)((a.BT + mm::kBM - 1) / mm::kBM);
+    sa.tiles_n = stiles_n;
+    (void)hipGetLastError();
+    const unsigned grid = mm::grid_for(sa.tiles_m, sa.tiles_n);
+    lm_stats_kernel<<<dim3(grid), dim3(mm::kThreads), 0, st>>>(sa);
+    hipError_t e = hipGetLastError();
+    if (e) return e;
+    if (teacher) {
+      sa.x = a.x_t; sa.w = a.w_t; sa.H = a.H_t; sa.slot = 2;
+      lm_stats_kernel<<<dim3(grid), dim3(mm::kThreads), 0, st>>>(sa);
+      if ((e = hipGetLastError())) return e;
+    }
+    if ((e = launch_vp_merge_stats_zt(w.stats, stiles_n, a.target, a.BT, V, a.ignore_index, teacher, a.ce, a.lse_s,
+                                      teacher ? a.lse_t : nullptr, w.zt, st)))
+      return e;
+  }
+  if (!teacher && !grads) return hipSuccess;
+  if (gx) {  // W_s^T: (H_s, V), both operands of grad_x = G W_s contiguous along V
+    if (hipError_t e = launch_transpose_bf16(a.w_s, a.H_s, V, a.H_s, w.wst, V, st)) return e;
+  }
+  for (int64_t r0 = 0; r0 < a.BT; r0 += chunk) {
+    const int64_t rows = a.BT - r0 < chunk ? a.BT - r0 : chunk;
+    // pass 2 over the chunk: (sum |p - q|, sum p s) per tile, and binary16 p + tie bits for G
+    DualArgs d{};
+    d.xs = a.x_s + r0 * a.H_s; d.ws = a.w_s; d.xt = teacher ? a.x_t + r0 * a.H_t : nullptr; d.wt = a.w_t;
+    d.Hs = a.H_s; d.Ht = a.H_t; d.rows = (int)rows; d.V = (int)V; d.target = a.target + r0;
+    d.ignore_index = a.ignore_index; d.partials = w.tv; d.lse_s = a.lse_s + r0;
+    d.lse_t = teacher ? a.lse_t + r0 : nullptr; d.p16 = w.p16; d.ties = w.ties;
+    d.tiles_m = (int)((rows + mm::kBM - 1) / mm::kBM);
+    d.tiles_n = tiles_n;
+    hipError_t e;
+    if (teacher) {
+      e = grads ? launch_tiles<Epi::TV, true, true>(d, st) : launch_tiles<Epi::TV, true, false>(d, st);
+      if (e) return e;
+      if ((e = launch_vp_merge_tv(w.tv, tiles_n, a.target + r0, rows, a.ignore_index, a.tvd + r0, a.sigma + r0, st)))
+        return e;
+    } else {
+      if ((e = launch_tiles<Epi::TV, false, true>(d, st))) return e;  // binary16 p only
+    }
+    if (!grads) continue;
+    // G (bf16, over the binary16 p) and G^T
+    GformArgs g{};
+    g.target = a.target + r0; g.rows = (int)rows; g.V = (int)V; g.ignore_index = a.ignore_index;
+    g.lse_s = a.lse_s + r0; g.sigma = teacher ? a.sigma + r0 : nullptr; g.zt = w.zt + r0;
+    g.ties = w.ties; g.g = w.p16; g.gt = gw ? w.gt : nullptr; g.ldr = w.ldr;
+    g.g_ce = a.g_ce; g.g_tvd = a.g_tvd; g.g_scale = a.g_scale;
+    const int64_t gtiles = ((rows + kGRows - 1) / kGRows) * ((V + kGCols - 1) / kGCols);
+    (void)hipGetLastError();
+    gform_kernel<<<dim3((unsigned)gtiles), dim3(256), 0, st>>>(g);
+    if ((e = hipGetLastError())) return e;
+    if (gx) {  // grad_x[chunk] = G W_s: M = rows, N = H_s, K = V
+      GemmArgs p{w.p16, V, w.wst, V, a.grad_x_s + r0 * a.H_s, a.H_s, rows, a.H_s, V, true, true, false};
+      if ((e = launch_gemm_bf16(p, st))) return e;
+    }
+    if (gw) {  // grad_w (+)= G^T X_s[chunk]: M = V, N = H_s, K = rows
+      if ((e = launch_transpose_bf16(a.x_s + r0 * a.H_s, a.H_s, rows, a.H_s, w.xst, w.ldr, st))) return e;
+      // K rounded up to whole 16-byte groups: a buffer load that runs past the
+      // operand's range reads zeros as a whole, so the last row's final group
+      // must lie inside it; the padding columns of G^T and X_s^T are zeros
+      const int64_t kr = (rows + 7) & ~(int64_t)7;
+      GemmArgs p{w.gt, w.ldr, w.xst, w.ldr, a.grad_w_s, a.H_s, V, a.H_s, kr, true, true, r0 > 0};
+      if ((e = launch_gemm_bf16(p, st))) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace lx

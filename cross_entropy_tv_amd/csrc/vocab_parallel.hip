@@ -93,7 +93,8 @@ __global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ stud
 template <bool TEACHER>
 __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
     const float* __restrict__ stats, int N, int64_t BT, const int64_t* __restrict__ target, int64_t V,
-    int64_t ignore_index, float* __restrict__ ce, float* __restrict__ lse_s, float* __restrict__ lse_t) {
+    int64_t ignore_index, float* __restrict__ ce, float* __restrict__ lse_s, float* __restrict__ lse_t,
+    float* __restrict__ zt_out) {
   constexpr int P = TEACHER ? 5 : 3;
   for (int64_t r = bid_x() * (int64_t)bdim_x() + tid_x(); r < BT; r += (int64_t)nblocks_x() * bdim_x()) {
     const int64_t t = target[r];
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
       ce[r] = 0.0f;
       lse_s[r] = 0.0f;
       if (TEACHER) lse_t[r] = 0.0f;
+      if (zt_out) zt_out[r] = 0.0f;
       continue;
     }
     const float* w = stats + r * P;
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
     if (t >= 0 && t < V) ce[r] = ls - zt; else store_nan(ce + r);
     lse_s[r] = ls;
     if (TEACHER) lse_t[r] = lse_value(ft);
+    if (zt_out) zt_out[r] = zt;  // the target logit itself
   }
 }
 
@@ -235,18 +238,24 @@ hipError_t launch_vp_tv(const VpArgs& a, Dt dt, hipStream_t st) {
   }
 }
 
-hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
-                                 int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
-                                 hipStream_t st) {
+hipError_t launch_vp_merge_stats_zt(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
+                                    int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
+                                    float* zt, hipStream_t st) {
   (void)hipGetLastError();
   if (teacher) {
     hipLaunchKernelGGL((vp_merge_stats_kernel<true>), dim3(merge_grid(BT)), dim3(kVpMergeThreads), 0, st, stats,
-                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t);
+                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t, zt);
   } else {
     hipLaunchKernelGGL((vp_merge_stats_kernel<false>), dim3(merge_grid(BT)), dim3(kVpMergeThreads), 0, st, stats,
-                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t);
+                       (int)N, BT, target, V, ignore_index, ce, lse_s, lse_t, zt);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_vp_merge_stats(const float* stats, int64_t N, const int64_t* target, int64_t BT, int64_t V,
+                                 int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t,
+                                 hipStream_t st) {
+  return launch_vp_merge_stats_zt(stats, N, target, BT, V, ignore_index, teacher, ce, lse_s, lse_t, nullptr, st);
 }
 
 hipError_t launch_vp_merge_tv(const float* tv, int64_t N, const int64_t* target, int64_t BT, int64_t ignore_index,

@@ -27,9 +27,15 @@
  * - Logits are row-major, shape (BT, V), element type `dt`; student and
  *   teacher share the type.  Row r starts at element r * V (the `_ex` entry
  *   points take a row stride per tensor instead: row r at element r * ld).
- * - All array pointers are DEVICE pointers owned by the caller.  The library
- *   allocates nothing, keeps no state between calls and is safe to call from
- *   several host threads (on different or on the same stream).
+ * - All array pointers are DEVICE pointers owned by the caller.  No entry
+ *   point allocates device or host memory, and the results of a call depend
+ *   on its arguments only; entry points that need scratch memory take a
+ *   caller-owned workspace.  The one exception is
+ *   lx_ce_tvd_forward_backward_noalloc, whose scratch is a fixed device array
+ *   inside the library (its address looked up once per device and kept in a
+ *   host table): calls of that entry point that overlap on one device race.
+ *   Every other entry point is safe to call from several host threads (on
+ *   different or on the same stream).
  * - `stream` is a hipStream_t passed as an opaque pointer; NULL selects the
  *   null stream.  Every call is asynchronous on that stream: the call returns
  *   after enqueueing its kernels.
@@ -66,7 +72,7 @@
 extern "C" {
 #endif
 
-#define LX_CE_TVD_ABI_VERSION 6
+#define LX_CE_TVD_ABI_VERSION 7
 
 typedef enum lx_status {
   LX_OK = 0,
@@ -388,17 +394,21 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  * analysis page's CE + TVD loss ("Forward Pass", "Backward Pass") runs here on
  * the logits of student and teacher lm_heads:
  *
- *   z = x_s w_s^T,  u = x_t w_t^T                       (logits, fp32)
+ *   z = x_s w_s^T,  u = x_t w_t^T                       (logits, never stored)
  *   ce, tvd, lse_s, lse_t, sigma per row               (as lx_ce_tvd_forward)
  *   G = k * (g_ce * d ce/dz + g_tvd * d tvd/dz)        (as lx_ce_tvd_backward)
  *   grad_x_s = G w_s,  grad_w_s = G^T x_s
  *
- * Rows are processed in chunks of chunk_rows; a chunk's logits and G live in
- * the workspace only while it is processed.  The matrix products run on the
- * matrix cores through lx_gemm_bf16 (bf16 inputs, fp32 accumulation; its
- * first call on a device allocates hipBLASLt's handle and workspace); the
- * logits are kept in fp32 and G is rounded to bf16 (nearest even) before the
- * two gradient products.
+ * The products run on the matrix cores (this library's own MFMA kernels:
+ * bf16 operands, fp32 accumulation).  Logit tiles are reduced in registers
+ * as they are computed: a first pass over all tiles gives each row's
+ * log-sum-exps and target logit, a second (per chunk of chunk_rows rows)
+ * recomputes the same tiles, bit for bit, for the total variation and keeps,
+ * for the gradient, 2^15 * p as binary16 with the sign of p - q and a tie bit
+ * per logit; G is formed from them in bf16 (rounded to nearest even; relative
+ * precision 2^-8 + 2^-10, the binary16 p included) and enters the two gradient
+ * products.  Nothing is allocated: every byte of scratch is in the caller's
+ * workspace.
  */
 
 /*
@@ -413,18 +423,23 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  *          must be a multiple of 8, lda and ldb multiples of 8 no smaller than
  *          that dimension and at most 2^22, A and B 16-byte aligned, C 4-byte aligned;
  *          1 <= M, N, K <= 2^31 - 1.  C must not overlap A or B.
- * Runs as one hipBLASLt matmul.  The first call on a device creates that
- * device's hipBLASLt handle and allocates a 64 MiB workspace for it (device
- * memory, kept until the process ends); the algorithm chosen for a shape is
- * cached.  Calls from several host threads are serialised per device.
+ * One launch of the library's MFMA kernel (256 x 256 tiles, fp32
+ * accumulation); it allocates nothing and keeps no state.  Operands
+ * contiguous along K are the fast layout.
  * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS, LX_ERR_HIP.
  */
 lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const void* B, int64_t ldb,
                        int b_k_contiguous, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        int accumulate, void* stream);
 
-/* Bytes of workspace lx_ce_tvd_linear_forward_backward needs (0 when BT == 0). */
-size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, int64_t chunk_rows);
+/*
+ * Bytes of workspace lx_ce_tvd_linear_forward_backward needs (0 when BT == 0 or
+ * for arguments it would reject): per-tile partials of every row (about 20 B
+ * per 128 logits with a teacher), and per chunk of rows 2 bytes of binary16 p
+ * plus a tie bit per logit (G in place) and 2 bytes per logit of G^T, plus
+ * w_s^T (V * H_s * 2 bytes) and the chunk's x_s^T.
+ */
+size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int64_t H_s, int has_teacher, int64_t chunk_rows);
 
 /*
  * Inputs : x_s bf16 (BT, H_s) and w_s bf16 (V, H_s), row-major; x_t bf16
@@ -436,9 +451,9 @@ size_t lx_ce_tvd_linear_workspace_bytes(int64_t BT, int64_t V, int has_teacher, 
  *          (V, H_s), each optional (NULL: not computed), both OVERWRITTEN.
  *          g_ce, g_tvd, g_scale as lx_ce_tvd_backward.  No output may overlap
  *          an input, another output or the workspace.
- * Workspace: at least lx_ce_tvd_linear_workspace_bytes(BT, V, teacher != NULL,
- *          chunk_rows) bytes, 256-byte aligned: about chunk_rows * V * 10
- *          bytes with a teacher (fp32 logits of both, bf16 G), 6 without.
+ * Workspace: at least lx_ce_tvd_linear_workspace_bytes(BT, V, H_s, teacher !=
+ *          NULL, chunk_rows) bytes, 256-byte aligned, contents ignored and
+ *          clobbered.
  * Errors : LX_ERR_INVALID_ARG (shapes, alignment, chunk_rows < 1),
  *          LX_ERR_ALIAS, LX_ERR_WORKSPACE, LX_ERR_HIP.
  */

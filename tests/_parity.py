@@ -186,11 +186,15 @@ def _row_vec(g, R):
 
 
 def check_grad(g_gpu: np.ndarray, g_bits: np.ndarray, z_raw, u_raw, target, ignore_index, g_ce, g_tvd, label="",
-               rel=G_REL, fmt="bf16", sigma_gpu=None, stats=None, ref=None, pq=None, sigma_ref=None):
+               rel=G_REL, fmt="bf16", sigma_gpu=None, stats=None, ref=None, pq=None, sigma_ref=None,
+               stated_rel=G_REL):
     """g_gpu: float64 view of the device gradient; g_bits: its raw bits.  g_ce and
     g_tvd are the upstream gradients of each row as applied (scalars or per-row
     arrays).  rel: the relative part of the scaled bound (G_REL_P16 for the
-    one-pass kernels).  fmt: the gradient's storage type ("f16" adds F16_FLOOR).
+    one-pass kernels).  stated_rel: the relative part of the stated bound (2^-8;
+    the lm_head path's G, an intermediate of its products formed from binary16
+    p, is held to G_REL_P16 there too).  fmt: the gradient's storage type ("f16"
+    adds F16_FLOOR).
     sigma_gpu: the sigma [R] the same kernel computed (optional): then it is held
     to 1e-5 against the oracle's sigma for the branch the gradient took.
     ref, pq, sigma_ref: the oracle gradient of these rows, their (p, q) and the
@@ -269,7 +273,7 @@ def check_grad(g_gpu: np.ndarray, g_bits: np.ndarray, z_raw, u_raw, target, igno
         # sigma's error reaches every element of the row through beta * p * (sigma - sigma_branch)
         widen[vi] += np.abs(beta) * p * ds[:, None]
     err = np.abs(g_gpu - ref)
-    tol_ns = G_REL * np.abs(ref) + G_ABS + widen
+    tol_ns = stated_rel * np.abs(ref) + G_ABS + widen
     tol_u = rel * np.abs(ref) + floor + widen
     st["grad_err/tol"] = float(np.max(err / np.maximum(tol_ns, 1e-300))) if err.size else 0.0
     st["grad_err/tol_scaled"] = float(np.max(err / np.maximum(tol_u, 1e-300))) if err.size else 0.0

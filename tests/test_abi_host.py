@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert lx.lx_abi_version() == 6
+    assert lx.lx_abi_version() == 7
     for code, name in ((0, "LX_OK"), (1, "LX_ERR_INVALID_ARG"), (2, "LX_ERR_UNSUPPORTED_DTYPE"),
                        (3, "LX_ERR_ALIAS"), (4, "LX_ERR_WORKSPACE"), (5, "LX_ERR_HIP"), (6, "LX_ERR_TOO_LARGE")):
         assert lx.lx_status_string(code) == name
@@ -312,12 +312,18 @@ def test_gemm_validation():
 
 def test_linear_validation():
     f = L.lx_ce_tvd_linear_forward_backward
-    ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 1, 128)
-    # fp32 logits of both lm_heads (2 x 4 B) and bf16 G per element of a 128-row chunk, plus the forward's share
-    assert ws_need >= 128 * 8200 * 10
-    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 0, 128) < ws_need
-    assert lx.lx_ce_tvd_linear_workspace_bytes(0, 8200, 1, 128) == 0
-    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 1, 0) == 0
+    ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 136, 1, 128)
+    # per logit of a 128-row chunk: binary16 p (then G) and the bf16 transpose of G (2 + 2 B) and a tie bit;
+    # besides: the transposed w (V x 136 bf16) and chunk of x, per-tile partials and the target logits.
+    # No logit of either lm_head is stored.
+    per_logit = 128 * 8200
+    assert per_logit * 4 <= ws_need
+    assert ws_need <= per_logit * (4 + 1 / 8) + 8200 * 136 * 2 + 136 * 128 * 2 + 300 * 4 * (1 + 5 * 33) + 128 * 8 * 65 + 4096
+    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 136, 0, 128) < ws_need
+    ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 64, 1, 128)  # the calls below: H = 64
+    assert lx.lx_ce_tvd_linear_workspace_bytes(0, 8200, 136, 1, 128) == 0
+    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 136, 1, 0) == 0
+    assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 0, 1, 128) == 0
 
     def call(xs=A, ws=A * 2, Hs=64, xt=A * 3, wt=A * 4, Ht=64, t=A * 5, BT=300, V=8200, ce=A * 6,
              tvd=A * 6 + 4096, lse_s=A * 6 + 8192, lse_t=A * 6 + 12288, sigma=A * 6 + 16384, gx=A * 7, gw=A * 8,
