@@ -8,13 +8,14 @@
 // For student hidden states X_s (BT, H_s), student weight W_s (V, H_s) and
 // teacher X_t, W_t, with logits z = X_s W_s^T and u = X_t W_t^T:
 //
-//   pass 1 (stats)  every 256 x 128 tile of z and u is computed on the matrix
-//                   cores and reduced in registers to per-row (max, sum-exp)
-//                   partials of z and of u, plus z at the target column when
-//                   the tile holds it; the tiles' partials are merged in tile
-//                   order (the vocabulary-parallel merge: each tile is a
-//                   column shard) -> lse_s, lse_t, ce;
-//   pass 2 (TV)     the same tiles are computed again and reduced to per-row
+//   pass 1 (stats)  every 256 x 256 tile of z (then of u) is computed on the
+//                   matrix cores and reduced in registers to per-row (max,
+//                   sum-exp) partials; the target logit z_t = x . w_t comes
+//                   from a per-row dot product; the tiles' partials are merged
+//                   in tile order (the vocabulary-parallel merge: each tile is
+//                   a column shard) -> lse_s, lse_t, ce;
+//   pass 2 (TV)     256 x 128 tiles of z and u together are computed again and
+//                   reduced to per-row
 //                   (sum |p - q|, sum p * sign(p - q)) partials, merged in tile
 //                   order -> tvd, sigma; when gradients are wanted the pass also
 //                   writes 2^15 p as binary16 with the sign of p - q in its sign
@@ -28,8 +29,8 @@
 //                   along K.
 //
 // z and u never reach memory: each pass recomputes its tiles from X and W
-// (the same kernel, the same accumulation order, so bit-identical logits in
-// both passes).  Rows go in chunks for pass 2 and the gradients; what a chunk
+// (every element is accumulated over k in the same order by the same main
+// loop, whatever the tile shape, so both passes see bit-identical logits).  Rows go in chunks for pass 2 and the gradients; what a chunk
 // keeps in the workspace is 2 bytes of binary16 p and 1 bit per logit
 // (becoming G), the transposed G (2 bytes per logit), and O(rows x V / 128)
 // partials.
@@ -45,13 +46,10 @@ namespace {
 
 using mm::f32x16_t;
 
-// K-slice stages in LDS: 256 x 256 tiles take 32 KB a stage, the dual 256 x
-// 128 tiles 24 KB; with 4 and 6 stages each keeps 3 and 5 slices in flight
-// (about 3000 and 2500 cycles of matrix-core time to cover a load's latency).
-constexpr int kStages = 4;
-constexpr int kStagesDual = 6;
-constexpr int kLds = kStages * 32768;
-constexpr int kLdsDual = kStagesDual * (16384 + 8192);
+// LDS of the main loop: 2 stages of a 64-k slice, 64 KB each for 256 x 256
+// tiles and 48 KB for the dual 256 x 128 tiles.
+constexpr int kLds = 2 * 65536;
+constexpr int kLdsDual = 2 * (32768 + 16384);
 
 // ---------------------------------------------------------------- plain products (fp32 C)
 
@@ -74,11 +72,13 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+  mm::pin_scalar(C);
+  mm::pin_scalar(ldc);
   mm::SliceLoader<AK, 256> la;
   mm::SliceLoader<BK, 256> lb;
   la.init(A, lda, a_end, M, K, m0, wave);
   lb.init(B, ldb, b_end, N, K, n0, wave);
-  mm::mainloop<AK, BK, 4, 256, kStages>(acc, lds, la, lb, K, wm, wn, wave);
+  mm::mainloop<AK, BK, 4, 256>(acc, lds, la, lb, K, wm, wn, wave);
   // (accumulating: the 16 values of a 32 x 32 tile are all read before any is
   // written back, so the reads are in flight together)
 #pragma unroll
@@ -138,6 +138,44 @@ struct DualArgs {
   int tiles_m, tiles_n;
 };
 
+// Reductions over the 32 lanes of each half-wave (the 32 columns of one
+// accumulator row), on the vector ALU: two quad permutations and two rotations
+// inside each row of 16 lanes (DPP), then the gfx950 swap of rows 0 <-> 1 and
+// 2 <-> 3.  Every lane ends with the reduction of its half; the sum's
+// association order is fixed, so the half's first lane always sees the same
+// value for the same data.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap16(float v, float* other) {
+  const unsigned u = __float_as_uint(v);
+  const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  // the elements go through scalars: this compiler's __builtin_bit_cast of an
+  // element of the returned pair reads element 0 whatever the index
+  const unsigned lo = pr[0], hi = pr[1];
+  *other = __uint_as_float(hi);
+  return __uint_as_float(lo);
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror 4
+  v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror 8
+  float hi;
+  const float lo = swap16(v, &hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float half_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x124>(v);
+  v += dpp_mov<0x128>(v);
+  float hi;
+  const float lo = swap16(v, &hi);
+  return lo + hi;
+}
+
 // Per-row (max, sum-exp) of one tensor's tile values for the wave's 128 rows x
 // 32 NJ columns, merged with the other wave of the same rows through LDS: the
 // wave's result for tile row `lr` lands in red[(wn != 0) * 256 + lr]
@@ -157,8 +195,7 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
         v[j] = acc[i][j][r];
         m = ok ? fmaxf(m, v[j]) : m;
       }
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      m = half_max(m);
       const float nb = -(m * kLog2e);
       float s = 0.0f;
 #pragma unroll
@@ -166,8 +203,7 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
         const bool ok = n0 + wn + 32 * j + (lane & 31) < V;
         s += ok ? exp2_hw(__builtin_fmaf(v[j], kLog2e, nb)) : 0.0f;
       }
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+      s = half_sum(s);
       if ((lane & 31) == 0) red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(r, lane)] = Lse{m, s};
     }
   }
@@ -176,15 +212,14 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
 // Pass 1 for one tensor: a 256 x 256 tile of its logits (the plain product's
 // main loop and tile), reduced to per-row (max, sum-exp) over the tile's
 // columns, written to slots `slot`, `slot + 1` of the row's record in
-// partials [tiles_n][rows][P]; the student's launch (slot 0) also writes the
-// target logit (or +0) to slot P - 1.  The teacher's launch fills slots 2, 3 of
-// the same records.
+// partials [tiles_n][rows][P]; the student's launch (slot 0) also writes +0
+// to slot P - 1 (the target logit's, filled for the target's tile by
+// target_logit_kernel).  The teacher's launch fills slots 2, 3 of the same
+// records.
 struct StatsArgs {
   const uint16_t *x, *w;
   int64_t H;
   int rows, V;
-  const int64_t* target;
-  int64_t ignore_index;
   float* partials;
   int P, slot;
   int tiles_m, tiles_n;
@@ -209,37 +244,13 @@ void lm_stats_kernel(StatsArgs a) {
     mm::SliceLoader<true, 256> lb;
     la.init(a.x, a.H, 2 * ((int64_t)(a.rows - 1) * a.H + a.H), a.rows, (int)a.H, m0, wave);
     lb.init(a.w, a.H, 2 * ((int64_t)(a.V - 1) * a.H + a.H), a.V, (int)a.H, n0, wave);
-    mm::mainloop<true, true, 4, 256, kStages>(acc, lds, la, lb, (int)a.H, wm, wn, wave);
+    mm::pin_scalar(a.partials);
+    mm::pin_scalar(a.P);
+    mm::pin_scalar(a.slot);
+    mm::mainloop<true, true, 4, 256>(acc, lds, la, lb, (int)a.H, wm, wn, wave);
   }
   const int tid = tid_x();
-  const bool student = a.slot == 0;
-  int* tcol = reinterpret_cast<int*>(lds);
-  float* ztp = reinterpret_cast<float*>(lds + 1024);  // [2][256]
-  Lse* red = reinterpret_cast<Lse*>(lds + 4096);      // [2][256]
-  if (student) {
-    const int m = m0 + tid;
-    int c = -1;
-    if (m < a.rows) {
-      const int64_t t = a.target[m];
-      if (t != a.ignore_index && t >= n0 && t < n0 + 256 && t < a.V) c = (int)(t - n0);
-    }
-    tcol[tid] = c;
-    ztp[tid] = 0.0f;
-    ztp[256 + tid] = 0.0f;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm + 32 * i + mm::acc_row(r, lane);
-        const int c = tcol[lr] - wn;
-        if (c >= 0 && c < 128 && (c & 31) == (lane & 31)) {
-          const int jj = c >> 5;
-          ztp[(wn != 0) * 256 + lr] = jj == 0 ? acc[i][0][r] : jj == 1 ? acc[i][1][r] : jj == 2 ? acc[i][2][r] : acc[i][3][r];
-        }
-      }
-    }
-  }
+  Lse* red = reinterpret_cast<Lse*>(lds);  // [2][256]
   tile_lse<4>(acc, wm, wn, n0, a.V, lane, red);
   __syncthreads();
   const int m = m0 + tid;
@@ -249,8 +260,39 @@ void lm_stats_kernel(StatsArgs a) {
     lse_merge(f, red[256 + tid]);
     o[a.slot] = f.m;
     o[a.slot + 1] = f.s;
-    if (student) o[a.P - 1] = ztp[tid] + ztp[256 + tid];  // one of the two is the logit, the other +0
+    if (a.slot == 0) o[a.P - 1] = 0.0f;  // the target-logit kernel fills the target tile's slot
   }
+}
+
+// The target logit z_t = x_m . w_t of every row with a target in [0, V),
+// one wave per row: products of bf16 pairs are exact in fp32 and summed in
+// fp32 (lanes take 16-byte pieces of the row in turn, then a fixed-order
+// reduction across the wave).  It goes into the last slot of the record of
+// the 256-column tile that holds column t, where the stats launches left +0.
+__global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w, int64_t H, int rows,
+                                                           int64_t V, const int64_t* __restrict__ target,
+                                                           int64_t ignore_index, float* __restrict__ partials, int P) {
+  const int lane = tid_x() & 63;
+  const int64_t m = (int64_t)bid_x() * 4 + (tid_x() >> 6);
+  if (m >= rows) return;
+  const int64_t t = target[m];
+  if (t == ignore_index || t < 0 || t >= V) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + m * H);
+  const uint4* wr = reinterpret_cast<const uint4*>(w + t * H);
+  float acc = 0.0f;
+  for (int64_t c = lane; c < H / 8; c += 64) {
+    const uint4 a = xr[c], b = wr[c];
+    const unsigned av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(bv[e] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(bv[e] & 0xffff0000u), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 32, 64);
+  acc = half_sum(acc);
+  if (lane == 0) partials[((t >> 8) * rows + m) * P + (P - 1)] = acc;
 }
 
 // One pass over the logit tiles: the products of a 256 x 128 tile of z (and
@@ -280,14 +322,14 @@ void lm_tile_kernel(DualArgs a) {
     mm::SliceLoader<true, 128> lb;
     la.init(a.xs, a.Hs, 2 * ((int64_t)(a.rows - 1) * a.Hs + a.Hs), a.rows, (int)a.Hs, m0, wave);
     lb.init(a.ws, a.Hs, 2 * ((int64_t)(a.V - 1) * a.Hs + a.Hs), a.V, (int)a.Hs, n0, wave);
-    mm::mainloop<true, true, 2, 128, kStagesDual>(az, lds, la, lb, (int)a.Hs, wm, wn, wave);
+    mm::mainloop<true, true, 2, 128>(az, lds, la, lb, (int)a.Hs, wm, wn, wave);
   }
   if (TEACHER) {
     mm::SliceLoader<true, 256> la;
     mm::SliceLoader<true, 128> lb;
     la.init(a.xt, a.Ht, 2 * ((int64_t)(a.rows - 1) * a.Ht + a.Ht), a.rows, (int)a.Ht, m0, wave);
     lb.init(a.wt, a.Ht, 2 * ((int64_t)(a.V - 1) * a.Ht + a.Ht), a.V, (int)a.Ht, n0, wave);
-    mm::mainloop<true, true, 2, 128, kStagesDual>(au, lds, la, lb, (int)a.Ht, wm, wn, wave);
+    mm::mainloop<true, true, 2, 128>(au, lds, la, lb, (int)a.Ht, wm, wn, wave);
   }
   // LDS is free again (every wave is past the main loops' final barrier)
   const int tid = tid_x();
@@ -393,11 +435,8 @@ void lm_tile_kernel(DualArgs a) {
           }
         }
         if (TEACHER) {
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) {
-            S += __shfl_xor(S, off, 64);
-            Q += __shfl_xor(Q, off, 64);
-          }
+          S = half_sum(S);
+          Q = half_sum(Q);
           if ((lane & 31) == 0) {
             red[((wn != 0) * 256 + lr) * 2] = S;
             red[((wn != 0) * 256 + lr) * 2 + 1] = Q;
@@ -669,8 +708,8 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
   {
     const int stiles_n = (int)((V + 255) / 256);
     StatsArgs sa{};
-    sa.x = a.x_s; sa.w = a.w_s; sa.H = a.H_s; sa.rows = (int)a.BT; sa.V = (int)V; sa.target = a.target;
-    sa.ignore_index = a.ignore_index; sa.partials = w.stats; sa.P = teacher ? 5 : 3; sa.slot = 0;
+    sa.x = a.x_s; sa.w = a.w_s; sa.H = a.H_s; sa.rows = (int)a.BT; sa.V = (int)V;
+    sa.partials = w.stats; sa.P = teacher ? 5 : 3; sa.slot = 0;
     sa.tiles_m = (int)((a.BT + mm::kBM - 1) / mm::kBM);
     sa.tiles_n = stiles_n;
     (void)hipGetLastError();
@@ -683,6 +722,9 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
       lm_stats_kernel<<<dim3(grid), dim3(mm::kThreads), 0, st>>>(sa);
       if ((e = hipGetLastError())) return e;
     }
+    target_logit_kernel<<<dim3((unsigned)((a.BT + 3) / 4)), dim3(256), 0, st>>>(
+        a.x_s, a.w_s, a.H_s, (int)a.BT, V, a.target, a.ignore_index, w.stats, sa.P);
+    if ((e = hipGetLastError())) return e;
     if ((e = launch_vp_merge_stats_zt(w.stats, stiles_n, a.target, a.BT, V, a.ignore_index, teacher, a.ce, a.lse_s,
                                       teacher ? a.lse_t : nullptr, w.zt, st)))
       return e;
