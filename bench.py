@@ -21,7 +21,8 @@ timed reps.  The practical ceilings are the library's own reference streams
 JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
-                    [--no-linear] [--no-vocab-parallel] [--no-ex]
+                    [--no-linear] [--no-vocab-parallel] [--no-ex] [--no-ceiling]
+    python bench.py --only-linear [--steps K] [--warmup W]    (the lm_head leg alone)
 """
 from __future__ import annotations
 
@@ -293,10 +294,22 @@ def run_linear(timer, steps, warmup, BT=8192, V=151936, H=4096, chunk_rows=8192)
         X, Wd, Xt, Wt, tg, II, ce, tvd, lse_s, lse_t, sigma, gx, gw, 1.0, 1.0, inv, chunk_rows, ws, s)],
         max(3, steps // 4), max(1, warmup // 2))
     flops = 2.0 * BT * V * H * 4  # student and teacher logits, grad of x, grad of w
+    # the kernels run 6 products of that size: each of the two loss passes recomputes
+    # the logits of both heads, since no logit is stored
+    flops_run = 2.0 * BT * V * H * 6
     out = {"shape": f"BT={BT} V={V} H_s=H_t={H} chunk_rows={chunk_rows}", "workspace_bytes": int(wsb),
+           "workspace_bytes_per_chunk_logit": round(wsb / (min(chunk_rows, BT) * V), 2),
            "ms": round(ms, 3), "tokens_per_s": round(BT / ms * 1e3, 1), "TFLOPs": round(flops / ms / 1e9, 1),
-           "pct_mfma_peak": round(100.0 * flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
-    del ws, gx, gw
+           "pct_mfma_peak": round(100.0 * flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+           "TFLOPs_executed": round(flops_run / ms / 1e9, 1),
+           "pct_mfma_peak_executed": round(100.0 * flops_run / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+    # the vendor library's product at the logits shape, same operands, as a reference
+    # for the library's own product kernel (context only: nothing above uses it)
+    C = torch.empty((BT, V), dtype=torch.bfloat16, device=dev)
+    (vm,), _, _ = timer.run([lambda: torch.matmul(X, Wd.t(), out=C)], max(3, steps // 4), max(1, warmup // 2))
+    out["vendor_logits_product_ms"] = round(vm, 3)
+    out["vendor_logits_product_pct_mfma_peak"] = round(100.0 * 2.0 * BT * V * H / vm / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)
+    del ws, gx, gw, C
     return out
 
 
@@ -427,6 +440,8 @@ def main():
     ap.add_argument("--no-vocab-parallel", action="store_true")
     ap.add_argument("--no-ex", action="store_true", help="skip the binary16 / strided / per-row one-pass legs")
     ap.add_argument("--no-linear", action="store_true", help="skip the lm_head product + loss leg")
+    ap.add_argument("--only-linear", action="store_true",
+                    help="run only the lm_head product + loss leg and print its JSON object (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
@@ -440,6 +455,9 @@ def main():
     dev = torch.device("cuda:0")
     timer = Timer(dev)
     K, Wm = args.steps, args.warmup
+    if args.only_linear:
+        print(json.dumps({"linear": run_linear(timer, K, Wm)}), flush=True)
+        return
     w, zs, us, tg, n_valid = load_workload("train", dev)
     head = measure(timer, w, zs, us, tg, n_valid, K, Wm, True)
     print(f"[bench] train ce_tvd: one pass {head['one_pass']['ms_per_step']:.4f} ms/step, separate "
