@@ -402,13 +402,16 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  * The products run on the matrix cores (this library's own MFMA kernels:
  * bf16 operands, fp32 accumulation).  Logit tiles are reduced in registers
  * as they are computed: a first pass over all tiles gives each row's
- * log-sum-exps and target logit, a second (per chunk of chunk_rows rows)
+ * log-sum-exps (a per-row dot product gives its target logit), a second (per
+ * chunk of chunk_rows rows)
  * recomputes the same tiles, bit for bit, for the total variation and keeps,
  * for the gradient, 2^15 * p as binary16 with the sign of p - q and a tie bit
  * per logit; G is formed from them in bf16 (rounded to nearest even; relative
  * precision 2^-8 + 2^-10, the binary16 p included) and enters the two gradient
  * products.  Nothing is allocated: every byte of scratch is in the caller's
- * workspace.
+ * workspace.  A target outside [0, V) that is not ignore_index makes its row
+ * of G NaN: ce and grad_x_s of that row are NaN, and since grad_w_s sums over
+ * the rows, so is every element of grad_w_s.
  */
 
 /*
@@ -434,8 +437,9 @@ lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const voi
 
 /*
  * Bytes of workspace lx_ce_tvd_linear_forward_backward needs (0 when BT == 0 or
- * for arguments it would reject): per-tile partials of every row (about 20 B
- * per 128 logits with a teacher), and per chunk of rows 2 bytes of binary16 p
+ * for arguments it would reject): per-tile partials of every row (20 B per
+ * 256 logits with a teacher, 12 without) and of the chunk's rows (8 B per
+ * 128 logits), and per chunk of rows 2 bytes of binary16 p
  * plus a tie bit per logit (G in place) and 2 bytes per logit of G^T, plus
  * w_s^T (V * H_s * 2 bytes) and the chunk's x_s^T.
  */

@@ -149,10 +149,11 @@ def grad_bounds(ref, x_s, w_s, t, teacher, g_tvd, with_w=True):
 @pytest.mark.parametrize("BT,V,H_s,H_t,chunk", [(300, 8200, 136, 200, 300), (300, 8200, 136, 200, 128),
                                                 (600, 4096, 64, 96, 600), (600, 4096, 64, 96, 1000),
                                                 (37, 2056, 256, 128, 16), (12, 2056, 256, 128, 2),
-                                                (530, 1160, 1000, 520, 530)],
+                                                (530, 1160, 1000, 520, 530), (5, 264, 8, 16, 5),
+                                                (3, 8, 24, 8, 1)],
                          ids=["300x8200_one_chunk", "300x8200_chunks_128", "600x4096",
                               "600x4096_chunk_above_rows", "37x2056_chunks_16", "12x2056_chunks_2",
-                              "530x1160_ragged_tiles"])
+                              "530x1160_ragged_tiles", "5x264_hidden_8_16", "3x8_hidden_24_8_chunks_1"])
 def test_linear_matches_the_oracle(BT, V, H_s, H_t, chunk, teacher):
     x_s, w_s, x_t, w_t, t = W.linear_inputs(BT, V, H_s, H_t if teacher else None, seed=BT + V + H_s)
     g_ce, g_tvd = 0.5, 1.5
@@ -191,6 +192,31 @@ def test_linear_one_pass_gradient_elementwise(BT, V, g_ce, g_tvd):
     assert np.all(G[~valid] == 0.0), f"{label}: ignored rows must have a zero gradient"
     bits = np.where(valid[:, None], bits32(G.astype(np.float32)), 0)
     check_grad(G, bits, z, u, t, II, g_ce, g_tvd, label, rel=G_REL_P16, stated_rel=G_REL_P16, sigma_gpu=out["sigma"])
+
+
+def test_linear_out_of_range_target_poisons_its_row_and_grad_w():
+    """A target outside [0, V) that is not ignore_index: that row's ce and its
+    grad_x row are NaN and, through the sum over rows, every element of grad_w;
+    every other row matches the oracle run with that row ignored."""
+    BT, V, H = 40, 264, 16
+    x_s, w_s, x_t, w_t, t = W.linear_inputs(BT, V, H, H, seed=13)
+    bad = 7
+    t = t.copy()
+    t[bad] = V + 5
+    announce("linear: out-of-range target row 7")
+    out, gx, gw = run_linear(x_s, w_s, x_t, w_t, t, 0.5, 1.5, BT)
+    assert np.isnan(out["ce"][bad])
+    assert np.all(np.isnan(gx.cpu().numpy()[bad]))
+    assert np.all(np.isnan(gw.cpu().numpy()))
+    t_ref = t.copy()
+    t_ref[bad] = II
+    ref = oracle.linear_forward_backward(x_s, w_s, x_t, w_t, t_ref, II, 0.5, 1.5)
+    keep = np.arange(BT) != bad
+    check_forward({k: v[keep] for k, v in out.items()}, ref["z"][keep], ref["u"][keep], t_ref[keep], II,
+                  "linear out-of-range target, other rows")
+    bx, _ = grad_bounds(ref, x_s, w_s, t_ref, True, 1.5, with_w=False)
+    ex = np.abs(gx.cpu().numpy()[keep] - ref["grad_x_s"][keep])
+    assert np.all(ex <= bx[keep]), f"grad_x of the other rows: max excess {np.max(ex / bx[keep])}"
 
 
 def test_linear_forward_only_and_device_scale():
