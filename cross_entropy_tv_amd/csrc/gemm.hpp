@@ -23,6 +23,12 @@ struct GemmArgs {
   int64_t ldc;
   int64_t M, N, K;
   bool a_kc, b_kc, accumulate;
+  // split-K: splits > 1 cuts K into `splits` ranges of whole 64-k slices; each
+  // range's product goes to partials[s] (M x N, row stride N, fp32) and a second
+  // kernel adds them to C in split order (deterministic).  partials: splits * M * N
+  // floats of scratch.
+  int splits = 1;
+  float* partials = nullptr;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);

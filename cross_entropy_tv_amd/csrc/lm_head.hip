@@ -55,14 +55,31 @@ constexpr int kLdsDual = 2 * (32768 + 16384);
 
 // C[m][n] (+)= sum_k A(m, k) B(n, k): 256 x 256 tiles, one workgroup of 4 waves
 // per compute unit (the accumulators take all 256 AGPRs).
+//
+// Split-K (splits > 1): the N sweep runs over tiles_n * splits virtual tiles, the
+// splits of one output tile next to each other; split s takes k in [s kslice,
+// min(K, (s + 1) kslice)) (kslice a multiple of the 64-k slice) by moving the
+// operands' bases to its first k, and writes its product (ACC = false) to
+// C + s * split_stride.
 template <bool AK, bool BK, bool ACC>
 __global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end, const uint16_t* __restrict__ B,
                       int64_t ldb, int64_t b_end, float* __restrict__ C, int64_t ldc, int M, int N, int K,
-                      int tiles_m, int tiles_n) {
+                      int tiles_m, int tiles_n, int splits, int kslice, int64_t split_stride) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   int tm, tn;
-  if (!mm::tile_coords(tiles_m, tiles_n, tm, tn)) return;
+  if (!mm::tile_coords(tiles_m, tiles_n * splits, tm, tn)) return;
+  if (splits > 1) {
+    const int s = tn % splits;
+    tn /= splits;
+    const int k0 = s * kslice;
+    A += AK ? (int64_t)k0 : (int64_t)k0 * lda;
+    B += BK ? (int64_t)k0 : (int64_t)k0 * ldb;
+    a_end -= 2 * (AK ? (int64_t)k0 : (int64_t)k0 * lda);
+    b_end -= 2 * (BK ? (int64_t)k0 : (int64_t)k0 * ldb);
+    K = min(K - k0, kslice);
+    C += s * split_stride;
+  }
   const int m0 = tm * mm::kBM, n0 = tn * 256;
   const int lane = tid_x() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
@@ -112,7 +129,44 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t st) {
   const int64_t b_end = 2 * (BK ? (g.N - 1) * g.ldb + g.K : (g.K - 1) * g.ldb + g.N);
   hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, ACC>), dim3(mm::grid_for(tiles_m, tiles_n)), dim3(mm::kThreads), 0, st,
                      g.A, g.lda, a_end, g.B, g.ldb, b_end, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, tiles_m,
-                     tiles_n);
+                     tiles_n, 1, (int)g.K, (int64_t)0);
+  return hipGetLastError();
+}
+
+// C (+)= sum over s in order of partials[s] (M x N, row stride N).
+template <bool ACC>
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ P, int splits, int64_t M, int64_t N,
+                                                        float* __restrict__ C, int64_t ldc) {
+  const int64_t total = M * N;
+  const int64_t plane = M * N;
+  for (int64_t i = (int64_t)bid_x() * 256 + tid_x(); i < total; i += (int64_t)nblocks_x() * 256) {
+    const int64_t m = i / N, n = i - m * N;
+    float v = ACC ? C[m * ldc + n] : 0.0f;
+    for (int s = 0; s < splits; ++s) v += P[s * plane + i];
+    C[m * ldc + n] = v;
+  }
+}
+
+template <bool AK, bool BK>
+hipError_t launch_gemm_split(const GemmArgs& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + mm::kBM - 1) / mm::kBM);
+  const int tiles_n = (int)((g.N + 255) / 256);
+  const int64_t a_end = 2 * (AK ? (g.M - 1) * g.lda + g.K : (g.K - 1) * g.lda + g.M);
+  const int64_t b_end = 2 * (BK ? (g.N - 1) * g.ldb + g.K : (g.K - 1) * g.ldb + g.N);
+  const int64_t per = (g.K + g.splits - 1) / g.splits;
+  const int kslice = (int)((per + mm::kBK - 1) / mm::kBK * mm::kBK);
+  const int splits = (int)((g.K + kslice - 1) / kslice);  // no empty split
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, false>), dim3(mm::grid_for(tiles_m, tiles_n * splits)),
+                     dim3(mm::kThreads), 0, st, g.A, g.lda, a_end, g.B, g.ldb, b_end, g.partials, g.N, (int)g.M,
+                     (int)g.N, (int)g.K, tiles_m, tiles_n, splits, kslice, g.M * g.N);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int64_t total = g.M * g.N;
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  if (g.accumulate)
+    hipLaunchKernelGGL(split_sum_kernel<true>, dim3(blocks), dim3(256), 0, st, g.partials, splits, g.M, g.N, g.C, g.ldc);
+  else
+    hipLaunchKernelGGL(split_sum_kernel<false>, dim3(blocks), dim3(256), 0, st, g.partials, splits, g.M, g.N, g.C,
+                       g.ldc);
   return hipGetLastError();
 }
 
@@ -646,9 +700,25 @@ struct LinearWs {
   uint16_t* gt;      // (V, ldr): G^T
   uint16_t* wst;     // (H_s, V): W_s^T
   uint16_t* xst;     // (H_s, ldr): X_s[chunk]^T
+  float* gxp;        // [gx_splits][chunk][H_s]: split-K partials of grad_x (gx_splits > 1)
+  int gx_splits;
   int64_t ldr;
   size_t bytes;
 };
+
+// Splits of grad_x = G W_s over the vocabulary for a chunk of `rows` rows: a chunk
+// whose product has fewer than two 256 x 256 tiles per compute unit would leave
+// compute units idle through its whole (V-long) K loop, so K is cut into up to 8
+// ranges of at least 2048 (whole 64-k slices each), the partials summed in order.
+int gx_splits(int64_t rows, int64_t Hs, int64_t V) {
+  const int64_t tiles = ((rows + 255) / 256) * ((Hs + 255) / 256);
+  constexpr int64_t kWanted = 512;
+  if (tiles >= kWanted) return 1;
+  int64_t s = (kWanted + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > V / 2048) s = V / 2048;
+  return s < 1 ? 1 : (int)s;
+}
 
 LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs, bool teacher, bool gx, bool gw) {
   LinearWs w{};
@@ -671,6 +741,8 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs,
   w.gt = gw ? reinterpret_cast<uint16_t*>(take((size_t)V * w.ldr * 2)) : nullptr;
   w.wst = gx ? reinterpret_cast<uint16_t*>(take((size_t)Hs * V * 2)) : nullptr;
   w.xst = gw ? reinterpret_cast<uint16_t*>(take((size_t)Hs * w.ldr * 2)) : nullptr;
+  w.gx_splits = gx ? gx_splits(chunk, Hs, V) : 1;
+  w.gxp = w.gx_splits > 1 ? reinterpret_cast<float*>(take((size_t)w.gx_splits * chunk * Hs * 4)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -681,6 +753,10 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs,
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   (void)hipGetLastError();
+  if (g.splits > 1) {
+    if (!g.partials || !g.a_kc || !g.b_kc) return hipErrorInvalidValue;  // the lm_head path's layout only
+    return launch_gemm_split<true, true>(g, st);
+  }
   if (g.a_kc) {
     if (g.b_kc) return g.accumulate ? launch_gemm_t<true, true, true>(g, st) : launch_gemm_t<true, true, false>(g, st);
     return g.accumulate ? launch_gemm_t<true, false, true>(g, st) : launch_gemm_t<true, false, false>(g, st);
@@ -765,6 +841,8 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     if ((e = hipGetLastError())) return e;
     if (gx) {  // grad_x[chunk] = G W_s: M = rows, N = H_s, K = V
       GemmArgs p{w.p16, V, w.wst, V, a.grad_x_s + r0 * a.H_s, a.H_s, rows, a.H_s, V, true, true, false};
+      p.splits = w.gx_splits;  // sized for a full chunk; a shorter last chunk uses as many
+      p.partials = w.gxp;
       if ((e = launch_gemm_bf16(p, st))) return e;
     }
     if (gw) {  // grad_w (+)= G^T X_s[chunk]: M = V, N = H_s, K = rows
