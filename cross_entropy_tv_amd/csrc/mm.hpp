@@ -211,6 +211,17 @@ __device__ __forceinline__ void step(Frags<NJ>& f, f32x16_t (&acc)[4][NJ],
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a_cur[I], f.b_cur[j], acc[I][j], 0, 0, 0);
+  // issue order inside the group: each MFMA followed by up to two memory
+  // instructions (LDS reads and writes, global loads), so the in-order wave
+  // never holds several MFMAs back behind a burst of memory instructions
+  // (6-7% faster than letting the compiler put the group's memory
+  // instructions first)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100 | 0x200 | 0x020, 2, 0);  // LDS read / write, VMEM read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100 | 0x200 | 0x020, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
   if (I == 3) {
 #pragma unroll
