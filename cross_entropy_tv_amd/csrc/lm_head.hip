@@ -177,15 +177,13 @@ constexpr int kDualBN = 128;  // logit columns per tile (each of z and u)
 __host__ __device__ __forceinline__ int64_t tie_words(int64_t V) { return (V + 31) >> 5; }
 constexpr float kInvPqBiasG = 0x1p-15f;  // 2^-kPqBias
 
-enum class Epi { Stats, TV };
-
 struct DualArgs {
   const uint16_t *xs, *ws, *xt, *wt;  // bf16 X_s (rows, H_s), W_s (V, H_s), X_t, W_t (nullptr: CE-only)
   int64_t Hs, Ht;
   int rows, V;                        // this launch's rows (from row 0 of xs / xt) and the vocabulary
   const int64_t* target;              // target of row 0 of this launch
   int64_t ignore_index;
-  float* partials;                    // [tiles_n][rows][P] (Stats: P = 5 / 3; TV: 2)
+  float* partials;                    // [tiles_n][rows][2]: (S - Q, S) per tile
   const float *lse_s, *lse_t;         // TV: per row
   uint16_t* p16;                      // TV with gradients: binary16 2^15 p, (rows, V), or nullptr
   uint32_t* ties;                     // TV with gradients and a teacher: (rows, tie_words(V)) tie bits
@@ -349,10 +347,10 @@ __global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __res
   if (lane == 0) partials[((t >> 8) * rows + m) * P + (P - 1)] = acc;
 }
 
-// One pass over the logit tiles: the products of a 256 x 128 tile of z (and
-// u), then the epilogue of the pass.  Four waves, 2 x 2, each 128 x 64 of each
+// Pass 2 over the logit tiles: the products of a 256 x 128 tile of z (and u),
+// then the total-variation epilogue.  Four waves, 2 x 2, each 128 x 64 of each
 // tensor (4 x 2 MFMA accumulators per tensor: 128 + 128 AGPRs).
-template <Epi EPI, bool TEACHER, bool WRITE_P>
+template <bool TEACHER, bool WRITE_P>
 __global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
 void lm_tile_kernel(DualArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDual];
@@ -388,54 +386,7 @@ void lm_tile_kernel(DualArgs a) {
   // LDS is free again (every wave is past the main loops' final barrier)
   const int tid = tid_x();
 
-  if constexpr (EPI == Epi::Stats) {
-    // per tile row: its target column relative to the tile, or -1
-    int* tcol = reinterpret_cast<int*>(lds);
-    float* ztp = reinterpret_cast<float*>(lds + 1024);   // [2][256] target logit (or 0) per wave column
-    Lse* red_z = reinterpret_cast<Lse*>(lds + 4096);      // [2][256]
-    Lse* red_u = reinterpret_cast<Lse*>(lds + 8192);      // [2][256]
-    {
-      const int m = m0 + tid;
-      int c = -1;
-      if (m < a.rows) {
-        const int64_t t = a.target[m];
-        if (t != a.ignore_index && t >= n0 && t < n0 + kDualBN && t < a.V) c = (int)(t - n0);
-      }
-      tcol[tid] = c;
-      ztp[tid] = 0.0f;
-      ztp[256 + tid] = 0.0f;
-    }
-    __syncthreads();
-    // the target logit: the lane holding column tcol of the row takes it from its accumulators
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm + 32 * i + mm::acc_row(r, lane);
-        const int c = tcol[lr] - wn;
-        if (c >= 0 && c < 64 && (c & 31) == (lane & 31)) ztp[(wn != 0) * 256 + lr] = (c >> 5) ? az[i][1][r] : az[i][0][r];
-      }
-    }
-    tile_lse<2>(az, wm, wn, n0, a.V, lane, red_z);
-    if (TEACHER) tile_lse<2>(au, wm, wn, n0, a.V, lane, red_u);
-    __syncthreads();
-    const int m = m0 + tid;
-    if (m < a.rows) {
-      constexpr int P = TEACHER ? 5 : 3;
-      float* o = a.partials + ((int64_t)tn * a.rows + m) * P;
-      Lse fz = red_z[tid];
-      lse_merge(fz, red_z[256 + tid]);
-      o[0] = fz.m;
-      o[1] = fz.s;
-      if (TEACHER) {
-        Lse fu = red_u[tid];
-        lse_merge(fu, red_u[256 + tid]);
-        o[2] = fu.m;
-        o[3] = fu.s;
-      }
-      o[P - 1] = ztp[tid] + ztp[256 + tid];  // one of the two is the logit, the other +0
-    }
-  } else {
+  {
     // TV: p' = 2^15 p, q' = 2^15 q and s' = 2^-24 sign(p - q) from the arguments
     // a = x log2(e) - lse log2(e) + 15, exactly as the other TV kernels form them
     float* nbs = reinterpret_cast<float*>(lds);         // [256]
@@ -512,10 +463,10 @@ void lm_tile_kernel(DualArgs a) {
   }
 }
 
-template <Epi EPI, bool TEACHER, bool WRITE_P>
+template <bool TEACHER, bool WRITE_P>
 hipError_t launch_tiles(const DualArgs& a, hipStream_t st) {
   (void)hipGetLastError();
-  hipLaunchKernelGGL((lm_tile_kernel<EPI, TEACHER, WRITE_P>), dim3(mm::grid_for(a.tiles_m, a.tiles_n)),
+  hipLaunchKernelGGL((lm_tile_kernel<TEACHER, WRITE_P>), dim3(mm::grid_for(a.tiles_m, a.tiles_n)),
                      dim3(mm::kThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -821,12 +772,12 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     d.tiles_n = tiles_n;
     hipError_t e;
     if (teacher) {
-      e = grads ? launch_tiles<Epi::TV, true, true>(d, st) : launch_tiles<Epi::TV, true, false>(d, st);
+      e = grads ? launch_tiles<true, true>(d, st) : launch_tiles<true, false>(d, st);
       if (e) return e;
       if ((e = launch_vp_merge_tv(w.tv, tiles_n, a.target + r0, rows, a.ignore_index, a.tvd + r0, a.sigma + r0, st)))
         return e;
     } else {
-      if ((e = launch_tiles<Epi::TV, false, true>(d, st))) return e;  // binary16 p only
+      if ((e = launch_tiles<false, true>(d, st))) return e;  // binary16 p only
     }
     if (!grads) continue;
     // G (bf16, over the binary16 p) and G^T
