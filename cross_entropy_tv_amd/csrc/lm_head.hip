@@ -22,18 +22,18 @@
 //                   bit, and a bit per logit marking exact ties (sign 0);
 //   G               from those, the per-row sigma and the target logit:
 //                   G = k (g_ce (p - [v == t]) + g_tvd / 2 * p (s - sigma)), bf16
-//                   (rounded to nearest even), written over the binary16 p and
-//                   also transposed;
-//   grad_x = G W_s  and  grad_w = G^T X_s on the matrix cores, from W_s^T and
-//                   X_s^T so that both operands of every product are contiguous
-//                   along K.
+//                   (rounded to nearest even), written over the binary16 p;
+//   grad_x = G W_s  and  grad_w = G^T X_s on the matrix cores, reading G, W_s
+//                   and X_s as they lie (W_s in grad_x, and G and X_s in
+//                   grad_w, down their columns: the main loop's transposing
+//                   LDS reads), so nothing is transposed in memory.
 //
 // z and u never reach memory: each pass recomputes its tiles from X and W
 // (every element is accumulated over k in the same order by the same main
-// loop, whatever the tile shape, so both passes see bit-identical logits).  Rows go in chunks for pass 2 and the gradients; what a chunk
-// keeps in the workspace is 2 bytes of binary16 p and 1 bit per logit
-// (becoming G), the transposed G (2 bytes per logit), and O(rows x V / 128)
-// partials.
+// loop, whatever the tile shape, so both passes see bit-identical logits).
+// Rows go in chunks for pass 2 and the gradients; what a chunk keeps in the
+// workspace is 2 bytes of binary16 p and 1 bit per logit (becoming G) and
+// O(rows x V / 128) partials.
 #include "launch.hpp"
 #include "linear.hpp"
 #include "gemm.hpp"
@@ -483,8 +483,6 @@ struct GformArgs {
   const float *lse_s, *sigma, *zt;   // per row (sigma nullptr: CE-only)
   const uint32_t* ties;              // (rows, tie_words(V)) or nullptr (CE-only)
   uint16_t* g;                       // (rows, V): binary16 p in, bf16 G out (in place)
-  uint16_t* gt;                      // (V, ldr) transposed G, or nullptr
-  int64_t ldr;
   float g_ce, g_tvd;
   const float* g_scale;
 };
@@ -494,12 +492,9 @@ struct GformArgs {
 // 2^15 p from the binary16 copy, a1 = alpha 2^-15, b1 = beta 2^9, s' = 2^-24
 // sign), the target element from its logit in fp32.  A tile of 64 rows x 256
 // columns per workgroup: each thread converts 8 groups of 8 consecutive
-// values (16 bytes in, 16 bytes out in place), and the tile goes through LDS
-// to be written transposed (16-byte stores along the rows of G^T).
+// values (16 bytes in, 16 bytes out in place).  The gradient products read G
+// as it lies: grad_x along its rows, grad_w down its columns.
 __global__ __launch_bounds__(256) void gform_kernel(GformArgs a) {
-  constexpr int kStride = kGCols + 2;  // halves per LDS row
-  __shared__ uint32_t tile32[kGRows * kStride / 2];
-  uint16_t* tile = reinterpret_cast<uint16_t*>(tile32);
   const int tid = tid_x();
   const unsigned tiles_c = (unsigned)(a.V + kGCols - 1) / kGCols;
   const unsigned b = bid_x();
@@ -513,129 +508,36 @@ __global__ __launch_bounds__(256) void gform_kernel(GformArgs a) {
   for (int i = 0; i < 8; ++i) {  // (row half, 64-column block)
     const int lr = (tid >> 3) + 32 * (i & 1), cc = lc + 64 * (i >> 1);
     const int r = r0 + lr, c = c0 + cc;
+    if (r >= a.rows || c >= a.V) continue;
+    const int64_t t = a.target[r];
+    uint16_t* gp = a.g + (int64_t)r * a.V + c;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (r < a.rows && c < a.V) {
-      const int64_t t = a.target[r];
-      uint16_t* gp = a.g + (int64_t)r * a.V + c;
-      if (t != a.ignore_index) {
-        const bool t_ok = t >= 0 && t < a.V;
-        const float alpha = kce - beta * (a.sigma ? a.sigma[r] : 0.0f);
-        const float a1 = alpha * kInvPqBiasG, b1 = beta * kTvScale;
-        const uint4 in = *reinterpret_cast<const uint4*>(gp);
-        const uint32_t tb = a.ties ? a.ties[(int64_t)r * tie_words(a.V) + (c >> 5)] >> (c & 31) : 0u;
-        // the target element from its logit in fp32 (p may be close to 1 there)
-        const float pt = t_ok ? exp2_hw(exparg(a.zt[r], pq_bias(a.lse_s[r]))) : 0.0f;
-        const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
-        float o[8];
+    if (t != a.ignore_index) {
+      const bool t_ok = t >= 0 && t < a.V;
+      const float alpha = kce - beta * (a.sigma ? a.sigma[r] : 0.0f);
+      const float a1 = alpha * kInvPqBiasG, b1 = beta * kTvScale;
+      const uint4 in = *reinterpret_cast<const uint4*>(gp);
+      const uint32_t tb = a.ties ? a.ties[(int64_t)r * tie_words(a.V) + (c >> 5)] >> (c & 31) : 0u;
+      // the target element from its logit in fp32 (p may be close to 1 there)
+      const float pt = t_ok ? exp2_hw(exparg(a.zt[r], pq_bias(a.lse_s[r]))) : 0.0f;
+      const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
+      float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t h = (uint16_t)(iw[e >> 1] >> (16 * (e & 1)));
-          const float pp = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0x7fffu));
-          const float sg = ((tb >> e) & 1u) ? 0.0f : ((h & 0x8000u) ? -kSignEps : kSignEps);
-          const float f = __builtin_fmaf(sg, b1, a1);
-          o[e] = (c + e == t) ? pt * f - kce : pp * f;
-        }
-        w[0] = pack_bf16x2(o[0], o[1]);
-        w[1] = pack_bf16x2(o[2], o[3]);
-        w[2] = pack_bf16x2(o[4], o[5]);
-        w[3] = pack_bf16x2(o[6], o[7]);
-        if (!t_ok) w[0] = w[1] = w[2] = w[3] = (uint32_t)kQNaN16 * 0x10001u;
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t h = (uint16_t)(iw[e >> 1] >> (16 * (e & 1)));
+        const float pp = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0x7fffu));
+        const float sg = ((tb >> e) & 1u) ? 0.0f : ((h & 0x8000u) ? -kSignEps : kSignEps);
+        const float f = __builtin_fmaf(sg, b1, a1);
+        o[e] = (c + e == t) ? pt * f - kce : pp * f;
       }
-      *reinterpret_cast<uint4*>(gp) = make_uint4(w[0], w[1], w[2], w[3]);
+      w[0] = pack_bf16x2(o[0], o[1]);
+      w[1] = pack_bf16x2(o[2], o[3]);
+      w[2] = pack_bf16x2(o[4], o[5]);
+      w[3] = pack_bf16x2(o[6], o[7]);
+      if (!t_ok) w[0] = w[1] = w[2] = w[3] = (uint32_t)kQNaN16 * 0x10001u;
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) tile32[(lr * kStride + cc) / 2 + q] = w[q];
+    *reinterpret_cast<uint4*>(gp) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (!a.gt) return;
-  __syncthreads();
-  const int lr = (tid & 7) * 8;  // 8 consecutive rows = columns of G^T
-  const int r = r0 + lr;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int oc = (tid >> 3) + 32 * i;  // a column of G = a row of G^T
-    const int c = c0 + oc;
-    if (c < a.V && r < a.ldr) {  // r % 8 == 0 and ldr % 8 == 0: the 8 values fit the row
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = (uint32_t)tile[(lr + 2 * q) * kStride + oc] | ((uint32_t)tile[(lr + 2 * q + 1) * kStride + oc] << 16);
-      *reinterpret_cast<uint4*>(a.gt + (int64_t)c * a.ldr + r) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- transpose (bf16)
-
-constexpr int kTrRows = 64;   // input rows per tile
-constexpr int kTrCols = 256;  // input columns per tile
-
-// out (cols x ld_out) = the transpose of in (rows x cols, row stride ld_in),
-// bf16 bit patterns, through a 64 x 256 LDS tile per workgroup: 16-byte loads
-// along the input rows, 16-byte stores along the output rows; output columns
-// rows..ld_out-1 are written as zeros.  ld_out % 8 == 0, out 16-byte aligned;
-// vec_in says whether in's rows are 16-byte aligned (else element loads).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
-                                                             int rows, int cols, uint16_t* __restrict__ out,
-                                                             int64_t ld_out, int vec_in) {
-  constexpr int kStride = kTrCols + 2;
-  __shared__ uint32_t tile32[kTrRows * kStride / 2];
-  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile32);
-  const int tid = tid_x();
-  const unsigned tiles_c = (unsigned)(cols + kTrCols - 1) / kTrCols;
-  const unsigned b = bid_x();
-  const unsigned tr = b / tiles_c;
-  const int r0 = (int)tr * kTrRows, c0 = (int)(b - tr * tiles_c) * kTrCols;
-  const int lc = (tid & 7) * 8;
-  uint32_t w[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lr = (tid >> 3) + 32 * (i & 1), c = c0 + lc + 64 * (i >> 1), r = r0 + lr;
-    w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
-    if (r < rows) {
-      const uint16_t* src = in + (int64_t)r * ld_in + c;
-      if (vec_in && c + 8 <= cols) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (c + k < cols) w[i][k >> 1] |= (uint32_t)src[k] << (16 * (k & 1));
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lr = (tid >> 3) + 32 * (i & 1), cc = lc + 64 * (i >> 1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) tile32[(lr * kStride + cc) / 2 + k] = w[i][k];
-  }
-  __syncthreads();
-  const int lr = (tid & 7) * 8;
-  const int r = r0 + lr;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int oc = (tid >> 3) + 32 * i;
-    const int c = c0 + oc;
-    if (c < cols && r < ld_out) {
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = (uint32_t)tile[(lr + 2 * k) * kStride + oc] | ((uint32_t)tile[(lr + 2 * k + 1) * kStride + oc] << 16);
-      *reinterpret_cast<uint4*>(out + (int64_t)c * ld_out + r) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t ld_in, int64_t rows, int64_t cols, uint16_t* out,
-                                 int64_t ld_out, hipStream_t st) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (ld_out % 8 || ld_out < rows || reinterpret_cast<uintptr_t>(out) % 16 || ld_in < cols) return hipErrorInvalidValue;
-  const int64_t tiles = ((rows + kTrRows - 1) / kTrRows) * ((cols + kTrCols - 1) / kTrCols);
-  if (rows > INT32_MAX || cols > INT32_MAX || tiles > UINT32_MAX) return hipErrorInvalidValue;
-  const int vec_in = (ld_in % 8 == 0 && reinterpret_cast<uintptr_t>(in) % 16 == 0) ? 1 : 0;
-  transpose_bf16_kernel<<<dim3((unsigned)tiles), dim3(256), 0, st>>>(in, ld_in, (int)rows, (int)cols, out, ld_out,
-                                                                     vec_in);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- workspace
@@ -648,12 +550,8 @@ struct LinearWs {
   float* tv;         // [tiles_n][chunk][2]
   uint16_t* p16;     // (chunk, V): binary16 p, then bf16 G
   uint32_t* ties;    // (chunk, tie_words(V))
-  uint16_t* gt;      // (V, ldr): G^T
-  uint16_t* wst;     // (H_s, V): W_s^T
-  uint16_t* xst;     // (H_s, ldr): X_s[chunk]^T
   float* gxp;        // [gx_splits][chunk][H_s]: split-K partials of grad_x (gx_splits > 1)
   int gx_splits;
-  int64_t ldr;
   size_t bytes;
 };
 
@@ -676,7 +574,6 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs,
   const int64_t tiles_n = (V + kDualBN - 1) / kDualBN;
   const int P = teacher ? 5 : 3;
   const bool grads = gx || gw;
-  w.ldr = (chunk + 7) & ~(int64_t)7;
   size_t off = 0;
   char* p = static_cast<char*>(base);
   auto take = [&](size_t bytes) {
@@ -689,9 +586,6 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs,
   w.tv = teacher ? reinterpret_cast<float*>(take((size_t)tiles_n * chunk * 2 * 4)) : nullptr;
   w.p16 = grads ? reinterpret_cast<uint16_t*>(take((size_t)chunk * V * 2)) : nullptr;
   w.ties = (grads && teacher) ? reinterpret_cast<uint32_t*>(take((size_t)chunk * tie_words(V) * 4)) : nullptr;
-  w.gt = gw ? reinterpret_cast<uint16_t*>(take((size_t)V * w.ldr * 2)) : nullptr;
-  w.wst = gx ? reinterpret_cast<uint16_t*>(take((size_t)Hs * V * 2)) : nullptr;
-  w.xst = gw ? reinterpret_cast<uint16_t*>(take((size_t)Hs * w.ldr * 2)) : nullptr;
   w.gx_splits = gx ? gx_splits(chunk, Hs, V) : 1;
   w.gxp = w.gx_splits > 1 ? reinterpret_cast<float*>(take((size_t)w.gx_splits * chunk * Hs * 4)) : nullptr;
   w.bytes = off;
@@ -705,8 +599,8 @@ LinearWs linear_ws(void* base, int64_t BT, int64_t chunk, int64_t V, int64_t Hs,
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   (void)hipGetLastError();
   if (g.splits > 1) {
-    if (!g.partials || !g.a_kc || !g.b_kc) return hipErrorInvalidValue;  // the lm_head path's layout only
-    return launch_gemm_split<true, true>(g, st);
+    if (!g.partials || !g.a_kc) return hipErrorInvalidValue;  // the lm_head path's layouts only
+    return g.b_kc ? launch_gemm_split<true, true>(g, st) : launch_gemm_split<true, false>(g, st);
   }
   if (g.a_kc) {
     if (g.b_kc) return g.accumulate ? launch_gemm_t<true, true, true>(g, st) : launch_gemm_t<true, true, false>(g, st);
@@ -757,9 +651,6 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
       return e;
   }
   if (!teacher && !grads) return hipSuccess;
-  if (gx) {  // W_s^T: (H_s, V), both operands of grad_x = G W_s contiguous along V
-    if (hipError_t e = launch_transpose_bf16(a.w_s, a.H_s, V, a.H_s, w.wst, V, st)) return e;
-  }
   for (int64_t r0 = 0; r0 < a.BT; r0 += chunk) {
     const int64_t rows = a.BT - r0 < chunk ? a.BT - r0 : chunk;
     // pass 2 over the chunk: (sum |p - q|, sum p s) per tile, and binary16 p + tie bits for G
@@ -780,29 +671,24 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
       if ((e = launch_tiles<false, true>(d, st))) return e;  // binary16 p only
     }
     if (!grads) continue;
-    // G (bf16, over the binary16 p) and G^T
+    // G (bf16, over the binary16 p, in place)
     GformArgs g{};
     g.target = a.target + r0; g.rows = (int)rows; g.V = (int)V; g.ignore_index = a.ignore_index;
     g.lse_s = a.lse_s + r0; g.sigma = teacher ? a.sigma + r0 : nullptr; g.zt = w.zt + r0;
-    g.ties = w.ties; g.g = w.p16; g.gt = gw ? w.gt : nullptr; g.ldr = w.ldr;
+    g.ties = w.ties; g.g = w.p16;
     g.g_ce = a.g_ce; g.g_tvd = a.g_tvd; g.g_scale = a.g_scale;
     const int64_t gtiles = ((rows + kGRows - 1) / kGRows) * ((V + kGCols - 1) / kGCols);
     (void)hipGetLastError();
     gform_kernel<<<dim3((unsigned)gtiles), dim3(256), 0, st>>>(g);
     if ((e = hipGetLastError())) return e;
-    if (gx) {  // grad_x[chunk] = G W_s: M = rows, N = H_s, K = V
-      GemmArgs p{w.p16, V, w.wst, V, a.grad_x_s + r0 * a.H_s, a.H_s, rows, a.H_s, V, true, true, false};
+    if (gx) {  // grad_x[chunk] = G W_s: M = rows, N = H_s, K = V; W_s read down its columns
+      GemmArgs p{w.p16, V, a.w_s, a.H_s, a.grad_x_s + r0 * a.H_s, a.H_s, rows, a.H_s, V, true, false, false};
       p.splits = w.gx_splits;  // sized for a full chunk; a shorter last chunk uses as many
       p.partials = w.gxp;
       if ((e = launch_gemm_bf16(p, st))) return e;
     }
-    if (gw) {  // grad_w (+)= G^T X_s[chunk]: M = V, N = H_s, K = rows
-      if ((e = launch_transpose_bf16(a.x_s + r0 * a.H_s, a.H_s, rows, a.H_s, w.xst, w.ldr, st))) return e;
-      // K rounded up to whole 16-byte groups: a buffer load that runs past the
-      // operand's range reads zeros as a whole, so the last row's final group
-      // must lie inside it; the padding columns of G^T and X_s^T are zeros
-      const int64_t kr = (rows + 7) & ~(int64_t)7;
-      GemmArgs p{w.gt, w.ldr, w.xst, w.ldr, a.grad_w_s, a.H_s, V, a.H_s, kr, true, true, r0 > 0};
+    if (gw) {  // grad_w (+)= G^T X_s[chunk]: M = V, N = H_s, K = rows; G and X_s read down their columns
+      GemmArgs p{w.p16, V, a.x_s + r0 * a.H_s, a.H_s, a.grad_w_s, a.H_s, V, a.H_s, rows, false, false, r0 > 0};
       if ((e = launch_gemm_bf16(p, st))) return e;
     }
   }

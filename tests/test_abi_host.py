@@ -313,13 +313,12 @@ def test_gemm_validation():
 def test_linear_validation():
     f = L.lx_ce_tvd_linear_forward_backward
     ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 136, 1, 128)
-    # per logit of a 128-row chunk: binary16 p (then G) and the bf16 transpose of G (2 + 2 B) and a tie bit;
-    # besides: the transposed w (V x 136 bf16) and chunk of x, per-tile partials, the target logits and
-    # split-K partials of grad_x (at most 8 splits of a 128 x 136 fp32 block).  No logit is stored.
+    # per logit of a 128-row chunk: binary16 p (then G, in place: 2 B) and a tie bit; besides: per-tile
+    # partials, the target logits and split-K partials of grad_x (at most 8 splits of a 128 x 136 fp32
+    # block).  No logit is stored and nothing is transposed.
     per_logit = 128 * 8200
-    assert per_logit * 4 <= ws_need
-    assert ws_need <= (per_logit * (4 + 1 / 8) + 8200 * 136 * 2 + 136 * 128 * 2 + 300 * 4 * (1 + 5 * 33)
-                       + 128 * 8 * 65 + 8 * 128 * 136 * 4 + 4096)
+    assert per_logit * 2 <= ws_need
+    assert ws_need <= (per_logit * (2 + 1 / 8) + 300 * 4 * (1 + 5 * 33) + 128 * 8 * 65 + 8 * 128 * 136 * 4 + 4096)
     assert lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 136, 0, 128) < ws_need
     ws_need = lx.lx_ce_tvd_linear_workspace_bytes(300, 8200, 64, 1, 128)  # the calls below: H = 64
     assert lx.lx_ce_tvd_linear_workspace_bytes(0, 8200, 136, 1, 128) == 0
