@@ -12,12 +12,13 @@
 //                   matrix cores and reduced in registers to per-row (max,
 //                   sum-exp) partials; the target logit z_t = x . w_t comes
 //                   from a per-row dot product; the tiles' partials are merged
-//                   in tile order (the vocabulary-parallel merge: each tile is
-//                   a column shard) -> lse_s, lse_t, ce;
+//                   like column shards of the vocabulary (in a fixed order:
+//                   eight contiguous tile ranges, then the ranges) -> lse_s,
+//                   lse_t, ce;
 //   pass 2 (TV)     256 x 128 tiles of z and u together are computed again and
 //                   reduced to per-row
-//                   (sum |p - q|, sum p * sign(p - q)) partials, merged in tile
-//                   order -> tvd, sigma; when gradients are wanted the pass also
+//                   (sum |p - q|, sum p * sign(p - q)) partials, merged the same
+//                   way -> tvd, sigma; when gradients are wanted the pass also
 //                   writes 2^15 p as binary16 with the sign of p - q in its sign
 //                   bit, and a bit per logit marking exact ties (sign 0);
 //   G               from those, the per-row sigma and the target logit:
@@ -540,6 +541,117 @@ __global__ __launch_bounds__(256) void gform_kernel(GformArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- merges of the per-tile partials
+
+// A row's partials from its ~600 (pass 1) or ~1200 (pass 2) tiles: kMergeRows
+// rows per workgroup and kMergeParts threads per row, thread j merging, in tile
+// order, the j-th of kMergeParts contiguous ranges of tiles; the ranges are then
+// merged in order.  A fixed order, so the result does not depend on timing.
+// (One thread per row, as in the vocabulary-parallel merges of a few shards,
+// would leave most of the GPU idle here.)
+constexpr int kMergeRows = 32;
+constexpr int kMergeParts = 8;
+
+// partials [N][BT][P]: (m_s, s_s[, m_t, s_t], target logit or +0) per tile -> ce,
+// lse_s, lse_t and the target logit
+template <bool TEACHER>
+__global__ __launch_bounds__(kMergeRows * kMergeParts) void lm_merge_stats_kernel(
+    const float* __restrict__ stats, int N, int64_t BT, const int64_t* __restrict__ target, int64_t V,
+    int64_t ignore_index, float* __restrict__ ce, float* __restrict__ lse_s, float* __restrict__ lse_t,
+    float* __restrict__ zt_out) {
+  constexpr int P = TEACHER ? 5 : 3;
+  __shared__ float red[kMergeParts][kMergeRows][5];
+  const int lr = tid_x() % kMergeRows, part = tid_x() / kMergeRows;
+  const int64_t r = (int64_t)bid_x() * kMergeRows + lr;
+  const int per = (N + kMergeParts - 1) / kMergeParts;
+  const int n0 = min(N, part * per), n1 = min(N, n0 + per);
+  Lse fs = lse_init(), ft = lse_init();
+  float zt = 0.0f;
+  if (r < BT) {
+    for (int n = n0; n < n1; ++n) {
+      const float* w = stats + ((int64_t)n * BT + r) * P;
+      lse_merge(fs, Lse{w[0], w[1]});
+      if (TEACHER) lse_merge(ft, Lse{w[2], w[3]});
+      zt += w[P - 1];  // the target's tile holds its logit, every other tile +0
+    }
+  }
+  red[part][lr][0] = fs.m;
+  red[part][lr][1] = fs.s;
+  red[part][lr][2] = ft.m;
+  red[part][lr][3] = ft.s;
+  red[part][lr][4] = zt;
+  __syncthreads();
+  if (part != 0 || r >= BT) return;
+  for (int j = 1; j < kMergeParts; ++j) {
+    lse_merge(fs, Lse{red[j][lr][0], red[j][lr][1]});
+    if (TEACHER) lse_merge(ft, Lse{red[j][lr][2], red[j][lr][3]});
+    zt += red[j][lr][4];
+  }
+  const int64_t t = target[r];
+  if (t == ignore_index) {
+    ce[r] = 0.0f;
+    lse_s[r] = 0.0f;
+    if (TEACHER) lse_t[r] = 0.0f;
+    zt_out[r] = 0.0f;
+    return;
+  }
+  const float ls = lse_value(fs);
+  if (t >= 0 && t < V) ce[r] = ls - zt; else store_nan(ce + r);
+  lse_s[r] = ls;
+  if (TEACHER) lse_t[r] = lse_value(ft);
+  zt_out[r] = zt;
+}
+
+// partials [N][BT][2]: (sum |p - q|, sum p sign) per tile -> tvd, sigma
+__global__ __launch_bounds__(kMergeRows * kMergeParts) void lm_merge_tv_kernel(
+    const float* __restrict__ tv, int N, int64_t BT, const int64_t* __restrict__ target, int64_t ignore_index,
+    float* __restrict__ tvd, float* __restrict__ sigma) {
+  __shared__ float red[kMergeParts][kMergeRows][2];
+  const int lr = tid_x() % kMergeRows, part = tid_x() / kMergeRows;
+  const int64_t r = (int64_t)bid_x() * kMergeRows + lr;
+  const int per = (N + kMergeParts - 1) / kMergeParts;
+  const int n0 = min(N, part * per), n1 = min(N, n0 + per);
+  float A = 0.0f, S = 0.0f;
+  if (r < BT) {
+    for (int n = n0; n < n1; ++n) {
+      const float2 w = *reinterpret_cast<const float2*>(tv + ((int64_t)n * BT + r) * 2);
+      A += w.x;
+      S += w.y;
+    }
+  }
+  red[part][lr][0] = A;
+  red[part][lr][1] = S;
+  __syncthreads();
+  if (part != 0 || r >= BT) return;
+  for (int j = 1; j < kMergeParts; ++j) {
+    A += red[j][lr][0];
+    S += red[j][lr][1];
+  }
+  const bool ign = target[r] == ignore_index;
+  tvd[r] = ign ? 0.0f : 0.5f * A;
+  sigma[r] = ign ? 0.0f : S;
+}
+
+hipError_t launch_lm_merge_stats(const float* stats, int N, const int64_t* target, int64_t BT, int64_t V,
+                                 int64_t ignore_index, bool teacher, float* ce, float* lse_s, float* lse_t, float* zt,
+                                 hipStream_t st) {
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)((BT + kMergeRows - 1) / kMergeRows)), block(kMergeRows * kMergeParts);
+  if (teacher)
+    lm_merge_stats_kernel<true><<<grid, block, 0, st>>>(stats, N, BT, target, V, ignore_index, ce, lse_s, lse_t, zt);
+  else
+    lm_merge_stats_kernel<false><<<grid, block, 0, st>>>(stats, N, BT, target, V, ignore_index, ce, lse_s, lse_t, zt);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_merge_tv(const float* tv, int N, const int64_t* target, int64_t BT, int64_t ignore_index,
+                              float* tvd, float* sigma, hipStream_t st) {
+  (void)hipGetLastError();
+  lm_merge_tv_kernel<<<dim3((unsigned)((BT + kMergeRows - 1) / kMergeRows)), dim3(kMergeRows * kMergeParts), 0, st>>>(
+      tv, N, BT, target, ignore_index, tvd, sigma);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- workspace
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -646,8 +758,8 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     target_logit_kernel<<<dim3((unsigned)((a.BT + 3) / 4)), dim3(256), 0, st>>>(
         a.x_s, a.w_s, a.H_s, (int)a.BT, V, a.target, a.ignore_index, w.stats, sa.P);
     if ((e = hipGetLastError())) return e;
-    if ((e = launch_vp_merge_stats_zt(w.stats, stiles_n, a.target, a.BT, V, a.ignore_index, teacher, a.ce, a.lse_s,
-                                      teacher ? a.lse_t : nullptr, w.zt, st)))
+    if ((e = launch_lm_merge_stats(w.stats, stiles_n, a.target, a.BT, V, a.ignore_index, teacher, a.ce, a.lse_s,
+                                   teacher ? a.lse_t : nullptr, w.zt, st)))
       return e;
   }
   if (!teacher && !grads) return hipSuccess;
@@ -665,7 +777,7 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     if (teacher) {
       e = grads ? launch_tiles<true, true>(d, st) : launch_tiles<true, false>(d, st);
       if (e) return e;
-      if ((e = launch_vp_merge_tv(w.tv, tiles_n, a.target + r0, rows, a.ignore_index, a.tvd + r0, a.sigma + r0, st)))
+      if ((e = launch_lm_merge_tv(w.tv, tiles_n, a.target + r0, rows, a.ignore_index, a.tvd + r0, a.sigma + r0, st)))
         return e;
     } else {
       if ((e = launch_tiles<false, true>(d, st))) return e;  // binary16 p only
