@@ -51,6 +51,13 @@ using mm::f32x16_t;
 // tiles and 48 KB for the dual 256 x 128 tiles.
 constexpr int kLds = 2 * 65536;
 constexpr int kLdsDual = 2 * (32768 + 16384);
+// pass 2's epilogue in the same LDS: row bases, (S, Q) partials, the tile's
+// binary16 p (rows padded to 272 bytes: the two half-waves' rows, 4 apart, fall
+// on different banks) and its tie words
+constexpr int kTilePStride = 136;  // halves per staged row
+constexpr int kTileP = 8192;
+constexpr int kTileT = kTileP + 256 * kTilePStride * 2;
+static_assert(kTileT + 256 * 4 * 4 <= kLdsDual, "pass 2 epilogue exceeds the main loops' LDS");
 
 // ---------------------------------------------------------------- plain products (fp32 C)
 
@@ -229,6 +236,46 @@ __device__ __forceinline__ float half_sum(float v) {
   return lo + hi;
 }
 
+// Row sums of a 32 x 32 accumulator block (one column per lane of each
+// half-wave, v[r] the lane's value in row r of its half, r = 0..15), all rows at
+// once: at the level of lane bit b every lane keeps half of its rows (those
+// its bit b selects), sends the other half to its partner (the lane differing
+// only in bit b) and adds what it receives.  Bit 4: the row-pair swap, two rows
+// an instruction; bit 3: row_ror 8; bits 0 and 1: quad permutations; then one
+// row per lane is left, and bit 2 (a swizzle) completes its sum.  Lane L of a
+// half ends with the total of row xsum_row(L) = b1 + 2 b0 + 4 b3 + 8 b4 (lanes
+// L and L ^ 4 the same row).  The association order is fixed.
+__device__ __forceinline__ int xsum_row(int lane) {
+  return ((lane >> 1) & 1) | ((lane & 1) << 1) | (((lane >> 3) & 1) << 2) | (((lane >> 4) & 1) << 3);
+}
+template <int CTRL>
+__device__ __forceinline__ float xsum_level(float lo, float hi, bool bit) {
+  const float keep = bit ? hi : lo, send = bit ? lo : hi;
+  return keep + dpp_mov<CTRL>(send);
+}
+__device__ __forceinline__ float xsum16(const float (&v)[16], int lane) {
+  float w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    // rows 0 and 2 of v[k] stay, rows 1 and 3 receive v[k + 8] of rows 0 and 2,
+    // and the reverse in the second result: a lane of row 0 gets v[k] of both
+    // partners, a lane of row 1 v[k + 8] of both
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 8]), false, false);
+    const unsigned a = pr[0], b = pr[1];  // copied out: see swap16
+    w[k] = __uint_as_float(a) + __uint_as_float(b);
+  }
+  const bool b3 = (lane >> 3) & 1, b0 = lane & 1, b1 = (lane >> 1) & 1;
+  float u[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) u[k] = xsum_level<0x128>(w[k], w[k + 4], b3);  // row_ror 8
+  float t[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) t[k] = xsum_level<0xB1>(u[k], u[k + 2], b0);    // quad_perm [1, 0, 3, 2]
+  const float x = xsum_level<0x4E>(t[0], t[1], b1);                           // quad_perm [2, 3, 0, 1]
+  // lane ^ 4 within each 32 lanes: and-mask 31, or-mask 0, xor-mask 4
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x101F));
+}
+
 // Per-row (max, sum-exp) of one tensor's tile values for the wave's 128 rows x
 // 32 NJ columns, merged with the other wave of the same rows through LDS: the
 // wave's result for tile row `lr` lands in red[(wn != 0) * 256 + lr]
@@ -389,10 +436,14 @@ void lm_tile_kernel(DualArgs a) {
 
   {
     // TV: p' = 2^15 p, q' = 2^15 q and s' = 2^-24 sign(p - q) from the arguments
-    // a = x log2(e) - lse log2(e) + 15, exactly as the other TV kernels form them
+    // a = x log2(e) - lse log2(e) + 15, exactly as the other TV kernels form them.
+    // With gradients the tile's binary16 p and its tie words are staged in LDS and
+    // written afterwards with whole 16-byte (p) and 4-byte (tie word) stores.
     float* nbs = reinterpret_cast<float*>(lds);         // [256]
     float* nbt = reinterpret_cast<float*>(lds + 1024);  // [256]
     float* red = reinterpret_cast<float*>(lds + 2048);  // [2][256][2] (S, Q) per wave column
+    uint16_t* ps = reinterpret_cast<uint16_t*>(lds + kTileP);  // [256][kTilePStride]
+    uint32_t* ts = reinterpret_cast<uint32_t*>(lds + kTileT);  // [256][4] tie words
     {
       const int m = m0 + tid;
       float bs = kMFloor, bt = kMFloor;  // ignored and absent rows: p = q = 0
@@ -404,18 +455,22 @@ void lm_tile_kernel(DualArgs a) {
       nbt[tid] = bt;
     }
     __syncthreads();
+    // tie words of this wave: lane 4 r + 2 j + h of tw[i] holds the word of
+    // accumulator row r of block i, column block j, half-wave h (row + 4 h)
+    uint32_t tw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      float Sr[16], Qr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = wm + 32 * i + mm::acc_row(r, lane);
-        const int m = m0 + lr;
         const float bs = nbs[lr], bt = nbt[lr];
         float S = 0.0f, Q = 0.0f;
+        uint64_t tie[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn + 32 * j + (lane & 31);
-          const bool ok = n < a.V;
+          const int lc = wn + 32 * j + (lane & 31);
+          const bool ok = n0 + lc < a.V;
           const float ap = exparg(az[i][j][r], bs);
           const float pp = exp2_hw(ap);
           float sg = 0.0f;
@@ -426,32 +481,38 @@ void lm_tile_kernel(DualArgs a) {
             Q = __builtin_fmaf(ok ? exp2_hw(aq) : 0.0f, sg, Q);
           }
           if (WRITE_P) {
-            const bool in = ok && m < a.rows;
             uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)pp);
             if (TEACHER && sg < 0.0f) h |= 0x8000u;
-            if (in) a.p16[(int64_t)m * a.V + n] = h;
-            if (TEACHER) {
-              // one bit per logit: sign(p - q) = 0 exactly (the lanes of a half
-              // hold 32 consecutive columns of one row)
-              const uint64_t tie = __ballot(in && sg == 0.0f);
-              const int first = lane & 32;
-              if ((lane & 31) == 0 && m < a.rows && n < a.V)
-                a.ties[(int64_t)m * tie_words(a.V) + (n >> 5)] = (uint32_t)(tie >> first);
-            }
+            ps[lr * kTilePStride + lc] = h;
+            // one bit per logit: sign(p - q) = 0 exactly (the lanes of a half
+            // hold 32 consecutive columns of one row)
+            if (TEACHER) tie[j] = __ballot(ok && sg == 0.0f);
           }
         }
-        if (TEACHER) {
-          S = half_sum(S);
-          Q = half_sum(Q);
-          if ((lane & 31) == 0) {
-            red[((wn != 0) * 256 + lr) * 2] = S;
-            red[((wn != 0) * 256 + lr) * 2 + 1] = Q;
-          }
+        if (WRITE_P && TEACHER) {
+          // lane 4 r + 2 j + h of tw[i] takes half h of ballot j
+          const uint32_t x0 = (lane & 1) ? (uint32_t)(tie[0] >> 32) : (uint32_t)tie[0];
+          const uint32_t x1 = (lane & 1) ? (uint32_t)(tie[1] >> 32) : (uint32_t)tie[1];
+          const uint32_t y = (lane & 2) ? x1 : x0;
+          if ((lane >> 2) == r) tw[i] = y;
         }
+        Sr[r] = S;
+        Qr[r] = Q;
+      }
+      if (TEACHER) {
+        const float S = xsum16(Sr, lane), Q = xsum16(Qr, lane);
+        const int lr = wm + 32 * i + mm::acc_row(xsum_row(lane & 31), lane);
+        red[((wn != 0) * 256 + lr) * 2] = S;
+        red[((wn != 0) * 256 + lr) * 2 + 1] = Q;
       }
     }
+    if (WRITE_P && TEACHER) {
+      const int h = lane & 1, j = (lane >> 1) & 1, r = lane >> 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ts[(wm + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * h) * 4 + (wn >> 5) + j] = tw[i];
+    }
+    __syncthreads();
     if (TEACHER) {
-      __syncthreads();
       const int m = m0 + tid;
       if (m < a.rows) {
         const float S = red[tid * 2] + red[(256 + tid) * 2];
@@ -459,6 +520,27 @@ void lm_tile_kernel(DualArgs a) {
         float* o = a.partials + ((int64_t)tn * a.rows + m) * 2;
         o[0] = (S - Q) * kTvScale;  // sum |p - q| over the tile's columns
         o[1] = S * kTvScale;        // sum p * sign(p - q)
+      }
+    }
+    if (WRITE_P) {
+      // 256 rows x 128 columns of binary16: 16 threads a row, 16 bytes each
+      const int c = (tid & 15) * 8;
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const int row = (tid >> 4) + 16 * k;
+        const int m = m0 + row;
+        if (m < a.rows && n0 + c < a.V)
+          *reinterpret_cast<uint4*>(a.p16 + (int64_t)m * a.V + n0 + c) =
+              *reinterpret_cast<const uint4*>(ps + row * kTilePStride + c);
+      }
+      if (TEACHER) {
+        const int64_t words = tie_words(a.V);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = (tid >> 2) + 64 * k, w = tid & 3;
+          const int m = m0 + row;
+          if (m < a.rows && tn * 4 + w < words) a.ties[(int64_t)m * words + tn * 4 + w] = ts[row * 4 + w];
+        }
       }
     }
   }
