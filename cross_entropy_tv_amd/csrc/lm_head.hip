@@ -277,7 +277,8 @@ __device__ __forceinline__ float xsum16(const float (&v)[16], int lane) {
 }
 
 // Per-row (max, sum-exp) of one tensor's tile values for the wave's 128 rows x
-// 32 NJ columns, merged with the other wave of the same rows through LDS: the
+// 32 NJ columns (the maxima reduced row by row, the sums 16 rows at a time),
+// merged with the other wave of the same rows through LDS: the
 // wave's result for tile row `lr` lands in red[(wn != 0) * 256 + lr]
 // (workgroup-visible after the caller's barrier).  Columns n >= V do not count.
 template <int NJ>
@@ -285,6 +286,7 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
                                          Lse* red /* [2][256] */) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float sr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v[NJ];
@@ -303,9 +305,12 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
         const bool ok = n0 + wn + 32 * j + (lane & 31) < V;
         s += ok ? exp2_hw(__builtin_fmaf(v[j], kLog2e, nb)) : 0.0f;
       }
-      s = half_sum(s);
-      if ((lane & 31) == 0) red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(r, lane)] = Lse{m, s};
+      sr[r] = s;
+      if ((lane & 31) == 0) red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(r, lane)].m = m;
     }
+    // the row sums, all 16 rows of the block at once (xsum16)
+    const float s = xsum16(sr, lane);
+    red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(xsum_row(lane & 31), lane)].s = s;
   }
 }
 
