@@ -51,6 +51,13 @@ using mm::f32x16_t;
 // tiles and 48 KB for the dual 256 x 128 tiles.
 constexpr int kLds = 2 * 65536;
 constexpr int kLdsDual = 2 * (32768 + 16384);
+// The 256 x 256 kernels (the gradient products and pass 1) run 8 waves, two per
+// SIMD, each 128 x 64 of the tile (4 x 2 accumulators, 128 registers): while one
+// wave of a SIMD waits for its slice data the other issues its MFMAs (6-7%
+// faster than 4 waves of 128 x 128 on the same main loop); each MFMA is then
+// followed by up to three of the slice's memory instructions.
+constexpr int kWideThreads = 512;
+constexpr int kWideMem = 3;
 // pass 2's epilogue in the same LDS: row bases, (S, Q) partials, the tile's
 // binary16 p (rows padded to 272 bytes: the two half-waves' rows, 4 apart, fall
 // on different banks) and its tie words
@@ -70,7 +77,7 @@ static_assert(kTileT + 256 * 4 * 4 <= kLdsDual, "pass 2 epilogue exceeds the mai
 // operands' bases to its first k, and writes its product (ACC = false) to
 // C + s * split_stride.
 template <bool AK, bool BK, bool ACC>
-__global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end, const uint16_t* __restrict__ B,
                       int64_t ldb, int64_t b_end, float* __restrict__ C, int64_t ldc, int M, int N, int K,
                       int tiles_m, int tiles_n, int splits, int kslice, int64_t split_stride) {
@@ -91,25 +98,25 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t a_end
   const int m0 = tm * mm::kBM, n0 = tn * 256;
   const int lane = tid_x() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
-  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
-  f32x16_t acc[4][4];
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 64;
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
   mm::pin_scalar(C);
   mm::pin_scalar(ldc);
-  mm::SliceLoader<AK, 256> la;
-  mm::SliceLoader<BK, 256> lb;
+  mm::SliceLoader<AK, 256, kWideThreads> la;
+  mm::SliceLoader<BK, 256, kWideThreads> lb;
   la.init(A, lda, a_end, M, K, m0, wave);
   lb.init(B, ldb, b_end, N, K, n0, wave);
-  mm::mainloop<AK, BK, 4, 256>(acc, lds, la, lb, K, wm, wn, wave);
+  mm::mainloop<AK, BK, 2, 256, kWideThreads, kWideMem>(acc, lds, la, lb, K, wm, wn, wave);
   // (accumulating: the 16 values of a 32 x 32 tile are all read before any is
   // written back, so the reads are in flight together)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + 32 * j + (lane & 31);
       float old[16];
       if (ACC) {
@@ -135,7 +142,7 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t st) {
   // bytes from each operand's start to the end of its last stored row
   const int64_t a_end = 2 * (AK ? (g.M - 1) * g.lda + g.K : (g.K - 1) * g.lda + g.M);
   const int64_t b_end = 2 * (BK ? (g.N - 1) * g.ldb + g.K : (g.K - 1) * g.ldb + g.N);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, ACC>), dim3(mm::grid_for(tiles_m, tiles_n)), dim3(mm::kThreads), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, ACC>), dim3(mm::grid_for(tiles_m, tiles_n)), dim3(kWideThreads), 0, st,
                      g.A, g.lda, a_end, g.B, g.ldb, b_end, g.C, g.ldc, (int)g.M, (int)g.N, (int)g.K, tiles_m,
                      tiles_n, 1, (int)g.K, (int64_t)0);
   return hipGetLastError();
@@ -165,7 +172,7 @@ hipError_t launch_gemm_split(const GemmArgs& g, hipStream_t st) {
   const int kslice = (int)((per + mm::kBK - 1) / mm::kBK * mm::kBK);
   const int splits = (int)((g.K + kslice - 1) / kslice);  // no empty split
   hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, false>), dim3(mm::grid_for(tiles_m, tiles_n * splits)),
-                     dim3(mm::kThreads), 0, st, g.A, g.lda, a_end, g.B, g.ldb, b_end, g.partials, g.N, (int)g.M,
+                     dim3(kWideThreads), 0, st, g.A, g.lda, a_end, g.B, g.ldb, b_end, g.partials, g.N, (int)g.M,
                      (int)g.N, (int)g.K, tiles_m, tiles_n, splits, kslice, g.M * g.N);
   if (hipError_t e = hipGetLastError()) return e;
   const int64_t total = g.M * g.N;
@@ -278,12 +285,12 @@ __device__ __forceinline__ float xsum16(const float (&v)[16], int lane) {
 
 // Per-row (max, sum-exp) of one tensor's tile values for the wave's 128 rows x
 // 32 NJ columns (the maxima reduced row by row, the sums 16 rows at a time),
-// merged with the other wave of the same rows through LDS: the
-// wave's result for tile row `lr` lands in red[(wn != 0) * 256 + lr]
+// merged with the other waves of the same rows through LDS: the
+// wave's result for tile row `lr` lands in red[wn / (32 NJ) * 256 + lr]
 // (workgroup-visible after the caller's barrier).  Columns n >= V do not count.
 template <int NJ>
 __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, int wn, int n0, int V, int lane,
-                                         Lse* red /* [2][256] */) {
+                                         Lse* red /* [256 / (32 NJ)][256] */) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float sr[16];
@@ -306,11 +313,11 @@ __device__ __forceinline__ void tile_lse(const f32x16_t (&acc)[4][NJ], int wm, i
         s += ok ? exp2_hw(__builtin_fmaf(v[j], kLog2e, nb)) : 0.0f;
       }
       sr[r] = s;
-      if ((lane & 31) == 0) red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(r, lane)].m = m;
+      if ((lane & 31) == 0) red[wn / (32 * NJ) * 256 + wm + 32 * i + mm::acc_row(r, lane)].m = m;
     }
     // the row sums, all 16 rows of the block at once (xsum16)
     const float s = xsum16(sr, lane);
-    red[(wn != 0) * 256 + wm + 32 * i + mm::acc_row(xsum_row(lane & 31), lane)].s = s;
+    red[wn / (32 * NJ) * 256 + wm + 32 * i + mm::acc_row(xsum_row(lane & 31), lane)].s = s;
   }
 }
 
@@ -330,7 +337,7 @@ struct StatsArgs {
   int tiles_m, tiles_n;
 };
 
-__global__ __attribute__((amdgpu_flat_work_group_size(mm::kThreads, mm::kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
 void lm_stats_kernel(StatsArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   int tm, tn;
@@ -338,31 +345,33 @@ void lm_stats_kernel(StatsArgs a) {
   const int m0 = tm * mm::kBM, n0 = tn * 256;
   const int lane = tid_x() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
-  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
-  f32x16_t acc[4][4];
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 64;
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
   {
-    mm::SliceLoader<true, 256> la;
-    mm::SliceLoader<true, 256> lb;
+    mm::SliceLoader<true, 256, kWideThreads> la;
+    mm::SliceLoader<true, 256, kWideThreads> lb;
     la.init(a.x, a.H, 2 * ((int64_t)(a.rows - 1) * a.H + a.H), a.rows, (int)a.H, m0, wave);
     lb.init(a.w, a.H, 2 * ((int64_t)(a.V - 1) * a.H + a.H), a.V, (int)a.H, n0, wave);
     mm::pin_scalar(a.partials);
     mm::pin_scalar(a.P);
     mm::pin_scalar(a.slot);
-    mm::mainloop<true, true, 4, 256>(acc, lds, la, lb, (int)a.H, wm, wn, wave);
+    mm::mainloop<true, true, 2, 256, kWideThreads, kWideMem>(acc, lds, la, lb, (int)a.H, wm, wn, wave);
   }
   const int tid = tid_x();
-  Lse* red = reinterpret_cast<Lse*>(lds);  // [2][256]
-  tile_lse<4>(acc, wm, wn, n0, a.V, lane, red);
+  Lse* red = reinterpret_cast<Lse*>(lds);  // [4][256]: the four waves of each row block
+  tile_lse<2>(acc, wm, wn, n0, a.V, lane, red);
   __syncthreads();
   const int m = m0 + tid;
-  if (m < a.rows) {
+  if (tid < 256 && m < a.rows) {
     float* o = a.partials + ((int64_t)tn * a.rows + m) * a.P;
     Lse f = red[tid];
     lse_merge(f, red[256 + tid]);
+    lse_merge(f, red[512 + tid]);
+    lse_merge(f, red[768 + tid]);
     o[a.slot] = f.m;
     o[a.slot + 1] = f.s;
     if (a.slot == 0) o[a.P - 1] = 0.0f;  // the target-logit kernel fills the target tile's slot
@@ -834,12 +843,12 @@ hipError_t run_linear(const LinearArgs& a, hipStream_t st) {
     sa.tiles_n = stiles_n;
     (void)hipGetLastError();
     const unsigned grid = mm::grid_for(sa.tiles_m, sa.tiles_n);
-    lm_stats_kernel<<<dim3(grid), dim3(mm::kThreads), 0, st>>>(sa);
+    lm_stats_kernel<<<dim3(grid), dim3(kWideThreads), 0, st>>>(sa);
     hipError_t e = hipGetLastError();
     if (e) return e;
     if (teacher) {
       sa.x = a.x_t; sa.w = a.w_t; sa.H = a.H_t; sa.slot = 2;
-      lm_stats_kernel<<<dim3(grid), dim3(mm::kThreads), 0, st>>>(sa);
+      lm_stats_kernel<<<dim3(grid), dim3(kWideThreads), 0, st>>>(sa);
       if ((e = hipGetLastError())) return e;
     }
     target_logit_kernel<<<dim3((unsigned)((a.BT + 3) / 4)), dim3(256), 0, st>>>(

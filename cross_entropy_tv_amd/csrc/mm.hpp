@@ -1,8 +1,9 @@
 // bf16 matrix-core (MFMA) building blocks of the lm_head path, gfx950.
 //
-// A workgroup of 4 waves computes a 256 x BN tile of C[m][n] = sum_k A(m, k)
-// B(n, k) with v_mfma_f32_32x32x16_bf16: waves 2 x 2, each a 128 x (32 NJ)
-// block held as 4 x NJ MFMA accumulators (fp32, 16 per lane each).  K advances
+// A workgroup of NT / 64 waves (4, or 8 for two waves per SIMD) computes a
+// 256 x BN tile of C[m][n] = sum_k A(m, k) B(n, k) with
+// v_mfma_f32_32x32x16_bf16: waves 2 x (NT / 128), each a 128 x (32 NJ) block
+// held as 4 x NJ MFMA accumulators (fp32, 16 per lane each).  K advances
 // in slices of 64.  A slice travels memory -> registers -> LDS: while slice kt
 // is multiplied out of one LDS stage, each thread writes its share of slice
 // kt + 1 (loaded during slice kt - 1) into the other stage and, piece by
@@ -77,11 +78,12 @@ __device__ __forceinline__ int tr_swizzle(int k) { return (k & 3) << 1; }
 // change from slice to slice is computed once per tile; rows past the matrix
 // get an out-of-range offset once, and the K bound is checked per slice, so
 // slices past the last one load zeros.
-template <bool KC, int ROWS>
+template <bool KC, int ROWS, int NT = kThreads>
 struct SliceLoader {
   static_assert(KC || ROWS == 256, "M/N-contiguous operands come in 256-row tiles");
   static constexpr int kTileBytes = ROWS * kBK * 2;
-  static constexpr int kLoads = kTileBytes / (kThreads * 16);  // 16-byte pieces per thread and slice
+  static constexpr int kLoads = kTileBytes / (NT * 16);  // 16-byte pieces per thread and slice
+  static_assert(kLoads >= 1 && kLoads * NT * 16 == kTileBytes, "whole 1 KB pieces per wave");
   uint32_t off[kLoads];
   int kk[kLoads];
   const uint16_t* P;
@@ -177,14 +179,15 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Group I of k-step S of a slice (see the schedule in the header comment).
-template <bool AK, bool BK, int NJ, int BROWS, int S, int I>
+template <bool AK, bool BK, int NJ, int BROWS, int NT, int MEM, int S, int I>
 __device__ __forceinline__ void step(Frags<NJ>& f, f32x16_t (&acc)[4][NJ],
-                                     Staged<SliceLoader<AK, 256>::kLoads, SliceLoader<BK, BROWS>::kLoads>& st,
-                                     const uint8_t* T, uint8_t* NX, int wm, int wn, const SliceLoader<AK, 256>& la,
-                                     const SliceLoader<BK, BROWS>& lb, const __amdgpu_buffer_rsrc_t& ra,
-                                     const __amdgpu_buffer_rsrc_t& rb, int k2, int wave) {
-  constexpr int kAT = SliceLoader<AK, 256>::kTileBytes;
-  constexpr int kLA = SliceLoader<AK, 256>::kLoads, kLB = SliceLoader<BK, BROWS>::kLoads;
+                                     Staged<SliceLoader<AK, 256, NT>::kLoads, SliceLoader<BK, BROWS, NT>::kLoads>& st,
+                                     const uint8_t* T, uint8_t* NX, int wm, int wn,
+                                     const SliceLoader<AK, 256, NT>& la, const SliceLoader<BK, BROWS, NT>& lb,
+                                     const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rb, int k2,
+                                     int wave) {
+  constexpr int kAT = SliceLoader<AK, 256, NT>::kTileBytes;
+  constexpr int kLA = SliceLoader<AK, 256, NT>::kLoads, kLB = SliceLoader<BK, BROWS, NT>::kLoads;
   constexpr int kP = kLA + kLB;  // pieces per thread and slice
   constexpr int G = S * 4 + I;
   if (S == 3 && I == 0) lds_barrier();
@@ -219,7 +222,7 @@ __device__ __forceinline__ void step(Frags<NJ>& f, f32x16_t (&acc)[4][NJ],
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100 | 0x200 | 0x020, 2, 0);  // LDS read / write, VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x100 | 0x200 | 0x020, MEM, 0);  // LDS reads / writes, VMEM reads
   }
   __builtin_amdgcn_sched_group_barrier(0x100 | 0x200 | 0x020, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -235,12 +238,12 @@ __device__ __forceinline__ void step(Frags<NJ>& f, f32x16_t (&acc)[4][NJ],
 // with LDS at `lds`: 2 stages of [A tile 32 KB][B tile BROWS * 128 B].
 // Leaves LDS free: every load and LDS access has retired and every wave is
 // past the final barrier.
-template <bool AK, bool BK, int NJ, int BROWS>
-__device__ __forceinline__ void mainloop(f32x16_t (&acc)[4][NJ], uint8_t* lds, const SliceLoader<AK, 256>& la,
-                                         const SliceLoader<BK, BROWS>& lb, int K, int wm, int wn, int wave) {
-  constexpr int kAT = SliceLoader<AK, 256>::kTileBytes;
-  constexpr int kStage = kAT + SliceLoader<BK, BROWS>::kTileBytes;
-  constexpr int kLA = SliceLoader<AK, 256>::kLoads, kLB = SliceLoader<BK, BROWS>::kLoads;
+template <bool AK, bool BK, int NJ, int BROWS, int NT = kThreads, int MEM = 2>
+__device__ __forceinline__ void mainloop(f32x16_t (&acc)[4][NJ], uint8_t* lds, const SliceLoader<AK, 256, NT>& la,
+                                         const SliceLoader<BK, BROWS, NT>& lb, int K, int wm, int wn, int wave) {
+  constexpr int kAT = SliceLoader<AK, 256, NT>::kTileBytes;
+  constexpr int kStage = kAT + SliceLoader<BK, BROWS, NT>::kTileBytes;
+  constexpr int kLA = SliceLoader<AK, 256, NT>::kLoads, kLB = SliceLoader<BK, BROWS, NT>::kLoads;
   const int nk = (K + kBK - 1) / kBK;
   Staged<kLA, kLB> st;
   {
@@ -278,7 +281,7 @@ __device__ __forceinline__ void mainloop(f32x16_t (&acc)[4][NJ], uint8_t* lds, c
     uint8_t* NX = lds + ((kt & 1) ^ 1) * kStage;
     const int k2 = (kt + 2) * kBK;
     const __amdgpu_buffer_rsrc_t ra = la.rsrc(k2), rb = lb.rsrc(k2);
-#define LX_STEP(S, I) step<AK, BK, NJ, BROWS, S, I>(f, acc, st, T, NX, wm, wn, la, lb, ra, rb, k2, wave)
+#define LX_STEP(S, I) step<AK, BK, NJ, BROWS, NT, MEM, S, I>(f, acc, st, T, NX, wm, wn, la, lb, ra, rb, k2, wave)
     LX_STEP(0, 0); LX_STEP(0, 1); LX_STEP(0, 2); LX_STEP(0, 3);
     LX_STEP(1, 0); LX_STEP(1, 1); LX_STEP(1, 2); LX_STEP(1, 3);
     LX_STEP(2, 0); LX_STEP(2, 1); LX_STEP(2, 2); LX_STEP(2, 3);
