@@ -6,7 +6,9 @@ member workgroups per row exchanging partials through device-coherent slots,
 merged in member order).  Each path runs 128 times on the same inputs; every
 output and the gradient must equal the first run bit for bit.  Arrival order
 of the members changes from run to run, so any order dependence in a merge
-would show here.
+would show here.  The lm_head path (per-tile partials merged in a fixed
+order, split-K partials of grad_x added in split order, grad_w accumulated
+chunk by chunk) is repeated 16 times the same way.
 """
 from __future__ import annotations
 
@@ -98,3 +100,31 @@ def test_read_once_exchange_128_repeats(BT, V):
     _repeat(f"one pass CE+TVD {BT}x{V}", _one_pass(zs, us, tg, True))
     announce(f"determinism: one pass CE-only, {BT}x{V} bf16, 128 runs")
     _repeat(f"one pass CE-only {BT}x{V}", _one_pass(zs, us, tg, False))
+
+
+@pytest.mark.parametrize("BT,V,H,chunk", [(300, 8200, 136, 128), (64, 151936, 64, 64)],
+                         ids=["300x8200_chunks_128_split_k", "64x151936_one_chunk"])
+def test_linear_16_repeats(BT, V, H, chunk):
+    x_s, w_s, x_t, w_t, t = W.linear_inputs(BT, V, H, H + 8, seed=73)
+    d = lambda b: to_dev(b)  # noqa: E731
+    X, Wd, Xt, Wt, tg = d(x_s), d(w_s), d(x_t), d(w_t), d(t)
+    announce(f"determinism: lm_head {BT}x{V} H {H} chunk {chunk}, 16 runs")
+
+    def step():
+        f = lambda: torch.empty(BT, dtype=torch.float32, device=DEV)  # noqa: E731
+        out = {"ce": f(), "tvd": f(), "lse_s": f(), "lse_t": f(), "sigma": f()}
+        gx = torch.empty((BT, H), dtype=torch.float32, device=DEV)
+        gw = torch.empty((V, H), dtype=torch.float32, device=DEV)
+        lx.lx_ce_tvd_linear_forward_backward(X, Wd, Xt, Wt, tg, II, out["ce"], out["tvd"], out["lse_s"],
+                                             out["lse_t"], out["sigma"], gx, gw, 0.5, 1.5, None, chunk)
+        return [v.view(torch.int32).clone() for v in out.values()] + [gx.view(torch.int32).clone(),
+                                                                      gw.view(torch.int32).clone()]
+    first = step()
+    torch.cuda.synchronize()
+    bad = 0
+    for _ in range(15):
+        cur = step()
+        bad += sum(int(not torch.equal(a, b)) for a, b in zip(first, cur))
+    torch.cuda.synchronize()
+    print(f"lm_head {BT}x{V}: 16 runs, {bad} differing arrays", flush=True)
+    assert bad == 0
