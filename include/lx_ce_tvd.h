@@ -428,7 +428,8 @@ lx_status lx_ce_tvd_backward_shard(void* grad, const void* student, const void* 
  *          1 <= M, N, K <= 2^31 - 1.  C must not overlap A or B.
  * One launch of the library's MFMA kernel (256 x 256 tiles, fp32
  * accumulation); it allocates nothing and keeps no state.  Operands
- * contiguous along K are the fast layout.
+ * contiguous along M or N are read with the LDS transpose read, at about the
+ * speed of K-contiguous ones (the lm_head path uses both).
  * Errors : LX_ERR_INVALID_ARG, LX_ERR_ALIAS, LX_ERR_HIP.
  */
 lx_status lx_gemm_bf16(const void* A, int64_t lda, int a_k_contiguous, const void* B, int64_t ldb,
