@@ -31,6 +31,12 @@ namespace lx {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kMFloor = -1.0e30f;
+// A thread's sum of exponentials taken against a reference maximum (its first
+// group's) is redone against its true maximum once it reaches 2^100 (a logit
+// ~69 above the reference): every such partial is then below 2^100 + the
+// count of its terms, so the merges of up to 2^27 of them (lanes, waves,
+// members or chunks, shards) cannot overflow fp32.
+constexpr float kRefSumLimit = 0x1p100f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -16,9 +16,9 @@
 //      into registers with streaming loads;
 //   3. step 1: sum of exp(x - m) against one reference m per thread (the
 //      maximum of the thread's first group), so no running rescale is needed;
-//      a logit ~88 above that reference would overflow, which the thread
-//      detects and then redoes its sums against its true maxima (exact either
-//      way, and from registers);
+//      a logit ~69 above that reference makes the sum reach kRefSumLimit,
+//      and the thread then redoes its sums against its true maxima (exact
+//      either way, and from registers), so no merge of the sums can overflow;
 //   4. the workgroup publishes its (max, sum-exp) pairs for both tensors and
 //      waits for the K pairs of its row, merges them in member order (every
 //      member gets bit-identical log-sum-exps), and runs step 2 over its
@@ -454,7 +454,7 @@ void cluster_kernel(const T* student, const T* __restrict__ teacher, const int64
       }
     }
   }
-  if (!(sz0 + sz1 < 3.0e38f) || !(su0 + su1 < 3.0e38f)) {
+  if (!(sz0 + sz1 < kRefSumLimit) || !(su0 + su1 < kRefSumLimit)) {
     // a logit far above the first group's maximum: redo against the true maxima
 #pragma unroll
     for (int i = 1; i < G; ++i) {
@@ -941,7 +941,7 @@ void cluster_f32_kernel(const float* student, const float* __restrict__ teacher,
       }
     }
   }
-  if (!(sz0 + sz1 < 3.0e38f) || !(su0 + su1 < 3.0e38f)) {
+  if (!(sz0 + sz1 < kRefSumLimit) || !(su0 + su1 < kRefSumLimit)) {
     // a logit far above the first quad's maximum: redo against the true maxima
 #pragma unroll
     for (int i = 1; i < G; ++i) {

@@ -30,17 +30,141 @@ namespace lx {
 namespace {
 
 constexpr int kVpThreads = 256;
+constexpr int kVpUnits = 10;  // 16-byte units per thread and tensor held at once
 constexpr int kVpMergeThreads = 256;
 constexpr int kMaxGrid = 1 << 20;
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16-byte unit of logits widened to f32: 8 bf16 or binary16 logits, or 4 fp32.
+template <typename T>
+struct Unit;
+template <>
+struct Unit<uint16_t> {
+  static constexpr int E = 8;
+  static __device__ __forceinline__ void get(const u32x4_t& w, float (&x)[8]) {
+    const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;  // copied out: see the one-pass kernels
+    x[0] = __uint_as_float(w0 << 16); x[1] = __uint_as_float(w0 & 0xffff0000u);
+    x[2] = __uint_as_float(w1 << 16); x[3] = __uint_as_float(w1 & 0xffff0000u);
+    x[4] = __uint_as_float(w2 << 16); x[5] = __uint_as_float(w2 & 0xffff0000u);
+    x[6] = __uint_as_float(w3 << 16); x[7] = __uint_as_float(w3 & 0xffff0000u);
+  }
+};
+template <>
+struct Unit<_Float16> {
+  static constexpr int E = 8;
+  static __device__ __forceinline__ void get(const u32x4_t& w, float (&x)[8]) {
+    const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    unpack_f16x2(w0, x[0], x[1]); unpack_f16x2(w1, x[2], x[3]);
+    unpack_f16x2(w2, x[4], x[5]); unpack_f16x2(w3, x[6], x[7]);
+  }
+};
+template <>
+struct Unit<float> {
+  static constexpr int E = 4;
+  static __device__ __forceinline__ void get(const u32x4_t& w, float (&x)[4]) {
+    const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    x[0] = __uint_as_float(w0); x[1] = __uint_as_float(w1);
+    x[2] = __uint_as_float(w2); x[3] = __uint_as_float(w3);
+  }
+};
+constexpr int kRsrcFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
+constexpr int kStreamPolicy = 2;        // non-temporal loads: every logit is read once
+
+// Hides a held unit from common-subexpression elimination, so that the
+// compiler keeps the 16 packed bytes (4 registers) until each use rather
+// than the widened floats (8).
+__device__ __forceinline__ void launder(u32x4_t& w) {
+  unsigned a = w.x, b = w.y, c = w.z, d = w.w;
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  w = (u32x4_t){a, b, c, d};
+}
+
+// Units [c, c + NT * U) of a row body of nu units: thread tid holds units
+// c + tid + k * NT, k < n, all requested at once.  The loads go through a
+// buffer resource covering just these units, so those past the body's end
+// return 0 without touching memory and need no branch (w[k], k >= n, is
+// never read).
+template <typename T, int NT, int U>
+__device__ __forceinline__ int load_units(const T* body, int nu, int c, int tid, u32x4_t (&w)[U]) {
+  constexpr int E = Unit<T>::E;
+  const int cnt = min(nu - c, NT * U);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(body + (int64_t)c * E), (short)0, cnt * 16, kRsrcFlags);
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+    w[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + k * NT) * 16, 0,
+                                                                            kStreamPolicy));
+  return tid < cnt ? min(U, (cnt - tid - 1) / NT + 1) : 0;
+}
+
+// (max, sum-exp) of n >= 1 held units merged into a: the sum is taken against
+// the maximum of the first unit (no rescaling per unit); a logit ~69 above it
+// takes the sum to kRefSumLimit, and then the sum is redone against the
+// units' maximum.
+template <typename T, int U>
+__device__ __forceinline__ void units_lse(u32x4_t (&w)[U], int n, Lse& a) {
+  constexpr int E = Unit<T>::E;
+  float x[E];
+  Unit<T>::get(w[0], x);
+  float m = x[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) m = fmaxf(m, x[e]);
+  float s0 = 0.0f, s1 = 0.0f;
+  {
+    const float nb = -(m * kLog2e);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (k < n) {
+        launder(w[k]);
+        Unit<T>::get(w[k], x);
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          s0 += exp2_hw(__builtin_fmaf(x[e], kLog2e, nb));
+          s1 += exp2_hw(__builtin_fmaf(x[e + 1], kLog2e, nb));
+        }
+      }
+    }
+  }
+  if (!(s0 + s1 < kRefSumLimit)) {
+#pragma unroll
+    for (int k = 1; k < U; ++k) {
+      if (k < n) {
+        launder(w[k]);
+        Unit<T>::get(w[k], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, x[e]);
+      }
+    }
+    const float nb = -(m * kLog2e);
+    s0 = s1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (k < n) {
+        launder(w[k]);
+        Unit<T>::get(w[k], x);
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          s0 += exp2_hw(__builtin_fmaf(x[e], kLog2e, nb));
+          s1 += exp2_hw(__builtin_fmaf(x[e + 1], kLog2e, nb));
+        }
+      }
+    }
+  }
+  lse_merge(a, Lse{m, s0 + s1});
+}
+
 // One workgroup per row (grid-stride over rows): the shard's (max, sum-exp)
 // pairs and its part of the target logit.  stats[r] = {m_s, s_s, m_t, s_t,
-// zt} with a teacher, {m_s, s_s, zt} without; ignored rows get zeros.
-template <typename T, bool TEACHER, int NT>
+// zt} with a teacher, {m_s, s_s, zt} without; ignored rows get zeros.  Each
+// thread requests up to U 16-byte units of each tensor before it works on
+// any, so a row's loads are all in flight at once.
+template <typename T, bool TEACHER, int NT, int U>
 __global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ student, const T* __restrict__ teacher,
                                                       const int64_t* __restrict__ target, int64_t BT, int Vs,
                                                       int64_t v0, int64_t ignore_index, int vec,
                                                       float* __restrict__ stats) {
+  constexpr int E = Unit<T>::E;
   __shared__ Lse red_s[NT / 64];
   __shared__ Lse red_t[NT / 64];
   constexpr int P = TEACHER ? 5 : 3;
@@ -54,23 +178,29 @@ __global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ stud
     }
     const T* z = student + r * (int64_t)Vs;
     const T* u = TEACHER ? teacher + r * (int64_t)Vs : nullptr;
+    // the target logit, requested now so that it has long arrived at the row's end
+    const int64_t tc = t - v0;
+    float zt = 0.0f;
+    if (tid == 0 && tc >= 0 && tc < Vs) zt = load1(z + tc);
     const RowLayout L = row_layout(z, Vs, vec);
     const int nsc = L.head + L.tail;
+    const int nu = L.groups * (8 / E);
+    const T* zb = z + L.head;
+    const T* ub = TEACHER ? u + L.head : nullptr;
     Lse as = lse_init(), at = lse_init();
+    for (int c = 0; c < nu; c += NT * U) {
+      u32x4_t wz[U], wu[U];
+      const int n = load_units<T, NT, U>(zb, nu, c, tid, wz);
+      if (TEACHER) load_units<T, NT, U>(ub, nu, c, tid, wu);
+      if (n > 0) {
+        units_lse<T, U>(wz, n, as);
+        if (TEACHER) units_lse<T, U>(wu, n, at);
+      }
+    }
     for (int i = tid; i < nsc; i += NT) {
       const int e = scalar_elem(L, i);
       lse_add1(as, load1(z + e));
       if (TEACHER) lse_add1(at, load1(u + e));
-    }
-    const T* zb = z + L.head;
-    const T* ub = TEACHER ? u + L.head : nullptr;
-#pragma unroll 2
-    for (int g = tid; g < L.groups; g += NT) {
-      float x[8], y[8];
-      load8(zb + 8 * g, x);
-      if (TEACHER) load8(ub + 8 * g, y);
-      lse_add8(as, x);
-      if (TEACHER) lse_add8(at, y);
     }
     const Lse fs = block_lse<NT>(as, red_s);
     Lse ft{0.0f, 0.0f};
@@ -82,8 +212,7 @@ __global__ __launch_bounds__(NT) void vp_stats_kernel(const T* __restrict__ stud
         o[2] = ft.m;
         o[3] = ft.s;
       }
-      const int64_t tc = t - v0;
-      o[P - 1] = (tc >= 0 && tc < Vs) ? load1(z + tc) : 0.0f;
+      o[P - 1] = zt;
     }
     __syncthreads();  // red_s / red_t are reused by the next row
   }
@@ -125,12 +254,13 @@ __global__ __launch_bounds__(kVpMergeThreads) void vp_merge_stats_kernel(
 }
 
 // One workgroup per row: the shard's (sum |p - q|, sum p * sign) from the
-// global log-sum-exps; ignored rows get zeros.
-template <typename T, int NT>
+// global log-sum-exps; ignored rows get zeros.  Loads as vp_stats_kernel.
+template <typename T, int NT, int U>
 __global__ __launch_bounds__(NT) void vp_tv_kernel(const T* __restrict__ student, const T* __restrict__ teacher,
                                                    const int64_t* __restrict__ target, int64_t BT, int Vs,
                                                    int64_t ignore_index, int vec, const float* __restrict__ lse_s,
                                                    const float* __restrict__ lse_t, float* __restrict__ tv) {
+  constexpr int E = Unit<T>::E;
   __shared__ float red_f[2][NT / 64];
   const int tid = tid_x();
   for (int64_t r = bid_x(); r < BT; r += nblocks_x()) {
@@ -143,20 +273,30 @@ __global__ __launch_bounds__(NT) void vp_tv_kernel(const T* __restrict__ student
     const T* u = teacher + r * (int64_t)Vs;
     const RowLayout L = row_layout(z, Vs, vec);
     const int nsc = L.head + L.tail;
+    const int nu = L.groups * (8 / E);
     const float nbs = pq_bias(lse_s[r]), nbt = pq_bias(lse_t[r]);
     float Q0 = 0.f, Q1 = 0.f, S0 = 0.f, S1 = 0.f;
+    for (int c = 0; c < nu; c += NT * U) {
+      u32x4_t wz[U], wu[U];
+      const int n = load_units<T, NT, U>(z + L.head, nu, c, tid, wz);
+      load_units<T, NT, U>(u + L.head, nu, c, tid, wu);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (k < n) {
+          float x[E], y[E];
+          Unit<T>::get(wz[k], x);
+          Unit<T>::get(wu[k], y);
+#pragma unroll
+          for (int e = 0; e < E; e += 2) {
+            tv_add1(x[e], y[e], nbs, nbt, Q0, S0);
+            tv_add1(x[e + 1], y[e + 1], nbs, nbt, Q1, S1);
+          }
+        }
+      }
+    }
     for (int i = tid; i < nsc; i += NT) {
       const int e = scalar_elem(L, i);
       tv_add1(load1(z + e), load1(u + e), nbs, nbt, Q0, S0);
-    }
-    const T* zb = z + L.head;
-    const T* ub = u + L.head;
-#pragma unroll 2
-    for (int g = tid; g < L.groups; g += NT) {
-      float x[8], y[8];
-      load8(zb + 8 * g, x);
-      load8(ub + 8 * g, y);
-      tv_add8(x, y, nbs, nbt, Q0, Q1, S0, S1);
     }
     const float Q = block_sum_t0<NT>(Q0 + Q1, red_f[0]);
     const float S = block_sum_t0<NT>(S0 + S1, red_f[1]);
@@ -202,10 +342,10 @@ hipError_t launch_vp_stats_t(const VpArgs& a, hipStream_t st) {
   const T* z = static_cast<const T*>(a.student);
   const T* u = static_cast<const T*>(a.teacher);
   if (u) {
-    hipLaunchKernelGGL((vp_stats_kernel<T, true, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st, z,
+    hipLaunchKernelGGL((vp_stats_kernel<T, true, kVpThreads, kVpUnits>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st, z,
                        u, a.target, a.BT, (int)a.Vs, a.v0, a.ignore_index, a.vec, a.out);
   } else {
-    hipLaunchKernelGGL((vp_stats_kernel<T, false, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
+    hipLaunchKernelGGL((vp_stats_kernel<T, false, kVpThreads, kVpUnits>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
                        z, u, a.target, a.BT, (int)a.Vs, a.v0, a.ignore_index, a.vec, a.out);
   }
   return hipGetLastError();
@@ -214,7 +354,7 @@ hipError_t launch_vp_stats_t(const VpArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t launch_vp_tv_t(const VpArgs& a, hipStream_t st) {
   (void)hipGetLastError();
-  hipLaunchKernelGGL((vp_tv_kernel<T, kVpThreads>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
+  hipLaunchKernelGGL((vp_tv_kernel<T, kVpThreads, kVpUnits>), dim3(row_grid(a.BT)), dim3(kVpThreads), 0, st,
                      static_cast<const T*>(a.student), static_cast<const T*>(a.teacher), a.target, a.BT, (int)a.Vs,
                      a.ignore_index, a.vec, a.lse_s, a.lse_t, a.out);
   return hipGetLastError();

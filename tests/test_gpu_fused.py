@@ -96,6 +96,39 @@ def test_one_pass_shapes(BT, V, in_place, teacher):
         assert abs(o["ce"][3] - math.log(V)) <= 1e-4
 
 
+def reference_trap_rows(BT, V, period, lo, hi, seed):
+    """bf16 rows whose groups of 8 columns hold lo where (group mod period) < 256
+    and hi elsewhere: with 256 threads a thread's first group is then a lo group
+    and its others hi ones, so every thread's sum against its first group's
+    maximum is about n e^(hi - lo) (n its hi elements) -- each below fp32's
+    limit, their sum over the workgroup far above it unless the kernels redo such
+    sums against the true maximum."""
+    g = np.arange(V) // 8
+    row = np.where(g % period < 256, lo, hi).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    z = np.repeat(row[None, :], BT, axis=0) + rng.integers(0, 4, (BT, V)).astype(np.float32) * 0.125
+    return W.bf16_bits_rne(z)
+
+
+def test_reference_sums_near_the_fp32_limit():
+    """One pass and read-once forward on 128 x 151936 (K = 4 members of 4748 groups):
+    each thread's sum against its first group is ~1e37 (82 between lo and hi), the
+    sum over a workgroup would overflow fp32; the redo against the true maximum
+    keeps every output finite and within tolerance."""
+    BT, V = 128, 151936
+    z = reference_trap_rows(BT, V, 4748, -57.0, 25.0, seed=3)
+    u = reference_trap_rows(BT, V, 4748, -50.0, 24.0, seed=4)
+    t = np.random.default_rng(5).integers(0, V, BT).astype(np.int64)
+    t[7] = II
+    assert one_pass(BT, V)
+    fused_case("reference sums near the fp32 limit", z, u, t)
+    announce("forward on the same rows")
+    zs, us, tg = to_dev(z), to_dev(u), to_dev(t)
+    out = outputs(BT)
+    lx.lx_ce_tvd_forward(zs, us, tg, II, out["ce"], out["tvd"], out["lse_s"], out["lse_t"], out["sigma"])
+    check_forward(host(out), z, u, t, II, "forward, reference sums near the fp32 limit")
+
+
 @pytest.mark.parametrize("V", [38400, 72000], ids=["K1_V38400", "K2_V72000"])
 def test_lds_part_of_the_chunk(V):
     """2048 rows make each row a single-digit number of members whose chunks are longer

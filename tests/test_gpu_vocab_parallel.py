@@ -142,6 +142,26 @@ def test_out_of_range_target_poisons_the_row_in_every_shard():
     assert np.all(np.isfinite(o["ce"][ok.numpy()]))
 
 
+def test_shard_sums_near_the_fp32_limit():
+    """8 shards of 18992 columns (2374 16-byte units each): in every shard the first
+    256 units (one per thread, the thread's reference) hold lo and the rest hi, 82
+    above, so each thread's sum against its reference is ~1e37 and the sum over a
+    workgroup would overflow fp32 unless the thread redoes it against its true
+    maximum."""
+    BT, V = 64, 151936
+    Vs = V // 8
+    col = np.arange(V) % Vs
+    row = np.where(col // 8 < 256, -57.0, 25.0).astype(np.float32)
+    rng = np.random.default_rng(11)
+    z = W.bf16_bits_rne(row[None, :] + rng.integers(0, 4, (BT, V)).astype(np.float32) * 0.125)
+    u = W.bf16_bits_rne(row[None, :] - 1.0 + rng.integers(0, 4, (BT, V)).astype(np.float32) * 0.125)
+    t = rng.integers(0, V, BT).astype(np.int64)
+    announce("vocab-parallel: per-thread sums near the fp32 limit, 8 shards of 18992")
+    o, g = run_vp(z, u, t, shard_bounds(V, [Vs] * 8), 0.5, 1.5)
+    check_forward(o, z, u, t, II, "vocab-parallel sums near the fp32 limit")
+    check_grad(grad_to_host(g), grad_bits(g), z, u, t, II, 0.5, 1.5, "vocab-parallel sums near the fp32 limit")
+
+
 def test_train_workload_in_eight_shards():
     """The training batch (8192 x 151936 bf16) cut into 8 shards of 18992 columns, the
     shape each device of an 8-way vocabulary-parallel layout holds; mean-reduced
