@@ -107,9 +107,9 @@ __device__ __forceinline__ void units_lse(u32x4_t (&w)[U], int n, Lse& a) {
   constexpr int E = Unit<T>::E;
   float x[E];
   Unit<T>::get(w[0], x);
-  float m = x[0];
+  float m = kMFloor;  // a floor, so that units of -inf logits give exp2(-inf) = 0, never inf - inf
 #pragma unroll
-  for (int e = 1; e < E; ++e) m = fmaxf(m, x[e]);
+  for (int e = 0; e < E; ++e) m = fmaxf(m, x[e]);
   float s0 = 0.0f, s1 = 0.0f;
   {
     const float nb = -(m * kLog2e);

@@ -142,6 +142,28 @@ def test_out_of_range_target_poisons_the_row_in_every_shard():
     assert np.all(np.isfinite(o["ce"][ok.numpy()]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_negative_infinity_columns_in_shards(dtype):
+    """-inf logits (masked columns): scattered columns, and for some rows a whole shard
+    (every unit a thread holds there is -inf)."""
+    BT, V = 64, 6000
+    z, u, t = W.custom(BT, V, dtype, seed=23, scale=2.0, teacher_noise=0.5)
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    cols = [0, 7, 1999, 2000, 3333]
+    z[:, cols] = ninf
+    u[:, cols] = ninf
+    z[:10, 4000:] = ninf
+    u[:10, 4000:] = ninf
+    bad = np.isin(t, cols) | ((np.arange(BT) < 10) & (t >= 4000))
+    t[bad] = 50
+    announce(f"vocab-parallel: -inf columns and a masked shard, {dtype}")
+    o, g = run_vp(z, u, t, shard_bounds(V, [2000, 2000, 2000]), 0.5, 1.5)
+    check_forward(o, z, u, t, II, "vocab-parallel -inf")
+    gh = grad_to_host(g)
+    check_grad(gh, grad_bits(g), z, u, t, II, 0.5, 1.5, "vocab-parallel -inf")
+    assert np.all(gh[:, cols] == 0.0) and np.all(gh[:10, 4000:] == 0.0)
+
+
 def test_shard_sums_near_the_fp32_limit():
     """8 shards of 18992 columns (2374 16-byte units each): in every shard the first
     256 units (one per thread, the thread's reference) hold lo and the rest hi, 82
