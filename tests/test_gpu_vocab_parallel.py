@@ -79,6 +79,8 @@ CASES = [
     (520, 8200, [2050, 2050, 2050, 2050], "bf16", False),
     (260, 6000, [2999, 3001], "f32", False),
     (8, 1024, [1024], "f32", True),                            # one shard: the plain loss
+    (64, 50000, [24996, 25004], "bf16", True),                 # shards over one pass of held units (2560 x 8)
+    (32, 31000, [31000], "f32", True),                         # fp32: 10240 logits per pass, 4 passes
 ]
 
 
