@@ -319,8 +319,10 @@ lx_status lx_ce_tvd_reduce_mean(const float* ce, const float* tvd, const int64_t
 #define LX_VP_TV_FLOATS 2
 
 /*
- * Per-shard step 1: for each row, the shard's maximum and sum of exp(x - max)
- * of the student (and teacher), and the student's target logit when the
+ * Per-shard step 1: for each row, a (m, s) pair of the student (and teacher)
+ * with s = sum of exp(x - m) over the shard, so that m + log(s) is the
+ * shard's log-sum-exp (m is at most the shard's maximum, or -1e30 when that
+ * is lower), and the student's target logit when the
  * target column lies in the shard (else +0).
  *
  * Inputs : student, teacher (NULL = CE-only) (BT, V_shard) dt; target int64[BT]
