@@ -166,6 +166,41 @@ def test_negative_infinity_columns_in_shards(dtype):
     assert np.all(gh[:, cols] == 0.0) and np.all(gh[:10, 4000:] == 0.0)
 
 
+def _offset_copy(raw: np.ndarray, elems: int) -> torch.Tensor:
+    """Device copy of raw starting `elems` elements past an aligned allocation."""
+    BT, V = raw.shape
+    base = torch.zeros(BT * V + 64, dtype=torch.bfloat16 if raw.dtype == np.uint16 else torch.float32, device=DEV)
+    view = base[elems:elems + BT * V].view(BT, V)
+    view.copy_(to_dev(raw))
+    return view
+
+
+@pytest.mark.parametrize("zoff,uoff", [(1, 1), (3, 5)], ids=["both+1", "mismatched"])
+def test_unaligned_shards(zoff, uoff):
+    """Shard arrays off the 16-byte grid: with equal offsets the rows keep a scalar
+    head and tail around 16-byte units; with different ones every element is read
+    singly.  The partials and merges against the oracle on whole rows."""
+    BT, V = 48, 9000
+    z, u, t = W.custom(BT, V, "bf16", seed=31 + zoff + 7 * uoff, scale=2.5, teacher_noise=0.5, ignore_rows=[4])
+    bounds = shard_bounds(V, [2999, 3001, 3000])
+    announce(f"vocab-parallel: shards at element offsets z+{zoff} u+{uoff}")
+    tg = to_dev(t)
+    stats = torch.full((3, BT, 5), 777.0, dtype=torch.float32, device=DEV)
+    tv = torch.full((3, BT, 2), 777.0, dtype=torch.float32, device=DEV)
+    zs = [_offset_copy(np.ascontiguousarray(z[:, a:b]), zoff) for a, b in bounds]
+    us = [_offset_copy(np.ascontiguousarray(u[:, a:b]), uoff) for a, b in bounds]
+    for n, (a, _) in enumerate(bounds):
+        lx.lx_ce_tvd_vp_stats(zs[n], us[n], tg, a, II, stats[n])
+    f = lambda: torch.full((BT,), 12345.0, dtype=torch.float32, device=DEV)
+    out = {k: f() for k in ("ce", "lse_s", "lse_t", "tvd", "sigma")}
+    lx.lx_ce_tvd_vp_merge_stats(stats, tg, V, II, out["ce"], out["lse_s"], out["lse_t"])
+    for n in range(3):
+        lx.lx_ce_tvd_vp_tv(zs[n], us[n], tg, II, out["lse_s"], out["lse_t"], tv[n])
+    lx.lx_ce_tvd_vp_merge_tv(tv, tg, II, out["tvd"], out["sigma"])
+    torch.cuda.synchronize()
+    check_forward({k: v.cpu().numpy() for k, v in out.items()}, z, u, t, II, "vocab-parallel unaligned")
+
+
 def test_shard_sums_near_the_fp32_limit():
     """8 shards of 18992 columns (2374 16-byte units each): in every shard the first
     256 units (one per thread, the thread's reference) hold lo and the rest hi, 82
